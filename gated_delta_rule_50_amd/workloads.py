@@ -1,0 +1,218 @@
+"""Seeded synthetic workloads for the KDA forward operator.
+
+This module only draws inputs: it holds none of the operator's arithmetic.
+Both the HIP path (through the tests and the benchmark) and the fp64 oracle
+consume what it produces.
+
+Value distributions follow the pages' KDA heads ("Kimi Linear: An Expressive,
+Efficient Attention Architecture", paper-graph-ui review, section "Neural
+Parameterization"): 128-dim heads, L2-normalised q and k, beta = sigmoid(.),
+alpha in (0, 1] per channel, supplied here as its natural log.
+
+Recipe (numpy PCG64, ``default_rng(seed)``), in draw order:
+  lengths (packed batches only) -> q -> k -> v -> beta -> log_alpha -> h0.
+  q, k  ~ N(0,1) float32, L2-normalised per (token, head) in fp64, then
+        rounded to the I/O dtype (bf16: round-to-nearest-even).
+  v     ~ N(0,1) float32, rounded to the I/O dtype.
+  beta  = sigmoid(z), z ~ N(0,1), float32.
+  log_alpha = log(sigmoid(z)) / 16 = -softplus(-z)/16, z ~ N(0,1), computed
+        in fp64, stored float32. "split" decay: channels [0, dk/2) use that
+        draw; channels [dk/2, dk) draw uniform [-1.0, -0.25] (strong decay).
+  h0    ~ N(0, std^2) float32 when std is given, else zeros (None).
+Large draws go in fixed row blocks, so results depend only on the seed.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+D = 128          # key / value head dimension of the pages' KDA heads
+CHUNK = 64       # chunk length of the chunkwise algorithm
+_BLOCK = 1 << 14  # rows per generation block
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bf16 (ties to even), returned as float32 values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """uint16 bit patterns of float32 values that are exactly bf16."""
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _to_io(x: np.ndarray, io: str) -> np.ndarray:
+    return round_bf16(x) if io == "bf16" else x.astype(np.float32)
+
+
+def _normal_f32(rng, shape):
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(shape[0], -1)
+    for s in range(0, shape[0], _BLOCK):
+        e = min(s + _BLOCK, shape[0])
+        flat[s:e] = rng.standard_normal(flat[s:e].shape, dtype=np.float32)
+    return out
+
+
+def _unit_rows(rng, shape, io):
+    """N(0,1) rows normalised along the last axis in fp64, rounded to io."""
+    x = _normal_f32(rng, shape)
+    flat = x.reshape(-1, shape[-1])
+    for s in range(0, flat.shape[0], _BLOCK):
+        e = min(s + _BLOCK, flat.shape[0])
+        blk = flat[s:e].astype(np.float64)
+        blk /= np.linalg.norm(blk, axis=-1, keepdims=True)
+        flat[s:e] = _to_io(blk.astype(np.float32), io)
+    return x
+
+
+def _log_sigmoid_over_16(z64: np.ndarray) -> np.ndarray:
+    # log(sigmoid(z)) = -softplus(-z) = -(max(-z,0) + log1p(exp(-|z|)))
+    return (-(np.maximum(-z64, 0.0) + np.log1p(np.exp(-np.abs(z64)))) / 16.0)
+
+
+def _log_alpha(rng, T, H, dk, decay):
+    la = np.empty((T, H, dk), dtype=np.float32)
+    half = dk // 2
+    for s in range(0, T, _BLOCK):
+        e = min(s + _BLOCK, T)
+        if decay == "mild":
+            z = rng.standard_normal((e - s, H, dk))
+            la[s:e] = _log_sigmoid_over_16(z).astype(np.float32)
+        elif decay == "split":
+            z = rng.standard_normal((e - s, H, half))
+            la[s:e, :, :half] = _log_sigmoid_over_16(z).astype(np.float32)
+            la[s:e, :, half:] = rng.uniform(-1.0, -0.25, (e - s, H, dk - half)).astype(np.float32)
+        else:
+            raise ValueError(f"unknown decay recipe {decay!r}")
+    return la
+
+
+@dataclass
+class Prefill:
+    """One packed prefill batch (numpy, host)."""
+    q: np.ndarray            # [T, H, dk] float32 (bf16-exact when io == "bf16")
+    k: np.ndarray            # [T, H, dk]
+    v: np.ndarray            # [T, H, dv]
+    log_alpha: np.ndarray    # [T, H, dk] float32
+    beta: np.ndarray         # [T, H] float32
+    h0: Optional[np.ndarray]  # [N, H, dk, dv] float32 or None
+    cu_seqlens: np.ndarray   # [N+1] int32
+    io: str                  # "bf16" or "f32"
+
+    @property
+    def T(self):
+        return self.k.shape[0]
+
+    @property
+    def H(self):
+        return self.k.shape[1]
+
+    @property
+    def N(self):
+        return len(self.cu_seqlens) - 1
+
+
+def make_prefill(lengths, H, seed, io="bf16", decay="mild", h0_std=None,
+                 dk=D, dv=D) -> Prefill:
+    """Draws one packed batch with sequences of the given lengths."""
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    q = _unit_rows(rng, (T, H, dk), io)
+    k = _unit_rows(rng, (T, H, dk), io)
+    v = _to_io(_normal_f32(rng, (T, H, dv)), io)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
+    la = _log_alpha(rng, T, H, dk, decay)
+    h0 = None
+    if h0_std is not None:
+        h0 = (_normal_f32(rng, (len(lengths), H, dk, dv)) * np.float32(h0_std)).astype(np.float32)
+    return Prefill(q, k, v, la, beta, h0, cu, io)
+
+
+@dataclass
+class DecodeStep:
+    """Inputs of one decode step: one token for each of N sequences."""
+    q: np.ndarray          # [N, H, dk]
+    k: np.ndarray          # [N, H, dk]
+    v: np.ndarray          # [N, H, dv]
+    log_alpha: np.ndarray  # [N, H, dk]
+    beta: np.ndarray       # [N, H]
+    io: str
+
+
+def make_decode_state(N, H, seed, std=0.02, dk=D, dv=D) -> np.ndarray:
+    """Initial decode states S0 [N, H, dk, dv] ~ N(0, std^2), float32."""
+    rng = np.random.default_rng(seed)
+    return (_normal_f32(rng, (N, H, dk, dv)) * np.float32(std)).astype(np.float32)
+
+
+def make_decode_step(N, H, seed, step, io="bf16", dk=D, dv=D) -> DecodeStep:
+    """Fresh token inputs for decode step ``step`` (rng seeded [seed, step])."""
+    rng = np.random.default_rng([seed, step])
+    q = _unit_rows(rng, (N, H, dk), io)
+    k = _unit_rows(rng, (N, H, dk), io)
+    v = _to_io(_normal_f32(rng, (N, H, dv)), io)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((N, H))))).astype(np.float32)
+    la = _log_alpha(rng, N, H, dk, "mild")
+    return DecodeStep(q, k, v, la, beta, io)
+
+
+@dataclass
+class Config:
+    """One of the five benchmark/parity configurations."""
+    cid: int
+    name: str
+    kind: str                      # "prefill" or "decode"
+    H: int
+    io: str
+    seed: int
+    lengths: tuple = ()
+    decay: str = "mild"
+    h0_std: Optional[float] = None
+    n_seqs: int = 1
+    steps: int = 0
+    extra: dict = field(default_factory=dict)
+
+    def prefill(self) -> Prefill:
+        assert self.kind == "prefill"
+        return make_prefill(self.lengths, self.H, self.seed, self.io,
+                            self.decay, self.h0_std)
+
+
+def _varlen_lengths(seed, n, lo, hi):
+    rng = np.random.default_rng(seed)
+    return tuple(int(x) for x in rng.integers(lo, hi, size=n, endpoint=True))
+
+
+def config(cid: int) -> Config:
+    """The five workloads: 0 tiny fp32, 1 8K prefill, 2 128K strong-decay
+    prefill, 3 packed variable-length prefill, 4 decode 256 x 32 heads."""
+    seed = 1000 + cid
+    if cid == 0:
+        return Config(0, "tiny_fp32_T512_H2", "prefill", H=2, io="f32",
+                      seed=seed, lengths=(512,))
+    if cid == 1:
+        return Config(1, "prefill_T8192_H32_bf16", "prefill", H=32, io="bf16",
+                      seed=seed, lengths=(8192,))
+    if cid == 2:
+        return Config(2, "prefill_T131072_H32_bf16_strong_decay", "prefill",
+                      H=32, io="bf16", seed=seed, lengths=(131072,),
+                      decay="split", h0_std=0.02)
+    if cid == 3:
+        # lengths are drawn from their own stream so the batch draw stays
+        # in the documented order (lengths first, then q, k, v, ...)
+        lengths = _varlen_lengths(seed + 100000, 16, 512, 16384)
+        return Config(3, "varlen_16seq_H32_bf16", "prefill", H=32, io="bf16",
+                      seed=seed, lengths=lengths, h0_std=0.02, n_seqs=16)
+    if cid == 4:
+        return Config(4, "decode_N256_H32_bf16_64steps", "decode", H=32,
+                      io="bf16", seed=seed, n_seqs=256, steps=64)
+    raise ValueError(cid)
