@@ -1,0 +1,7 @@
+"""MI355X-native Kimi Delta Attention forward operator.
+
+``kda`` binds the C ABI of libkda.so (HIP kernels for gfx950);
+``workloads`` draws the seeded synthetic inputs.
+"""
+from .kda import (KDAError, alloc_workspace, chunk_fwd, chunk_fwd_workspace_bytes,  # noqa: F401
+                  decode_step, lib)

@@ -1,0 +1,155 @@
+// Host side of the C ABI declared in include/kda.h: argument validation,
+// workspace sizing and launch sequencing. No compute happens here; every
+// step of the operator runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+hipError_t launch_decode_step(bool bf16_io, const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* beta, float* S,
+                              void* o, int64_t pairs, hipStream_t stream);
+hipError_t launch_chunk_fwd(bool bf16_io, const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* beta, const float* h0,
+                            const int32_t* cu, int32_t n_seqs, int64_t T, int32_t H,
+                            int64_t n_slots, void* o, float* h_final, int32_t* status,
+                            int32_t* chunk_offset, uint8_t* inter, hipStream_t stream);
+size_t inter_block_bytes(bool bf16_io);
+}  // namespace kda
+
+namespace {
+
+constexpr int64_t kChunk = KDA_CHUNK;
+constexpr int64_t kDim = KDA_HEAD_DIM;
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+  Range() = default;
+  Range(const void* p, int64_t bytes)
+      : lo((uintptr_t)p), hi((uintptr_t)p + (uintptr_t)(p ? bytes : 0)) {}
+  bool empty() const { return hi <= lo; }
+};
+
+bool overlap(const Range& a, const Range& b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool valid_io(kda_io_dtype io) { return io == KDA_IO_F32 || io == KDA_IO_BF16; }
+
+int64_t io_bytes(kda_io_dtype io) { return io == KDA_IO_BF16 ? 2 : 4; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Chunk slots the prefill launch is sized for: sum_n ceil(L_n / 64) is at
+// most ceil(T / 64) + N - 1 for any split of T tokens into N sequences.
+int64_t chunk_slots(int64_t n_seqs, int64_t T) {
+  return (T + kChunk - 1) / kChunk + n_seqs - 1;
+}
+
+int64_t inter_offset(int64_t n_seqs) { return 256 + round_up(4 * (n_seqs + 1), 256); }
+
+// Returns 0 when the sizes are unusable.
+size_t workspace_bytes(int64_t n_seqs, int64_t T, int64_t heads, kda_io_dtype io) {
+  if (n_seqs < 1 || T < 0 || heads < 1 || heads > 65535 || !valid_io(io)) return 0;
+  const int64_t slots = chunk_slots(n_seqs, T);
+  if (slots > INT32_MAX) return 0;
+  const int64_t block = (int64_t)kda::inter_block_bytes(io == KDA_IO_BF16);
+  return (size_t)(inter_offset(n_seqs) + slots * heads * block);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t heads,
+                                     int32_t dk, int32_t dv, kda_io_dtype io) {
+  if (dk != kDim || dv != kDim) return 0;
+  return workspace_bytes(n_seqs, total_tokens, heads, io);
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* beta, const float* h0,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                         int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io, void* o,
+                         float* h_final, void* workspace, size_t workspace_bytes_given,
+                         void* stream) {
+  const int64_t T = total_tokens;
+  if (T < 0 || n_seqs < 1 || heads < 1) return KDA_ERR_SHAPE;
+  if (dk != kDim || dv != kDim || !valid_io(io) || heads > 65535) return KDA_ERR_UNSUPPORTED;
+  if (cu_seqlens == nullptr && n_seqs != 1) return KDA_ERR_NULL;
+  if (cu_seqlens != nullptr && T > INT32_MAX) return KDA_ERR_SHAPE;
+  if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
+  const size_t need = workspace_bytes(n_seqs, T, heads, io);
+  if (need == 0) return KDA_ERR_SHAPE;
+  if (!workspace || workspace_bytes_given < need || ((uintptr_t)workspace & 255u))
+    return KDA_ERR_WORKSPACE;
+
+  const int64_t th = T * heads;
+  const int64_t eb = io_bytes(io);
+  const Range rq(q, th * kDim * eb), rk(k, th * kDim * eb), rv(v, th * kDim * eb);
+  const Range rla(log_alpha, th * kDim * 4), rb(beta, th * 4);
+  const Range ro(o, th * kDim * eb);
+  const int64_t state_bytes = (int64_t)n_seqs * heads * kDim * kDim * 4;
+  const Range rh0(h0, state_bytes), rhf(h_final, state_bytes);
+  const Range rcu(cu_seqlens, 4 * ((int64_t)n_seqs + 1));
+  const Range rws(workspace, (int64_t)need);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rh0, &rcu, &rws})
+    if (overlap(ro, *in)) return KDA_ERR_ALIAS;
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro, &rcu, &rws})
+    if (overlap(rhf, *in)) return KDA_ERR_ALIAS;
+  if (overlap(rhf, rh0) && rhf.lo != rh0.lo) return KDA_ERR_ALIAS;
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rh0, &rcu})
+    if (overlap(rws, *in)) return KDA_ERR_ALIAS;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* status = reinterpret_cast<int32_t*>(ws);
+  int32_t* chunk_offset = reinterpret_cast<int32_t*>(ws + 256);
+  uint8_t* inter = ws + inter_offset(n_seqs);
+  const hipError_t err = kda::launch_chunk_fwd(
+      io == KDA_IO_BF16, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, T, heads,
+      chunk_slots(n_seqs, T), o, h_final, status, chunk_offset, inter,
+      static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, float* S_inout,
+                           int32_t n_seqs, int32_t heads, int32_t dk, int32_t dv,
+                           kda_io_dtype io, void* o, void* stream) {
+  if (n_seqs < 0 || heads < 1) return KDA_ERR_SHAPE;
+  if (dk != kDim || dv != kDim || !valid_io(io)) return KDA_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return KDA_OK;
+  if (!q || !k || !v || !log_alpha || !beta || !S_inout || !o) return KDA_ERR_NULL;
+  const int64_t pairs = (int64_t)n_seqs * heads;
+  if (pairs > INT32_MAX) return KDA_ERR_SHAPE;
+  const int64_t eb = io_bytes(io);
+  const Range rq(q, pairs * kDim * eb), rk(k, pairs * kDim * eb), rv(v, pairs * kDim * eb);
+  const Range rla(log_alpha, pairs * kDim * 4), rb(beta, pairs * 4);
+  const Range rs(S_inout, pairs * kDim * kDim * 4), ro(o, pairs * kDim * eb);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro})
+    if (overlap(rs, *in)) return KDA_ERR_ALIAS;
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb})
+    if (overlap(ro, *in)) return KDA_ERR_ALIAS;
+  const hipError_t err = kda::launch_decode_step(io == KDA_IO_BF16, q, k, v, log_alpha,
+                                                 beta, S_inout, o, pairs,
+                                                 static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is negative or inconsistent";
+    case KDA_ERR_UNSUPPORTED: return "unsupported head size or dtype (d_k = d_v = 128 only)";
+    case KDA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case KDA_ERR_ALIAS: return "an output overlaps an input it must not";
+    case KDA_ERR_HIP: return "the HIP runtime reported a launch error";
+  }
+  return "unknown status";
+}
+
+int32_t kda_version(void) { return 100; }
+
+}  // extern "C"

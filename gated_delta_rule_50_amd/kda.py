@@ -1,0 +1,167 @@
+"""Thin Python binding of libkda.so (the C ABI in include/kda.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the operator runs in the HIP kernels. If
+the library is not built the calls raise instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libkda.so"
+
+KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_UNSUPPORTED = 0, 1, 2, 3
+KDA_ERR_WORKSPACE, KDA_ERR_ALIAS, KDA_ERR_HIP = 4, 5, 6
+KDA_IO_F32, KDA_IO_BF16 = 0, 1
+CHUNK = 64
+HEAD_DIM = 128
+
+EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_decode_step",
+           "kda_status_string", "kda_version")
+
+_LIB = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libkda.so once; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m gated_delta_rule_50_amd.build` first")
+        L = ctypes.CDLL(str(LIB_PATH))
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+        L.kda_chunk_fwd_workspace_bytes.restype = sz
+        L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                    ctypes.c_int, vp, vp, vp, sz, vp]
+        L.kda_chunk_fwd.restype = ctypes.c_int
+        L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                      ctypes.c_int, vp, vp]
+        L.kda_decode_step.restype = ctypes.c_int
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_version.restype = i32
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def _io(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return KDA_IO_BF16
+    if dtype == torch.float32:
+        return KDA_IO_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(stream, device):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def chunk_fwd_workspace_bytes(n_seqs: int, total_tokens: int, heads: int,
+                              io_dtype: torch.dtype) -> int:
+    return int(lib().kda_chunk_fwd_workspace_bytes(n_seqs, total_tokens, heads,
+                                                   HEAD_DIM, HEAD_DIM, _io(io_dtype)))
+
+
+def alloc_workspace(n_seqs, total_tokens, heads, io_dtype, device) -> torch.Tensor:
+    """A 256-byte aligned uint8 device buffer of the required size."""
+    nbytes = chunk_fwd_workspace_bytes(n_seqs, total_tokens, heads, io_dtype)
+    if nbytes == 0:
+        raise ValueError("invalid sizes for the prefill workspace")
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + nbytes]
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
+              h_final=None, want_final=True, workspace=None, stream=None):
+    """Chunked prefill. Returns (o, h_final or None).
+
+    q, k [T, H, 128], v [T, H, 128] (bf16 or fp32, one dtype); log_alpha
+    [T, H, 128] fp32; beta [T, H] fp32; h0 [N, H, 128, 128] fp32 or None;
+    cu_seqlens int32 [N + 1] on the device or None (one sequence). h_final
+    may be passed as h0 to continue in place.
+    """
+    dev = k.device
+    io = _io(k.dtype)
+    T, H = int(k.shape[0]), int(k.shape[1])
+    N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, k.dtype, dev)
+    _check(log_alpha, "log_alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(h0, "h0", torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if o is None:
+        o = torch.empty((T, H, v.shape[2]), dtype=k.dtype, device=dev)
+    _check(o, "o", k.dtype, dev)
+    if h_final is None and want_final:
+        h_final = torch.empty((N, H, k.shape[2], v.shape[2]), dtype=torch.float32, device=dev)
+    _check(h_final, "h_final", torch.float32, dev)
+    if workspace is None:
+        workspace = alloc_workspace(N, T, H, k.dtype, dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    st = lib().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+        N, T, H, int(k.shape[2]), int(v.shape[2]), io, _ptr(o), _ptr(h_final),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, h_final
+
+
+def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
+    """One recurrent step; S [N, H, 128, 128] fp32 is updated in place.
+
+    q, k, v [N, H, 128] (bf16 or fp32); log_alpha [N, H, 128] fp32;
+    beta [N, H] fp32. Returns o [N, H, 128].
+    """
+    dev = k.device
+    io = _io(k.dtype)
+    N, H = int(k.shape[0]), int(k.shape[1])
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, k.dtype, dev)
+    _check(log_alpha, "log_alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(S, "S", torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, v.shape[2]), dtype=k.dtype, device=dev)
+    _check(o, "o", k.dtype, dev)
+    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                               _ptr(S), N, H, int(k.shape[2]), int(v.shape[2]), io,
+                               _ptr(o), _stream(stream, dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_decode_step")
+    return o

@@ -1,0 +1,187 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) Kimi Delta Attention forward operator.
+ *
+ * The operator is the channel-wise gated delta rule
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * ("Kimi Linear: An Expressive, Efficient Attention Architecture",
+ * paper-graph-ui review, section "The KDA State Update Equation"; Eq. 1 of
+ * the "L2 Deep Distill" page). Prefill uses the chunkwise WY/UT algorithm of
+ * the review's section "Chunkwise Parallelization" (UT transform, Eq. 8
+ * state update, Eq. 9 output) with chunks of KDA_CHUNK tokens; decode is one
+ * step of the recurrence per sequence (the review's "FLOPs Accounting and
+ * Inference Strategy": chunk kernel for prefill, recurrent kernel for
+ * generation).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates device memory; scratch space is a caller-supplied
+ *    workspace sized by kda_chunk_fwd_workspace_bytes().
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream). Nothing synchronises the host.
+ *  - Arguments that the host can see (pointers, sizes, dtypes, aliasing) are
+ *    checked before anything is launched; a failed check returns a status
+ *    and launches nothing. A launch failure returns KDA_ERR_HIP. No C++
+ *    exception crosses the ABI.
+ *  - Only d_k = d_v = 128 is supported (the pages' head size).
+ *  - Tensor layouts are dense row-major with the last index fastest:
+ *      q, k       [T, H, d_k]   I/O dtype
+ *      v, o       [T, H, d_v]   I/O dtype
+ *      log_alpha  [T, H, d_k]   float32: natural log of the per-channel decay
+ *                               alpha_t in (0, 1], i.e. finite and <= 0
+ *      beta       [T, H]        float32
+ *      states     [N, H, d_k, d_v] float32, S[c][j]: row c = key channel,
+ *                               column j = value channel
+ *    For decode, T is replaced by the batch N (one token per sequence).
+ *  - No query scaling is applied (o_t = S_t^T q_t as printed), q and k are
+ *    used as given (callers L2-normalise them), and bf16 outputs are rounded
+ *    to nearest even.
+ *  - Unchecked preconditions (the device cannot report them synchronously):
+ *    finite inputs, log_alpha <= 0, cu_seqlens non-decreasing with
+ *    cu_seqlens[0] = 0 and cu_seqlens[N] = T. Violations give unspecified
+ *    values but never out-of-bounds accesses: kernels clamp every index, and
+ *    a malformed cu_seqlens sets the workspace status word (below).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_CHUNK 64    /* tokens per chunk of the chunkwise algorithm */
+#define KDA_HEAD_DIM 128 /* the only supported d_k = d_v */
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                   */
+  KDA_ERR_SHAPE = 2,       /* a size is negative or inconsistent           */
+  KDA_ERR_UNSUPPORTED = 3, /* d_k or d_v != 128, or unknown dtype          */
+  KDA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned   */
+  KDA_ERR_ALIAS = 5,       /* an output overlaps an input it must not      */
+  KDA_ERR_HIP = 6          /* the HIP runtime reported a launch error      */
+} kda_status;
+
+typedef enum {
+  KDA_IO_F32 = 0,  /* q, k, v, o are float32 */
+  KDA_IO_BF16 = 1  /* q, k, v, o are bfloat16 */
+} kda_io_dtype;
+
+/*
+ * kda_chunk_fwd_workspace_bytes
+ *   Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if an
+ *   argument is invalid). The workspace must be 256-byte aligned.
+ *   n_seqs: sequences N in the packed batch (N = 1 when cu_seqlens is NULL).
+ *   total_tokens: T, tokens over all sequences.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
+                                     int32_t heads, int32_t dk, int32_t dv,
+                                     kda_io_dtype io);
+
+/*
+ * kda_chunk_fwd - chunked prefill over a packed batch of sequences.
+ *
+ * Computes, for every sequence n (tokens [cu_seqlens[n], cu_seqlens[n+1]))
+ * and head h independently, the outputs o_t of every token and the state
+ * after the last token, starting from h0[n, h] (zeros when h0 is NULL).
+ * Chunks of KDA_CHUNK tokens never straddle sequences; a sequence's last
+ * chunk may be shorter. Paper: review section "Chunkwise Parallelization",
+ * Eq. 8 (chunk state update) and Eq. 9 (chunk output); the UT transform
+ * gives W and U from StrictTril(Diag(beta)(Gamma*K)(K/Gamma)^T).
+ *
+ *   q, k, v, o      see layouts above; io selects float32 or bfloat16
+ *   log_alpha, beta float32
+ *   h0              [N, H, 128, 128] float32, or NULL for zero states
+ *   cu_seqlens      device int32 [N + 1], or NULL for one sequence (N = 1)
+ *   h_final         [N, H, 128, 128] float32, or NULL to skip; it may be the
+ *                   same pointer as h0 (in-place continuation) but must not
+ *                   partially overlap it
+ *   workspace       device scratch of at least
+ *                   kda_chunk_fwd_workspace_bytes(...) bytes, 256-byte
+ *                   aligned; its contents on return are described below
+ *   A sequence of length 0 copies h0 (or zeros) to h_final. T = 0 writes
+ *   nothing but h_final.
+ *   Errors: KDA_ERR_NULL (q, k, v, log_alpha, beta or o NULL when T > 0;
+ *   cu_seqlens NULL with n_seqs != 1), KDA_ERR_SHAPE (negative sizes,
+ *   n_seqs < 1, heads < 1, T > INT32_MAX with cu_seqlens),
+ *   KDA_ERR_UNSUPPORTED (d_k, d_v != 128, unknown dtype, heads > 65535),
+ *   KDA_ERR_WORKSPACE (NULL, smaller than required, not 256-byte aligned),
+ *   KDA_ERR_ALIAS (o overlapping an input; h_final overlapping q, k, v,
+ *   log_alpha, beta or o; h_final partially overlapping h0), KDA_ERR_HIP.
+ *
+ * Workspace contents after the call (for inspection and tests; the format
+ * is internal and may change). E is the element type: bf16 for
+ * KDA_IO_BF16, float32 for KDA_IO_F32.
+ *   [0, 4)          int32 status: 0 ok, 1 malformed cu_seqlens
+ *   [256, ...)      int32 chunk_offset[N + 1]: first global chunk index of
+ *                   each sequence (exclusive prefix sum of ceil(L_n / 64))
+ *   [inter_offset)  per (global chunk b, head h), a block of
+ *                   40960 E + 128 float32, blocks ordered [b][h], where
+ *                   inter_offset = 256 + round_up(4 (N + 1), 256):
+ *       XA  16384 E  [-W ; Qt]  as A-fragments, 8 row tiles x 4 k-blocks
+ *       KT   8192 E  K'^T       as A-fragments, 8 row tiles x 2 k-blocks
+ *       UC  16384 E  [U ; Ut]   as C-fragments, 8 column tiles x 8 row tiles
+ *       GC   128 f32 gamma_C[c] = exp(g_last[c])
+ *   with, inside the chunk (rows i = token position, padded to 64 with
+ *   k = v = q = 0, beta = 0, log_alpha = 0):
+ *       g_i   = sum_{t <= i} log_alpha_t,        Gamma rows exp(g_i)
+ *       L     = StrictTril(Diag(beta) A_kk),     A_kk[i][t] = sum_c k_i k_t exp(g_i - g_t)
+ *       W     = (I + L)^{-1} Diag(beta) (Gamma * K),  U = (I + L)^{-1} Diag(beta) V
+ *       A_qk  = Tril(sum_c q_i k_t exp(g_i - g_t))
+ *       Qt    = Gamma * Q - A_qk W,  Ut = A_qk U,  K'[t][c] = k_t[c] exp(g_last[c] - g_t[c])
+ *   so that, from the chunk's start state S, U - W S is the pseudo-value,
+ *   O = Qt S + Ut (Eq. 9 regrouped) and the next state is
+ *   Diag(gamma_C) S + K'^T (U - W S) (Eq. 8).
+ *   Fragment maps: an A-fragment (mt, kb) of matrix X gives lane
+ *   l = r + 16 g (r < 16, g < 4) the 8 elements X[16 mt + r][32 kb + 4 g + e]
+ *   for e < 4 and X[16 mt + r][32 kb + 16 + 4 g + e - 4] for e >= 4; a
+ *   C-fragment (jt, mt) of Y gives lane l the 4 elements
+ *   Y[16 mt + 4 g + e][16 jt + r]. Fragments are stored lane-major,
+ *   A-fragments ordered [mt][kb], C-fragments ordered [jt][mt].
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *beta,
+                         const float *h0, const int32_t *cu_seqlens,
+                         int32_t n_seqs, int64_t total_tokens, int32_t heads,
+                         int32_t dk, int32_t dv, kda_io_dtype io, void *o,
+                         float *h_final, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_step - one recurrent step for a batch of sequences.
+ *
+ * For each sequence n and head h, with alpha = exp(log_alpha[n, h]):
+ *   S~ = Diag(alpha) S,  e = S~^T k,  S <- S~ - beta k (e - v)^T,
+ *   o  = S^T q (on the updated state)
+ * which is Eq. 1 written in the review's "Online Learning Interpretation"
+ * form (decode = "the recurrent kernel (Eq. 2)" of the review's "FLOPs
+ * Accounting and Inference Strategy"). S_inout [N, H, 128, 128] float32 is
+ * read once and overwritten in place.
+ *   q, k [N, H, 128], v [N, H, 128], o [N, H, 128]: I/O dtype
+ *   log_alpha [N, H, 128], beta [N, H]: float32
+ * n_seqs = 0 does nothing. Errors: KDA_ERR_NULL, KDA_ERR_SHAPE,
+ * KDA_ERR_UNSUPPORTED, KDA_ERR_ALIAS (S_inout or o overlapping an input, or
+ * each other), KDA_ERR_HIP.
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           float *S_inout, int32_t n_seqs, int32_t heads,
+                           int32_t dk, int32_t dv, kda_io_dtype io, void *o,
+                           void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *kda_status_string(kda_status s);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */
