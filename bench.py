@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward operator on one MI355X.
+
+One step is one pass of the whole hot path: a chunked prefill call on the
+8K workload (one sequence, T = 8192, H = 32, d_k = d_v = 128, bf16 q/k/v,
+fp32 gates and state, h0 = 0) followed by one decode step on the decode
+workload (256 sequences x 32 heads, fp32 states of 512 MiB updated in place).
+Inputs are synthetic (seeded generators), resident in HBM before timing.
+
+Printed: ONE JSON line. ``value`` is prefill tokens/s (T / mean prefill time
+per call from HIP events on the launch stream); decode tokens/s is reported
+beside it. ``roofline`` describes the kernel with the longest mean duration
+per step; every kernel's figures are under ``kernels``.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "KDA prefill tokens/s (H=32,d=128,T=8K) + decode tokens/s; % MFMA/HBM peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+D, C = 128, 64
+
+# Algorithmic bytes and FLOPs (bf16 I/O). Per token-head of prefill:
+# q, k, v 256 B each, log_alpha 512 B, beta 4 B, o 256 B.
+PREFILL_IN_BYTES = 3 * 256 + 512 + 4     # read by the intra-chunk kernel
+PREFILL_OUT_BYTES = 256                  # o, written by the carry kernel
+PREFILL_BYTES = PREFILL_IN_BYTES + PREFILL_OUT_BYTES   # 1540
+STATE_BYTES = D * D * 4
+FLOPS_EQ13 = 6 * D * D + 3 * C * D + C * C             # 126976 per token-head
+FLOPS_DENSE = 6 * D * D + 10 * C * D                   # 180224 per token-head
+# Decode, per (sequence, head): state read + write, q/k/v, log_alpha, beta, o.
+DECODE_BYTES = 2 * STATE_BYTES + 3 * 256 + 512 + 4 + 256   # 132612
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing on the host cores")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter scale factor)")
+    return ap.parse_args()
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def copy_calibration(torch):
+    """A plain copy of 1 GiB, three times: read 1 GiB, write 1 GiB each."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": a.numel() * 4, "repeats": 3}))
+
+
+def cpu_baseline(p, seconds):
+    """The fp64 oracle, as it stands, on the prefill workload (all heads),
+    repeated until at least `seconds` of wall time; plus one decode step of
+    the decode workload."""
+    from oracle import recurrent
+    from gated_delta_rule_50_amd import workloads
+    threads = recurrent.host_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        recurrent.forward(p.q, p.k, p.v, p.log_alpha, p.beta, None, p.cu_seqlens,
+                          threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    cfg = workloads.config(4)
+    S0 = workloads.make_decode_state(cfg.n_seqs, cfg.H, cfg.seed)
+    d = workloads.make_decode_step(cfg.n_seqs, cfg.H, cfg.seed, 0, io=cfg.io)
+    t1 = time.perf_counter()
+    recurrent.decode_step(d.q, d.k, d.v, d.log_alpha, d.beta, S0, threads=threads)
+    ddt = time.perf_counter() - t1
+    return {"value": reps * p.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"prefill workload (T={p.T}, H={p.H}, all heads) x {reps}, "
+                      f"fp64 recurrence, {dt:.1f} s; decode: one step of "
+                      f"{cfg.n_seqs}x{cfg.H} states in {ddt:.2f} s",
+            "decode_value": cfg.n_seqs / ddt}
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}): the "
+              "KDA operator here runs on a single MI355X and this build has no multi-GPU "
+              "path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    from gated_delta_rule_50_amd import Prefill, decode_step, lib, workloads
+    lib()  # fail loudly if the HIP library is missing
+
+    cfg1 = workloads.config(1)
+    p = cfg1.prefill()
+    bf = torch.bfloat16
+
+    def d(x, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dt)
+
+    pre = Prefill(d(p.q, bf), d(p.k, bf), d(p.v, bf), d(p.log_alpha), d(p.beta), None,
+                  d(p.cu_seqlens, torch.int32))
+    cfg4 = workloads.config(4)
+    S = d(workloads.make_decode_state(cfg4.n_seqs, cfg4.H, cfg4.seed))
+    ds = workloads.make_decode_step(cfg4.n_seqs, cfg4.H, cfg4.seed, 0, io=cfg4.io)
+    dq, dk, dv = d(ds.q, bf), d(ds.k, bf), d(ds.v, bf)
+    dla, db = d(ds.log_alpha), d(ds.beta)
+    do = torch.empty_like(dv)
+    pairs = cfg4.n_seqs * cfg4.H
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for ph in range(3):
+            pre.run_phase(ph)
+            if ev is not None:
+                ev[1 + ph].record()
+        decode_step(dq, dk, dv, dla, db, S, o=do)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(torch, 5) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["chunk_map", "intra", "carry", "decode"]
+    dur = {n: [] for n in names}
+    prefill_ms = []
+    for ev in evs:
+        for i, n in enumerate(names):
+            dur[n].append(ev[i].elapsed_time(ev[i + 1]))
+        prefill_ms.append(ev[0].elapsed_time(ev[3]))
+    mean = {n: float(np.mean(v)) for n, v in dur.items()}
+    t_pre = float(np.mean(prefill_ms)) * 1e-3
+    t_dec = mean["decode"] * 1e-3
+
+    th = p.T * p.H
+    nh = p.N * p.H
+    kernels = {
+        "chunk_map": {"mean_us": mean["chunk_map"] * 1e3},
+        "intra": {"mean_us": mean["intra"] * 1e3, "bound": "hbm",
+                  "alg_bytes": th * PREFILL_IN_BYTES,
+                  "unit_note": "q,k,v,log_alpha,beta per token-head (1284 B)"},
+        "carry": {"mean_us": mean["carry"] * 1e3, "bound": "hbm",
+                  "alg_bytes": th * PREFILL_OUT_BYTES + nh * STATE_BYTES,
+                  "unit_note": "o per token-head (256 B) + h_final per sequence-head"},
+        "decode": {"mean_us": mean["decode"] * 1e3, "bound": "hbm",
+                   "alg_bytes": pairs * DECODE_BYTES,
+                   "unit_note": "132612 B per (sequence, head)"},
+    }
+    for n, kdesc in kernels.items():
+        if "alg_bytes" in kdesc:
+            gbps = kdesc["alg_bytes"] / (kdesc["mean_us"] * 1e-6) / 1e9
+            kdesc["achieved_GBps"] = gbps
+            kdesc["frac"] = gbps / HBM_PEAK_GBPS
+    dom = max(("intra", "carry", "decode"), key=lambda n: kernels[n]["mean_us"])
+    kd = kernels[dom]
+    roofline = {"bound": "hbm", "achieved": kd["achieved_GBps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": kd["frac"], "traffic": None, "kernel": dom}
+
+    pre_bytes = th * PREFILL_BYTES + nh * STATE_BYTES
+    t_roof = max(pre_bytes / (HBM_PEAK_GBPS * 1e9), th * FLOPS_EQ13 / (BF16_PEAK_TFLOPS * 1e12))
+    prefill_path = {
+        "time_us": t_pre * 1e6,
+        "alg_bytes": pre_bytes,
+        "achieved_GBps": pre_bytes / t_pre / 1e9,
+        "frac_hbm": pre_bytes / t_pre / 1e9 / HBM_PEAK_GBPS,
+        "tflops_eq13": th * FLOPS_EQ13 / t_pre / 1e12,
+        "frac_mfma_eq13": th * FLOPS_EQ13 / t_pre / 1e12 / BF16_PEAK_TFLOPS,
+        "tflops_dense": th * FLOPS_DENSE / t_pre / 1e12,
+        "frac_mfma_dense": th * FLOPS_DENSE / t_pre / 1e12 / BF16_PEAK_TFLOPS,
+        "attainable_frac": t_roof / t_pre,
+    }
+    decode_tps = cfg4.n_seqs / t_dec
+
+    out = {
+        "metric": METRIC,
+        "value": p.T / t_pre,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill T={p.T} H={p.H} d=128 chunk=64 bf16 q/k/v, fp32 "
+                               f"gates/state, h0=0; + decode step {cfg4.n_seqs}x{cfg4.H} "
+                               f"fp32 states", "T": p.T, "H": p.H, "d": D, "chunk": C,
+                   "decode_batch": cfg4.n_seqs},
+        "decode_tokens_per_s": decode_tps,
+        "roofline": roofline,
+        "prefill_path": prefill_path,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

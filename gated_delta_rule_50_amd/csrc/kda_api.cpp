@@ -10,11 +10,12 @@ namespace kda {
 hipError_t launch_decode_step(bool bf16_io, const void* q, const void* k, const void* v,
                               const float* log_alpha, const float* beta, float* S,
                               void* o, int64_t pairs, hipStream_t stream);
-hipError_t launch_chunk_fwd(bool bf16_io, const void* q, const void* k, const void* v,
-                            const float* log_alpha, const float* beta, const float* h0,
-                            const int32_t* cu, int32_t n_seqs, int64_t T, int32_t H,
-                            int64_t n_slots, void* o, float* h_final, int32_t* status,
-                            int32_t* chunk_offset, uint8_t* inter, hipStream_t stream);
+hipError_t launch_chunk_fwd(int phases, bool bf16_io, const void* q, const void* k,
+                            const void* v, const float* log_alpha, const float* beta,
+                            const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
+                            int32_t H, int64_t n_slots, void* o, float* h_final,
+                            int32_t* status, int32_t* chunk_offset, uint8_t* inter,
+                            hipStream_t stream);
 size_t inter_block_bytes(bool bf16_io);
 }  // namespace kda
 
@@ -68,12 +69,18 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32
   return workspace_bytes(n_seqs, total_tokens, heads, io);
 }
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
-                         const float* log_alpha, const float* beta, const float* h0,
-                         const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
-                         int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io, void* o,
-                         float* h_final, void* workspace, size_t workspace_bytes_given,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates the prefill arguments and launches the phases selected by the
+// bit mask `phases` (bit 0: chunk map, bit 1: intra-chunk, bit 2: carry).
+kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta, const float* h0,
+                          const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                          int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io, void* o,
+                          float* h_final, void* workspace, size_t workspace_bytes_given,
+                          void* stream) {
   const int64_t T = total_tokens;
   if (T < 0 || n_seqs < 1 || heads < 1) return KDA_ERR_SHAPE;
   if (dk != kDim || dv != kDim || !valid_io(io) || heads > 65535) return KDA_ERR_UNSUPPORTED;
@@ -107,10 +114,36 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
   int32_t* chunk_offset = reinterpret_cast<int32_t*>(ws + 256);
   uint8_t* inter = ws + inter_offset(n_seqs);
   const hipError_t err = kda::launch_chunk_fwd(
-      io == KDA_IO_BF16, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, T, heads,
+      phases, io == KDA_IO_BF16, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, T, heads,
       chunk_slots(n_seqs, T), o, h_final, status, chunk_offset, inter,
       static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* beta, const float* h0,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                         int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io, void* o,
+                         float* h_final, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return chunk_fwd_impl(7, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens,
+                        heads, dk, dv, io, o, h_final, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_phase(int32_t phase, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const float* h0,
+                               const int32_t* cu_seqlens, int32_t n_seqs,
+                               int64_t total_tokens, int32_t heads, int32_t dk, int32_t dv,
+                               kda_io_dtype io, void* o, float* h_final, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (phase < 0 || phase > 2) return KDA_ERR_SHAPE;
+  return chunk_fwd_impl(1 << phase, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs,
+                        total_tokens, heads, dk, dv, io, o, h_final, workspace,
+                        workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v,

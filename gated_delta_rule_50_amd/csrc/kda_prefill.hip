@@ -522,16 +522,21 @@ size_t inter_block_bytes(bool bf16_io) {
 
 constexpr int kCarryWaves = 1;
 
-hipError_t launch_chunk_fwd(bool bf16_io, const void* q, const void* k, const void* v,
-                            const float* log_alpha, const float* beta, const float* h0,
-                            const int32_t* cu, int32_t n_seqs, int64_t T, int32_t H,
-                            int64_t n_slots, void* o, float* h_final,
+// phases: bit 0 chunk map, bit 1 intra-chunk, bit 2 carry (all three, in
+// order on one stream, make one prefill call).
+hipError_t launch_chunk_fwd(int phases, bool bf16_io, const void* q, const void* k,
+                            const void* v, const float* log_alpha, const float* beta,
+                            const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
+                            int32_t H, int64_t n_slots, void* o, float* h_final,
                             int32_t* status, int32_t* chunk_offset, uint8_t* inter,
                             hipStream_t stream) {
-  chunk_map_kernel<<<1, 256, 0, stream>>>(cu, n_seqs, T, n_slots, chunk_offset, status);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (T > 0 && n_slots > 0) {
+  hipError_t err = hipSuccess;
+  if (phases & 1) {
+    chunk_map_kernel<<<1, 256, 0, stream>>>(cu, n_seqs, T, n_slots, chunk_offset, status);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if ((phases & 2) && T > 0 && n_slots > 0) {
     dim3 grid((unsigned)n_slots, (unsigned)H);
     if (bf16_io)
       intra_kernel<bf16><<<grid, 256, 0, stream>>>(
@@ -544,6 +549,7 @@ hipError_t launch_chunk_fwd(bool bf16_io, const void* q, const void* k, const vo
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  if (!(phases & 4)) return hipSuccess;
   const int64_t pairs = (int64_t)n_seqs * H;
   const int64_t groups = 8 / kCarryWaves;
   const int64_t nblocks = ((pairs + 7) / 8) * 8 * groups;

@@ -19,8 +19,8 @@ KDA_IO_F32, KDA_IO_BF16 = 0, 1
 CHUNK = 64
 HEAD_DIM = 128
 
-EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_decode_step",
-           "kda_status_string", "kda_version")
+EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_phase",
+           "kda_decode_step", "kda_status_string", "kda_version")
 
 _LIB = None
 
@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                     ctypes.c_int, vp, vp, vp, sz, vp]
         L.kda_chunk_fwd.restype = ctypes.c_int
+        L.kda_chunk_fwd_phase.argtypes = [i32] + L.kda_chunk_fwd.argtypes
+        L.kda_chunk_fwd_phase.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                       ctypes.c_int, vp, vp]
         L.kda_decode_step.restype = ctypes.c_int
@@ -105,41 +107,62 @@ def alloc_workspace(n_seqs, total_tokens, heads, io_dtype, device) -> torch.Tens
     return raw[off:off + nbytes]
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
-              h_final=None, want_final=True, workspace=None, stream=None):
-    """Chunked prefill. Returns (o, h_final or None).
+class Prefill:
+    """Device buffers of one prefill call, marshalled once for repeated use.
 
     q, k [T, H, 128], v [T, H, 128] (bf16 or fp32, one dtype); log_alpha
     [T, H, 128] fp32; beta [T, H] fp32; h0 [N, H, 128, 128] fp32 or None;
     cu_seqlens int32 [N + 1] on the device or None (one sequence). h_final
     may be passed as h0 to continue in place.
     """
-    dev = k.device
-    io = _io(k.dtype)
-    T, H = int(k.shape[0]), int(k.shape[1])
-    N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, k.dtype, dev)
-    _check(log_alpha, "log_alpha", torch.float32, dev)
-    _check(beta, "beta", torch.float32, dev)
-    _check(h0, "h0", torch.float32, dev)
-    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    if o is None:
-        o = torch.empty((T, H, v.shape[2]), dtype=k.dtype, device=dev)
-    _check(o, "o", k.dtype, dev)
-    if h_final is None and want_final:
-        h_final = torch.empty((N, H, k.shape[2], v.shape[2]), dtype=torch.float32, device=dev)
-    _check(h_final, "h_final", torch.float32, dev)
-    if workspace is None:
-        workspace = alloc_workspace(N, T, H, k.dtype, dev)
-    _check(workspace, "workspace", torch.uint8, dev)
-    st = lib().kda_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
-        N, T, H, int(k.shape[2]), int(v.shape[2]), io, _ptr(o), _ptr(h_final),
-        _ptr(workspace), workspace.numel(), _stream(stream, dev))
-    if st != KDA_OK:
-        raise KDAError(st, "kda_chunk_fwd")
-    return o, h_final
+
+    def __init__(self, q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
+                 h_final=None, want_final=True, workspace=None):
+        dev = k.device
+        self.io = _io(k.dtype)
+        self.T, self.H = int(k.shape[0]), int(k.shape[1])
+        self.N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _check(t, n, k.dtype, dev)
+        _check(log_alpha, "log_alpha", torch.float32, dev)
+        _check(beta, "beta", torch.float32, dev)
+        _check(h0, "h0", torch.float32, dev)
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if o is None:
+            o = torch.empty((self.T, self.H, v.shape[2]), dtype=k.dtype, device=dev)
+        _check(o, "o", k.dtype, dev)
+        if h_final is None and want_final:
+            h_final = torch.empty((self.N, self.H, k.shape[2], v.shape[2]),
+                                  dtype=torch.float32, device=dev)
+        _check(h_final, "h_final", torch.float32, dev)
+        if workspace is None:
+            workspace = alloc_workspace(self.N, self.T, self.H, k.dtype, dev)
+        _check(workspace, "workspace", torch.uint8, dev)
+        self.device = dev
+        self.o, self.h_final, self.workspace = o, h_final, workspace
+        self._keep = (q, k, v, log_alpha, beta, h0, cu_seqlens)
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                      _ptr(cu_seqlens), self.N, self.T, self.H, int(k.shape[2]),
+                      int(v.shape[2]), self.io, _ptr(o), _ptr(h_final), _ptr(workspace),
+                      workspace.numel())
+
+    def run(self, stream=None):
+        st = lib().kda_chunk_fwd(*self._args, _stream(stream, self.device))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_chunk_fwd")
+        return self.o, self.h_final
+
+    def run_phase(self, phase: int, stream=None):
+        st = lib().kda_chunk_fwd_phase(int(phase), *self._args, _stream(stream, self.device))
+        if st != KDA_OK:
+            raise KDAError(st, f"kda_chunk_fwd_phase({phase})")
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
+              h_final=None, want_final=True, workspace=None, stream=None):
+    """Chunked prefill (see Prefill for shapes). Returns (o, h_final or None)."""
+    return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
+                   want_final=want_final, workspace=workspace).run(stream)
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):

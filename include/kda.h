@@ -153,6 +153,27 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd_phase - one of the three launches that make up kda_chunk_fwd,
+ * for per-kernel timing and inspection of the workspace.
+ *   phase 0: chunk map (chunk_offset and status from cu_seqlens)
+ *   phase 1: intra-chunk kernel (gate cumsum, UT transform; fills the
+ *            per-chunk blocks of the workspace)
+ *   phase 2: carry kernel (state propagation and chunk outputs; writes o and
+ *            h_final)
+ * Arguments, validation and errors are those of kda_chunk_fwd (an invalid
+ * phase returns KDA_ERR_SHAPE). Phases 0, 1, 2 enqueued in order on one
+ * stream with the same arguments compute exactly what kda_chunk_fwd does.
+ */
+kda_status kda_chunk_fwd_phase(int32_t phase, const void *q, const void *k,
+                               const void *v, const float *log_alpha,
+                               const float *beta, const float *h0,
+                               const int32_t *cu_seqlens, int32_t n_seqs,
+                               int64_t total_tokens, int32_t heads, int32_t dk,
+                               int32_t dv, kda_io_dtype io, void *o,
+                               float *h_final, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * kda_decode_step - one recurrent step for a batch of sequences.
  *
  * For each sequence n and head h, with alpha = exp(log_alpha[n, h]):

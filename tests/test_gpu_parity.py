@@ -119,3 +119,21 @@ def test_decode_steps_small(io):
         tol_o, tol_s = TOL[io]
         assert rel_max_err(host(o), ro) <= tol_o
         assert rel_fro_err(host(S), ref) <= tol_s
+
+
+def test_phases_equal_full_call_and_deterministic():
+    """Phases 0, 1, 2 in order equal kda_chunk_fwd bitwise; repeated calls are
+    bitwise identical (no atomics, fixed reduction orders)."""
+    p = workloads.make_prefill([100, 300], H=4, seed=21, io="bf16", h0_std=0.05)
+    bf = torch.bfloat16
+    args = (dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta),
+            dev(p.h0), dev(p.cu_seqlens, torch.int32))
+    pre = kda.Prefill(*args)
+    o1, h1 = (x.clone() for x in pre.run())
+    for ph in range(3):
+        pre.run_phase(ph)
+    torch.cuda.synchronize()
+    assert torch.equal(pre.o, o1) and torch.equal(pre.h_final, h1)
+    o3, h3 = pre.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o1) and torch.equal(h3, h1)
