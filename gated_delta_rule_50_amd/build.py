@@ -32,7 +32,10 @@ def hipcc() -> str:
 def _flags():
     return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            f"-I{INCLUDE}", f"-I{CSRC}", "-Wall"]
+            f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
+            # keep MFMA accumulators in VGPRs (no AGPR copies around VALU use)
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+            *os.environ.get("KDA_EXTRA_FLAGS", "").split()]
 
 
 def _compile(src: str, verbose: bool) -> Path:

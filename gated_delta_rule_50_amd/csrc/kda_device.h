@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 typedef __bf16 bf16;
@@ -112,6 +114,16 @@ __device__ __forceinline__ void store_frag(float* base, int lane, const Frag<flo
   p[0] = float4{f.v[0], f.v[1], f.v[2], f.v[3]};
   p[1] = float4{f.v[4], f.v[5], f.v[6], f.v[7]};
 }
+// Writes four accumulator values into slots 4*half .. 4*half+3 of a lane's
+// fragment record (the other half belongs to another wave).
+__device__ __forceinline__ void store_half_frag(bf16* base, int lane, int half, floatx4 x) {
+  bf16x4 v;
+  v[0] = (bf16)x[0]; v[1] = (bf16)x[1]; v[2] = (bf16)x[2]; v[3] = (bf16)x[3];
+  *reinterpret_cast<bf16x4*>(base + lane * 8 + 4 * half) = v;
+}
+__device__ __forceinline__ void store_half_frag(float* base, int lane, int half, floatx4 x) {
+  *reinterpret_cast<float4*>(base + lane * 8 + 4 * half) = float4{x[0], x[1], x[2], x[3]};
+}
 __device__ __forceinline__ void load_frag(const bf16* base, int lane, Frag<bf16>& f) {
   f.v = *reinterpret_cast<const bf16x8*>(base + lane * 8);
 }
@@ -128,6 +140,15 @@ __device__ __forceinline__ void store_c4(bf16* base, int lane, floatx4 x) {
 }
 __device__ __forceinline__ void store_c4(float* base, int lane, floatx4 x) {
   *reinterpret_cast<float4*>(base + lane * 4) = float4{x[0], x[1], x[2], x[3]};
+}
+// Four consecutive I/O elements from an accumulator (8 B bf16, 16 B fp32).
+__device__ __forceinline__ void store4_io(bf16* p, floatx4 x) {
+  bf16x4 v;
+  v[0] = (bf16)x[0]; v[1] = (bf16)x[1]; v[2] = (bf16)x[2]; v[3] = (bf16)x[3];
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4_io(float* p, floatx4 x) {
+  *reinterpret_cast<float4*>(p) = float4{x[0], x[1], x[2], x[3]};
 }
 __device__ __forceinline__ floatx4 load_c4(const bf16* base, int lane) {
   bf16x4 v = *reinterpret_cast<const bf16x4*>(base + lane * 4);
