@@ -105,6 +105,15 @@ __device__ __forceinline__ void load4(const float* p, float* out) {
   out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
 }
 
+// Stores a fragment's eight elements contiguously (LDS rows).
+__device__ __forceinline__ void store8(bf16* p, const Frag<bf16>& f) {
+  *reinterpret_cast<bf16x8*>(p) = f.v;
+}
+__device__ __forceinline__ void store8(float* p, const Frag<float>& f) {
+  reinterpret_cast<float4*>(p)[0] = float4{f.v[0], f.v[1], f.v[2], f.v[3]};
+  reinterpret_cast<float4*>(p)[1] = float4{f.v[4], f.v[5], f.v[6], f.v[7]};
+}
+
 // Fragment stores / loads in the lane-major workspace layout.
 __device__ __forceinline__ void store_frag(bf16* base, int lane, const Frag<bf16>& f) {
   *reinterpret_cast<bf16x8*>(base + lane * 8) = f.v;
