@@ -125,7 +125,9 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
  *                   inter_offset = 256 + round_up(4 (N + 1), 256):
  *       XA  16384 E  [-W ; Qt]  as A-fragments, 8 row tiles x 4 k-blocks
  *       KT   8192 E  K'^T       as A-fragments, 8 row tiles x 2 k-blocks
- *       UC  16384 E  [U ; Ut]   as C-fragments, 8 column tiles x 8 row tiles
+ *       UC  16384 E  U and Ut^T as C-fragments, 8 column tiles x 8 row
+ *                    tiles: row tiles 0-3 hold U (rows = token), 4-7 hold
+ *                    Ut^T (rows = value column)
  *       GC   128 f32 gamma_C[c] = exp(g_last[c])
  *   with, inside the chunk (rows i = token position, padded to 64 with
  *   k = v = q = 0, beta = 0, log_alpha = 0):
@@ -135,14 +137,16 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
  *       A_qk  = Tril(sum_c q_i k_t exp(g_i - g_t))
  *       Qt    = Gamma * Q - A_qk W,  Ut = A_qk U,  K'[t][c] = k_t[c] exp(g_last[c] - g_t[c])
  *   so that, from the chunk's start state S, U - W S is the pseudo-value,
- *   O = Qt S + Ut (Eq. 9 regrouped) and the next state is
- *   Diag(gamma_C) S + K'^T (U - W S) (Eq. 8).
+ *   O = Qt S + Ut (Eq. 9 regrouped; computed transposed, O^T = Ut^T +
+ *   S^T Qt^T) and the next state is Diag(gamma_C) S + K'^T (U - W S)
+ *   (Eq. 8).
  *   Fragment maps: an A-fragment (mt, kb) of matrix X gives lane
  *   l = r + 16 g (r < 16, g < 4) the 8 elements X[16 mt + r][32 kb + 4 g + e]
  *   for e < 4 and X[16 mt + r][32 kb + 16 + 4 g + e - 4] for e >= 4; a
- *   C-fragment (jt, mt) of Y gives lane l the 4 elements
- *   Y[16 mt + 4 g + e][16 jt + r]. Fragments are stored lane-major,
- *   A-fragments ordered [mt][kb], C-fragments ordered [jt][mt].
+ *   C-fragment (jt, mt) gives lane l the 4 elements U[16 mt + 4 g + e][16 jt + r]
+ *   for mt < 4 and Ut[16 (mt - 4) + r][16 jt + 4 g + e] for mt >= 4.
+ *   Fragments are stored lane-major, A-fragments ordered [mt][kb],
+ *   C-fragments ordered [jt][mt].
  */
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          const float *log_alpha, const float *beta,

@@ -31,3 +31,57 @@ def rel_fro_err(got, ref):
 # Frobenius error. fp32 I/O: 1e-4 on o and (unstated on the pages, chosen
 # here) 1e-4 on the state; bf16 I/O: 2e-2 on o, 1e-2 on the state.
 TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-2)}
+
+
+# --------------------------------------------------------------- workspace
+# Decoder of the per-(chunk, head) blocks the prefill leaves in its workspace
+# (layout documented in include/kda.h). Test-side only.
+def _split_k(g, e):
+    return 4 * g + e if e < 4 else 16 + 4 * g + (e - 4)
+
+
+def _lane_maps():
+    L = np.arange(64)
+    r, g = L % 16, L // 16
+    return r, g
+
+
+def decode_block(ws_bytes, b, h, H, N, io):
+    """Returns dict(W, Qt, Kp, U, Ut, gC) (float64) of chunk b, head h."""
+    esz = 2 if io == "bf16" else 4
+    block = 40960 * esz + 128 * 4
+    inter = 256 + (4 * (N + 1) + 255) // 256 * 256
+    base = inter + (b * H + h) * block
+    raw = np.frombuffer(ws_bytes, dtype=np.uint8, count=block, offset=base)
+    if io == "bf16":
+        el = (raw[:40960 * 2].view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    else:
+        el = raw[:40960 * 4].view(np.float32)
+    el = el.astype(np.float64)
+    gC = raw[40960 * esz:].view(np.float32).astype(np.float64)
+    r, g = _lane_maps()
+    X = np.zeros((128, 128))
+    for mt in range(8):
+        for kb in range(4):
+            frag = el[((mt * 4 + kb) * 64) * 8:((mt * 4 + kb) * 64 + 64) * 8].reshape(64, 8)
+            for e in range(8):
+                X[16 * mt + r, 32 * kb + np.array([_split_k(gg, e) for gg in g])] = frag[:, e]
+    KT = np.zeros((128, 64))
+    off = 16384
+    for mt in range(8):
+        for kb in range(2):
+            frag = el[off + ((mt * 2 + kb) * 64) * 8:off + ((mt * 2 + kb) * 64 + 64) * 8].reshape(64, 8)
+            for e in range(8):
+                KT[16 * mt + r, 32 * kb + np.array([_split_k(gg, e) for gg in g])] = frag[:, e]
+    U = np.zeros((64, 128))
+    Ut = np.zeros((64, 128))
+    off = 16384 + 8192
+    for jt in range(8):
+        for mt in range(8):
+            frag = el[off + ((jt * 8 + mt) * 64) * 4:off + ((jt * 8 + mt) * 64 + 64) * 4].reshape(64, 4)
+            for e in range(4):
+                if mt < 4:
+                    U[16 * mt + 4 * g + e, 16 * jt + r] = frag[:, e]
+                else:
+                    Ut[16 * (mt - 4) + r, 16 * jt + 4 * g + e] = frag[:, e]
+    return dict(W=-X[:64], Qt=X[64:], Kp=KT.T, U=U, Ut=Ut, gC=gC)

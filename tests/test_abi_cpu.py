@@ -1,0 +1,201 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/kda.h declares, and rejects bad arguments before launching anything.
+
+All pointers here are fake addresses; the argument checks never dereference
+them, and every call below returns before the first HIP call.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "kda.h"
+LIB = ROOT / "gated_delta_rule_50_amd" / "libkda.so"
+
+OK, NULL, SHAPE, UNSUP, WS, ALIAS, HIPERR = range(7)
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not LIB.exists():
+        pytest.skip("libkda.so not built (run python -m gated_delta_rule_50_amd.build)")
+    L = ctypes.CDLL(str(LIB))
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+    L.kda_chunk_fwd_workspace_bytes.restype = sz
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                ctypes.c_int, vp, vp, vp, sz, vp]
+    L.kda_chunk_fwd.restype = ctypes.c_int
+    L.kda_chunk_fwd_phase.argtypes = [i32] + L.kda_chunk_fwd.argtypes
+    L.kda_chunk_fwd_phase.restype = ctypes.c_int
+    L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                  vp, vp]
+    L.kda_decode_step.restype = ctypes.c_int
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_version.restype = i32
+    return L
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
+                     "kda_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_names_match_header():
+    from gated_delta_rule_50_amd import kda
+    assert sorted(kda.EXPORTS) == declared_functions()
+
+
+def test_status_strings_and_version(lib):
+    for s in range(7):
+        assert lib.kda_status_string(s)
+    assert lib.kda_status_string(99) == b"unknown status"
+    assert lib.kda_version() >= 100
+
+
+# ------------------------------------------------------------ workspace size
+def _block_bytes(io):
+    e = 2 if io == BF16 else 4
+    return 40960 * e + 128 * 4
+
+
+@pytest.mark.parametrize("io", [F32, BF16])
+@pytest.mark.parametrize("N,T,H", [(1, 0, 1), (1, 1, 1), (1, 8192, 32), (16, 135000, 32),
+                                   (3, 64, 2), (300, 100000, 4)])
+def test_workspace_formula(lib, io, N, T, H):
+    slots = (T + 63) // 64 + N - 1
+    inter = 256 + (4 * (N + 1) + 255) // 256 * 256
+    assert lib.kda_chunk_fwd_workspace_bytes(N, T, H, 128, 128, io) == inter + slots * H * _block_bytes(io)
+
+
+def test_workspace_invalid(lib):
+    assert lib.kda_chunk_fwd_workspace_bytes(0, 10, 1, 128, 128, BF16) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, -1, 1, 128, 128, BF16) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 10, 0, 128, 128, BF16) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 10, 1, 64, 128, BF16) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 10, 1, 128, 128, 7) == 0
+
+
+# ------------------------------------------------------ prefill validation
+BASE = 0x7F0000000000          # fake, 256-byte aligned, never dereferenced
+MB = 1 << 20
+
+
+def prefill_args(lib, T=100, H=2, N=1, io=BF16, **over):
+    e = 2 if io == BF16 else 4
+    th = T * H
+    a = dict(q=BASE, k=BASE + 1 * 64 * MB, v=BASE + 2 * 64 * MB, log_alpha=BASE + 3 * 64 * MB,
+             beta=BASE + 4 * 64 * MB, h0=BASE + 5 * 64 * MB,
+             cu=(BASE + 6 * 64 * MB) if N != 1 else None, N=N, T=T, H=H, dk=128, dv=128,
+             io=io, o=BASE + 7 * 64 * MB, h_final=BASE + 8 * 64 * MB,
+             ws=BASE + 9 * 64 * MB, ws_bytes=None, stream=None)
+    a.update(over)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.kda_chunk_fwd_workspace_bytes(a["N"] if a["N"] > 0 else 1,
+                                                          max(a["T"], 0), max(a["H"], 1),
+                                                          128, 128, io) or 0
+    assert th * 128 * e < 64 * MB
+    return a
+
+
+def call_prefill(lib, a, phase=None):
+    args = (a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["h0"], a["cu"], a["N"],
+            a["T"], a["H"], a["dk"], a["dv"], a["io"], a["o"], a["h_final"], a["ws"],
+            a["ws_bytes"], a["stream"])
+    if phase is None:
+        return lib.kda_chunk_fwd(*args)
+    return lib.kda_chunk_fwd_phase(phase, *args)
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(T=-1), SHAPE),
+    (dict(N=0), SHAPE),
+    (dict(H=0), SHAPE),
+    (dict(dk=64), UNSUP),
+    (dict(dv=256), UNSUP),
+    (dict(io=5), UNSUP),
+    (dict(H=70000), UNSUP),
+    (dict(q=None), NULL),
+    (dict(beta=None), NULL),
+    (dict(o=None), NULL),
+    (dict(N=2, cu=None), NULL),
+    (dict(ws=None), WS),
+    (dict(ws_bytes=100), WS),
+    (dict(ws=BASE + 9 * 64 * MB + 128), WS),
+])
+def test_prefill_argument_errors(lib, over, expect):
+    a = prefill_args(lib)
+    a.update(over)
+    assert call_prefill(lib, a) == expect
+
+
+def test_prefill_alias_errors(lib):
+    a = prefill_args(lib)
+    assert call_prefill(lib, dict(a, o=a["q"] + 4096)) == ALIAS          # o inside q
+    assert call_prefill(lib, dict(a, h_final=a["o"])) == ALIAS            # h_final = o
+    assert call_prefill(lib, dict(a, h_final=a["h0"] + 1024)) == ALIAS    # partial overlap
+    assert call_prefill(lib, dict(a, ws=a["k"])) == ALIAS                 # workspace over k
+    assert call_prefill(lib, dict(a, o=a["ws"] + 256)) == ALIAS           # o inside workspace
+
+
+def test_prefill_invalid_phase(lib):
+    a = prefill_args(lib)
+    assert call_prefill(lib, a, phase=3) == SHAPE
+    assert call_prefill(lib, a, phase=-1) == SHAPE
+
+
+def test_prefill_large_T_needs_int32_cu(lib):
+    a = prefill_args(lib, N=2)
+    a["T"] = 1 << 31
+    assert call_prefill(lib, a) == SHAPE
+
+
+# ------------------------------------------------------- decode validation
+def call_decode(lib, **over):
+    a = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, la=BASE + 3 * MB, beta=BASE + 4 * MB,
+             S=BASE + 64 * MB, N=4, H=2, dk=128, dv=128, io=BF16, o=BASE + 5 * MB, stream=None)
+    a.update(over)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["la"], a["beta"], a["S"], a["N"],
+                               a["H"], a["dk"], a["dv"], a["io"], a["o"], a["stream"])
+
+
+def test_decode_argument_errors(lib):
+    assert call_decode(lib, N=-1) == SHAPE
+    assert call_decode(lib, H=0) == SHAPE
+    assert call_decode(lib, dk=96) == UNSUP
+    assert call_decode(lib, io=3) == UNSUP
+    assert call_decode(lib, q=None) == NULL
+    assert call_decode(lib, S=None) == NULL
+    assert call_decode(lib, S=BASE + 1024) == ALIAS           # state over q
+    assert call_decode(lib, o=BASE + 64 * MB + 4096) == ALIAS  # o inside the state
+    assert call_decode(lib, o=BASE + 3 * MB + 64) == ALIAS    # o over log_alpha
+
+
+def test_decode_empty_batch_is_a_noop(lib):
+    # returns before any HIP call
+    assert call_decode(lib, N=0, q=None, S=None, o=None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_50_amd import kda
+    x = torch.zeros(4, 2, 128)
+    with pytest.raises(ValueError):
+        kda.decode_step(x, x, x, x, torch.zeros(4, 2), torch.zeros(4, 2, 128, 128))

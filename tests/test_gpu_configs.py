@@ -1,0 +1,81 @@
+"""Parity at the full sizes of the benchmark workloads.
+
+The HIP path runs every head of the full workload; the fp64 oracle checks a
+sample of heads (heads are independent), and for decode a sample of
+sequences, carried over all 64 steps with the oracle's own fp64 state.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gated_delta_rule_50_amd import kda, workloads  # noqa: E402
+from oracle import recurrent  # noqa: E402
+from tests.kda_testutil import TOL, dev, host, io_dtype, rel_fro_err, rel_max_err  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(p):
+    dt = io_dtype(p.io)
+    o, hf = kda.chunk_fwd(dev(p.q, dt), dev(p.k, dt), dev(p.v, dt), dev(p.log_alpha),
+                          dev(p.beta), None if p.h0 is None else dev(p.h0),
+                          dev(p.cu_seqlens, torch.int32))
+    torch.cuda.synchronize()
+    return o, hf
+
+
+def _check_heads(p, o, hf, heads, per_sequence=False):
+    o_h = o[:, heads].float().cpu().numpy().astype(np.float64)
+    hf_h = hf[:, heads].cpu().numpy().astype(np.float64)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(hf).all()
+    ro, rh = recurrent.forward(p.q[:, heads], p.k[:, heads], p.v[:, heads],
+                               p.log_alpha[:, heads], p.beta[:, heads],
+                               None if p.h0 is None else p.h0[:, heads], p.cu_seqlens)
+    tol_o, tol_s = TOL[p.io]
+    eo, es = rel_max_err(o_h, ro), rel_fro_err(hf_h, rh)
+    print(f"heads {heads}: o err {eo:.3e}, state err {es:.3e}")
+    assert eo <= tol_o and es <= tol_s
+    if per_sequence:
+        for n in range(p.N):
+            e_n = rel_fro_err(hf_h[n], rh[n])
+            assert e_n <= tol_s, (n, e_n)
+
+
+def test_config2_long_context_strong_decay():
+    """T = 131072, 2048 chunk carries, half the channels decaying by
+    e^-16..e^-64 per chunk, nonzero h0."""
+    p = workloads.config(2).prefill()
+    o, hf = _prefill(p)
+    _check_heads(p, o, hf, [0, 17, 31])
+
+
+def test_config3_packed_variable_length():
+    p = workloads.config(3).prefill()
+    assert p.N == 16 and 512 <= np.diff(p.cu_seqlens).min() and np.diff(p.cu_seqlens).max() <= 16384
+    o, hf = _prefill(p)
+    _check_heads(p, o, hf, [0, 13, 31], per_sequence=True)
+
+
+def test_config4_decode_64_steps():
+    cfg = workloads.config(4)
+    N, H = cfg.n_seqs, cfg.H
+    S0 = workloads.make_decode_state(N, H, cfg.seed)
+    S = dev(S0)
+    sample = np.arange(0, N, 16)            # 16 of the 256 sequences, all heads
+    ref = S0[sample].astype(np.float64)
+    bf = torch.bfloat16
+    worst_o = worst_s = 0.0
+    for step in range(cfg.steps):
+        d = workloads.make_decode_step(N, H, cfg.seed, step, io=cfg.io)
+        o = kda.decode_step(dev(d.q, bf), dev(d.k, bf), dev(d.v, bf), dev(d.log_alpha),
+                            dev(d.beta), S)
+        torch.cuda.synchronize()
+        ro, ref = recurrent.decode_step(d.q[sample], d.k[sample], d.v[sample],
+                                        d.log_alpha[sample], d.beta[sample], ref)
+        eo = rel_max_err(host(o[sample]), ro)
+        es = rel_fro_err(S[sample].cpu().numpy().astype(np.float64), ref)
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1], (step, eo, es)
+        assert torch.isfinite(o.float()).all()
+    print(f"decode worst over 64 steps: o {worst_o:.3e}, state {worst_s:.3e}")
