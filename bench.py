@@ -17,14 +17,21 @@ per step; every kernel's figures are under ``kernels``.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
 import time
+from pathlib import Path
 
 import numpy as np
 
 METRIC = "KDA prefill tokens/s (H=32,d=128,T=8K) + decode tokens/s; % MFMA/HBM peak"
+ROOT = Path(__file__).resolve().parent
+TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_bench_step.txt"
+COPY_BYTES = 1 << 30        # the calibration copy reads and writes 1 GiB
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 D, C = 128, 64
@@ -51,8 +58,78 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy (counter scale factor)")
+                    help="also run a plain 1 GiB device copy first (counter scale factor)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script with --copy-calibration into the traffic summary text")
     return ap.parse_args()
+
+
+def sources_hash() -> str:
+    """Hash of the kernel sources: counter readings apply only to this code."""
+    h = hashlib.sha256()
+    for f in sorted((ROOT / "gated_delta_rule_50_amd" / "csrc").glob("*")):
+        h.update(f.name.encode())
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def _kernel_key(name):
+    for k in ("intra", "carry", "decode", "chunk_map"):
+        if k in name:
+            return k
+    low = name.lower()
+    # torch's device-to-device copy kernel (not the runtime's host copies)
+    return "copy" if ("copy" in low and "rocclr" not in low) else None
+
+
+def _pmc_means(run_dir, counter):
+    """Mean counter value (KiB) per dispatch of each kernel in one pmc run."""
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            k = _kernel_key(row["Kernel_Name"])
+            if k is None:
+                continue
+            per.setdefault(k, {}).setdefault(row["Dispatch_Id"], 0.0)
+            per[k][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    f, w = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
+    # the largest 'copy' dispatch is the 1 GiB calibration copy
+    fr = COPY_BYTES / (f["copy"] * 1024.0)
+    wr = COPY_BYTES / (w["copy"] * 1024.0)
+    lines = [f"sources_sha256 = {sources_hash()}",
+             f"copy_read_factor = {fr:.6f}", f"copy_write_factor = {wr:.6f}"]
+    for k in ("chunk_map", "intra", "carry", "decode"):
+        if k in f and k in w:
+            lines.append(f"{k}_fetch_KiB = {f[k]:.1f}")
+            lines.append(f"{k}_write_KiB = {w[k]:.1f}")
+    print("\n".join(lines))
+
+
+def load_traffic():
+    """Scaled HBM bytes per launch for each kernel, or {} if the committed
+    counter readings were taken on other kernel sources."""
+    if not TRAFFIC_FILE.exists():
+        return {}
+    kv = {}
+    for line in TRAFFIC_FILE.read_text().splitlines():
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = (x.strip() for x in line.split("=", 1))
+            kv[key] = val
+    if kv.get("sources_sha256") != sources_hash():
+        return {}
+    fr, wr = float(kv["copy_read_factor"]), float(kv["copy_write_factor"])
+    out = {}
+    for k in ("intra", "carry", "decode"):
+        if f"{k}_fetch_KiB" in kv:
+            out[k] = (float(kv[f"{k}_fetch_KiB"]) * fr + float(kv[f"{k}_write_KiB"]) * wr) * 1024
+    return out
 
 
 def _events(torch, n):
@@ -60,14 +137,15 @@ def _events(torch, n):
 
 
 def copy_calibration(torch):
-    """A plain copy of 1 GiB, three times: read 1 GiB, write 1 GiB each."""
-    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    """A plain device copy of 1 GiB (reads 1 GiB, writes 1 GiB), three times,
+    so hardware byte counters can be scaled against a known transfer."""
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": a.numel() * 4, "repeats": 3}))
+    del a, b
 
 
 def cpu_baseline(p, seconds):
@@ -100,6 +178,9 @@ def cpu_baseline(p, seconds):
 
 def main():
     args = _parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}): the "
@@ -113,7 +194,6 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(torch)
-        return
 
     from gated_delta_rule_50_amd import Prefill, decode_step, lib, workloads
     lib()  # fail loudly if the HIP library is missing
@@ -187,10 +267,14 @@ def main():
             gbps = kdesc["alg_bytes"] / (kdesc["mean_us"] * 1e-6) / 1e9
             kdesc["achieved_GBps"] = gbps
             kdesc["frac"] = gbps / HBM_PEAK_GBPS
+    traffic = load_traffic()
+    for n, b in traffic.items():
+        kernels[n]["traffic_bytes"] = b
     dom = max(("intra", "carry", "decode"), key=lambda n: kernels[n]["mean_us"])
     kd = kernels[dom]
     roofline = {"bound": "hbm", "achieved": kd["achieved_GBps"], "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": kd["frac"], "traffic": None, "kernel": dom}
+                "unit": "GB/s", "frac": kd["frac"], "traffic": traffic.get(dom),
+                "kernel": dom}
 
     pre_bytes = th * PREFILL_BYTES + nh * STATE_BYTES
     t_roof = max(pre_bytes / (HBM_PEAK_GBPS * 1e9), th * FLOPS_EQ13 / (BF16_PEAK_TFLOPS * 1e12))
