@@ -88,597 +88,514 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(
 }
 
 // ----------------------------------------------------------- intra-chunk
+// One workgroup per (chunk, head); two fit on a CU (LDS <= 80 KiB, <= 128
+// VGPRs), so one workgroup's loads overlap the other's compute.
 constexpr int kIntraThreads = 512;   // 8 waves
-constexpr int kGS = kD + 4;          // LDS row stride of g (floats)
-constexpr int kLS = kC + 4;          // LDS row stride of the 64 x 64 fp32 matrices
-constexpr int kTS = 20;              // LDS row stride of 16 x 16 scratch blocks
-constexpr int kBS = kC + 8;          // LDS row stride of the bf16 copies of Ti and P
+constexpr int kLS = kC + 4;          // row stride (floats) of the 64 x 64 fp32 buffers
+constexpr int kTS = 20;              // row stride of 16 x 16 fp32 scratch blocks
 
-// Staging layout of one chunk's q / k / v rows in LDS.
+// Staged rows: 128 elements per row, no padding; 16-byte pieces are XOR
+// swizzled by the row (piece p of row i sits at p ^ (i & 15) for bf16, at
+// p ^ (i & 31) for fp32) so row reads, column gathers and row writes by
+// lanes of different rows hit different banks.
 template <class E>
-struct Stage {
-  static constexpr int kRS = kD + 16 / (int)sizeof(E);   // 16-byte pad per row
-  static constexpr bool kStageV = sizeof(E) == 2;        // fp32 v is read from global
-  static constexpr int kPer16 = 16 / (int)sizeof(E);      // elements per 16 bytes
-  static constexpr int kRow16 = kD / kPer16;              // 16-byte pieces per row
-  static constexpr int kPieces = kC * kRow16 / kIntraThreads;  // per thread, per tensor
-  static constexpr int kLA = kC * (kD / 4) / kIntraThreads;    // float4 of log alpha
+struct Rows {
+  static constexpr int kPer16 = 16 / (int)sizeof(E);   // elements per piece
+  static constexpr int kPieces = kD / kPer16;           // pieces per row
+  __device__ static int at(int i, int c) {               // element offset of (i, c)
+    const int p = (c / kPer16) ^ (i & (kPieces - 1));
+    return i * kD + p * kPer16 + c % kPer16;
+  }
 };
 
-// 16-byte vector of I/O elements (8 bf16 or 4 fp32).
+// 64 x 64 bf16 matrix, 8 pieces per row, swizzled the same way.
+__device__ __forceinline__ int mat_at(int i, int c) {
+  return i * kC + (((c >> 3) ^ (i & 7)) << 3) + (c & 7);
+}
+
 template <class E>
 using Vec16 = typename std::conditional<sizeof(E) == 2, bf16x8, float4>::type;
 
-// acc += A (16x16) * B (16x16), fp32, operands in LDS (row strides lda, ldb).
-__device__ __forceinline__ floatx4 blk16(floatx4 acc, const float* A, int lda,
-                                         const float* B, int ldb, int r, int g) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    acc = mma4(acc, A[r * lda + 4 * s + g], B[(4 * s + g) * ldb + r]);
-  return acc;
-}
-
-// Workgroup barrier that waits for this wave's LDS traffic only: outstanding
-// global loads (the next chunk's prefetch) and stores stay in flight.
+// Workgroup barrier that waits for this wave's LDS traffic only (outstanding
+// global stores stay in flight).
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unchanged
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Eight consecutive elements of an LDS row as an MFMA operand fragment.
+// Eight consecutive elements as an MFMA fragment.
 __device__ __forceinline__ void lds_frag(const bf16* p, Frag<bf16>& f) {
   f.v = *reinterpret_cast<const bf16x8*>(p);
 }
-__device__ __forceinline__ void lds_frag(const float* p, Frag<float>& f) {
-  load8(p, f.v);
-}
+__device__ __forceinline__ void lds_frag(const float* p, Frag<float>& f) { load8(p, f.v); }
 
-// One chunk-head's inputs, prefetched into registers.
-template <class E>
-struct ChunkIn {
-  Vec16<E> k[Stage<E>::kPieces], q[Stage<E>::kPieces];
-  Vec16<E> v[Stage<E>::kStageV ? Stage<E>::kPieces : 1];
-  float4 la[Stage<E>::kLA];
-  float beta;
-};
-
-struct ChunkPos {
-  int b, h, len;
-  int64_t tok0;
-};
-
-__device__ __forceinline__ ChunkPos chunk_pos(int64_t item, int H, const int32_t* cu,
-                                              const int32_t* chunk_offset, int n_seqs,
-                                              int64_t T) {
-  ChunkPos c;
-  c.b = (int)(item / H);
-  c.h = (int)(item % H);
-  int lo = 0, hi = n_seqs;  // chunk_offset[lo] <= b < chunk_offset[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (chunk_offset[mid] <= c.b) lo = mid; else hi = mid;
-  }
-  const int64_t seq_start = cu ? cu[lo] : 0, seq_end = cu ? cu[lo + 1] : T;
-  c.tok0 = seq_start + (int64_t)(c.b - chunk_offset[lo]) * kC;
-  c.len = (int)min((int64_t)kC, seq_end - c.tok0);
-  return c;
+// Element (r, k) of a 16 x 16 block of Ti, stored strictly lower in `M`
+// (row stride kLS) with an implied unit diagonal and zero upper part.
+__device__ __forceinline__ float ti_at(const float* M, int R, int K) {
+  return K < R ? M[R * kLS + K] : (K == R ? 1.f : 0.f);
 }
 
 template <class E>
-__device__ __forceinline__ void load_chunk(ChunkIn<E>& in, const ChunkPos& c, int t,
-                                           const E* q, const E* k, const E* v,
-                                           const float* log_alpha, const float* beta, int H) {
-  using St = Stage<E>;
-  const Vec16<E> zero16 = {};
-  auto row = [&](int i) -> int64_t { return ((c.tok0 + i) * H + c.h) * (int64_t)kD; };
-#pragma unroll
-  for (int u = 0; u < St::kPieces; ++u) {
-    const int pc = t + u * kIntraThreads, i = pc / St::kRow16, col = (pc % St::kRow16) * St::kPer16;
-    in.k[u] = i < c.len ? *reinterpret_cast<const Vec16<E>*>(k + row(i) + col) : zero16;
-    in.q[u] = i < c.len ? *reinterpret_cast<const Vec16<E>*>(q + row(i) + col) : zero16;
-    if constexpr (St::kStageV)
-      in.v[u] = i < c.len ? *reinterpret_cast<const Vec16<E>*>(v + row(i) + col) : zero16;
-  }
-#pragma unroll
-  for (int u = 0; u < St::kLA; ++u) {
-    const int pc = t + u * kIntraThreads, i = pc / (kD / 4), col = (pc % (kD / 4)) * 4;
-    in.la[u] = i < c.len ? *reinterpret_cast<const float4*>(log_alpha + row(i) + col)
-                         : float4{0.f, 0.f, 0.f, 0.f};
-  }
-  in.beta = (t < kC && t < c.len) ? beta[(c.tok0 + t) * H + c.h] : 0.f;
-}
-
-// Persistent over (chunk, head) items: while one item is computed, the next
-// one's inputs are already on their way into registers.
-template <class E>
-__global__ __launch_bounds__(kIntraThreads) void intra_kernel(
+__global__ __launch_bounds__(kIntraThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_offset,
     const int32_t* __restrict__ status, int32_t n_seqs, int64_t T, int32_t H,
     uint8_t* __restrict__ inter) {
-  using St = Stage<E>;
-  constexpr int RS = St::kRS;
-  constexpr bool kStageV = St::kStageV;
+  using R = Rows<E>;
   // LDS, by lifetime:
-  //   rA   g (steps 0-2), then the bf16 Ti / P copies and 16x16 scratch
-  //   sK   k, then Kr = k exp(g - g_s)        (row factor, s = block start)
+  //   sK   k, then Kr = k exp(g - g_s)          (s = first row of the 16-row block)
   //   sQ   q, then Qr = q exp(g - g_s)
-  //   sV   v, then beta v                      (bf16 only)
-  //   rE   Kf = k exp(g_e - g) (steps 1-2, e = block end), then Ti | A_qk
-  //   sL   L, then P = A_qk Ti
-  //   sF   per block / block pair / channel factors
-  __shared__ __attribute__((aligned(16))) float rA[kC * kGS];
-  __shared__ __attribute__((aligned(16))) E sK[kC * RS];
-  __shared__ __attribute__((aligned(16))) E sQ[kC * RS];
-  __shared__ __attribute__((aligned(16))) E sV[kStageV ? kC * RS : 8];
-  __shared__ __attribute__((aligned(16))) float rE[2 * kC * kLS];
-  __shared__ __attribute__((aligned(16))) float sL[kC * kLS];
+  //   rM   Kf = k exp(g_e - g) (e = last row of the block), until the A tiles
+  //        are done; then M1 = [L strictly lower | A_qk^T upper + diagonal]
+  //        and M2 = [Ti strictly lower | P^T upper + diagonal]; after P, M1's
+  //        storage takes the bf16 copies of Ti and P (bf16 I/O)
+  //   sF   per block / block-pair / channel factors
+  //   sX   per (block, channel) sums of log alpha, later 16 x 16 scratch
+  __shared__ __attribute__((aligned(16))) E sK[kC * kD];
+  __shared__ __attribute__((aligned(16))) E sQ[kC * kD];
+  __shared__ __attribute__((aligned(16))) float rM[2 * kC * kLS];
   __shared__ __attribute__((aligned(16))) float sF[(4 + 4 + 10) * kD];
+  __shared__ __attribute__((aligned(16))) float sX[3 * 16 * kTS];
   __shared__ float sb[kC];
-  float* const sg = rA;
-  E* const sKf = reinterpret_cast<E*>(rE);
-  float* const sTi = rE;
-  float* const sAqk = rE + kC * kLS;
-  float* const sEs = sF;              // exp(g_s[c]) per block start s
-  float* const sEc = sF + 4 * kD;     // exp(g_C[c] - g_e[c]) per block end e
-  float* const sDf = sF + 8 * kD;     // exp(g_{s_I}[c] - g_{e_J}[c]), pair index below
-  bf16* const sTib = reinterpret_cast<bf16*>(rA);            // bf16 Ti, rows of kBS
-  bf16* const sPb = reinterpret_cast<bf16*>(rA) + kC * kBS;  // bf16 P
-  float* const stmp = rA + kC * kBS;                         // after both bf16 copies
+  E* const sKf = reinterpret_cast<E*>(rM);
+  float* const M1 = rM;
+  float* const M2 = rM + kC * kLS;
+  bf16* const sTib = reinterpret_cast<bf16*>(rM);
+  bf16* const sPb = reinterpret_cast<bf16*>(rM) + kC * kC;
+  float* const sEs = sF;              // exp(g_s[c]) per block
+  float* const sEc = sF + 4 * kD;     // exp(g_C[c] - g_e[c]) per block
+  float* const sDf = sF + 8 * kD;     // exp(g_{s_I}[c] - g_{e_J}[c]), J <= I
+  float* const xTot = sX;             // per-block sums of log alpha (4 x 128)
+  float* const stmp = sX;             // 3 scratch blocks (after the exchange)
 
   if (status[0] != 0) return;
-  const int64_t n_items = (int64_t)chunk_offset[n_seqs] * H;
-  int64_t item = blockIdx.x;
-  if (item >= n_items) return;
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int total = chunk_offset[n_seqs];
+  if (b >= total) return;
+  int lo = 0, hi = n_seqs;  // chunk_offset[lo] <= b < chunk_offset[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunk_offset[mid] <= b) lo = mid; else hi = mid;
+  }
+  const int64_t seq_start = cu ? cu[lo] : 0, seq_end = cu ? cu[lo + 1] : T;
+  const int64_t tok0 = seq_start + (int64_t)(b - chunk_offset[lo]) * kC;
+  const int len = (int)min((int64_t)kC, seq_end - tok0);
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int r = lane & 15, g = lane >> 4;
-  // block pair (I, J <= I) -> index into sDf
+  auto row = [&](int i) -> int64_t { return ((tok0 + i) * H + h) * (int64_t)kD; };
   auto pidx = [](int I, int J) { return I * (I + 1) / 2 + J; };
 
-  ChunkIn<E> in;
-  ChunkPos cp = chunk_pos(item, H, cu, chunk_offset, n_seqs, T);
-  load_chunk<E>(in, cp, t, q, k, v, log_alpha, beta, H);
+  E* blk = reinterpret_cast<E*>(inter + ((int64_t)b * H + h) * Inter<E>::kBytes);
+  E* XA = blk + Inter<E>::kXA;
+  E* KT = blk + Inter<E>::kKT;
+  E* UC = blk + Inter<E>::kUC;
+  float* GC = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(blk) + Inter<E>::kGCByte);
 
-  for (; item < n_items; item += gridDim.x) {
-    const int len = cp.len, h = cp.h;
-    const int64_t tok0 = cp.tok0;
-    E* blk = reinterpret_cast<E*>(inter + ((int64_t)cp.b * H + h) * Inter<E>::kBytes);
-    E* XA = blk + Inter<E>::kXA;
-    E* KT = blk + Inter<E>::kKT;
-    E* UC = blk + Inter<E>::kUC;
-    float* GC = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(blk) + Inter<E>::kGCByte);
-
-    // ---- 0. stage this chunk (rows past the sequence end are zeros, i.e.
-    //         identity tokens), then start fetching the next one.
+  // ---- 0. loads, all issued up front. k and q rows go to LDS; each thread
+  //         keeps one channel c of one 16-row block of log alpha.
+  const int cch = t & 127, seg = t >> 7;       // channel, 16-row block
+  float la[16];
+  {
+    constexpr int kPer = kC * R::kPieces / kIntraThreads;
+    Vec16<E> vk[kPer], vq[kPer];
+    const Vec16<E> zero16 = {};
+    // Rows past the sequence end (identity tokens) are loaded from the last
+    // valid row and replaced by zeros with a select: no branches, no
+    // out-of-range addresses (a chunk always has len >= 1).
 #pragma unroll
-    for (int u = 0; u < St::kPieces; ++u) {
-      const int pc = t + u * kIntraThreads, i = pc / St::kRow16, c = (pc % St::kRow16) * St::kPer16;
-      *reinterpret_cast<Vec16<E>*>(&sK[i * RS + c]) = in.k[u];
-      *reinterpret_cast<Vec16<E>*>(&sQ[i * RS + c]) = in.q[u];
-      if constexpr (kStageV) *reinterpret_cast<Vec16<E>*>(&sV[i * RS + c]) = in.v[u];
+    for (int u = 0; u < kPer; ++u) {
+      const int pc = t + u * kIntraThreads, i = pc / R::kPieces, c = (pc % R::kPieces) * R::kPer16;
+      const int ic = min(i, len - 1);
+      const Vec16<E> a = *reinterpret_cast<const Vec16<E>*>(k + row(ic) + c);
+      const Vec16<E> b2 = *reinterpret_cast<const Vec16<E>*>(q + row(ic) + c);
+      vk[u] = i < len ? a : zero16;
+      vq[u] = i < len ? b2 : zero16;
     }
 #pragma unroll
-    for (int u = 0; u < St::kLA; ++u) {
-      const int pc = t + u * kIntraThreads, i = pc / (kD / 4), c = (pc % (kD / 4)) * 4;
-      *reinterpret_cast<float4*>(&sg[i * kGS + c]) = in.la[u];
+    for (int ii = 0; ii < 16; ++ii) {
+      const int i = 16 * seg + ii;
+      const float x = log_alpha[row(min(i, len - 1)) + cch];
+      la[ii] = i < len ? x : 0.f;
     }
-    if (t < kC) sb[t] = in.beta;
-    lds_barrier();
+    if (t < kC) {
+      const float x = beta[(tok0 + min(t, len - 1)) * H + h];
+      sb[t] = t < len ? x : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pc = t + u * kIntraThreads, i = pc / R::kPieces, c = (pc % R::kPieces) * R::kPer16;
+      *reinterpret_cast<Vec16<E>*>(&sK[R::at(i, c)]) = vk[u];
+      *reinterpret_cast<Vec16<E>*>(&sQ[R::at(i, c)]) = vq[u];
+    }
+  }
 
-    // ---- 1. gate: g = inclusive cumsum of log alpha along the chunk, in
-    //         four 16-row segments per channel plus segment offsets.
+  // ---- 1. gate: in-register cumsum of this thread's 16 log alphas, block
+  //         offsets through LDS, then g_i for the thread's rows.
+#pragma unroll
+  for (int ii = 1; ii < 16; ++ii) la[ii] += la[ii - 1];
+  xTot[seg * kD + cch] = la[15];
+  lds_barrier();
+  {
+    float off = 0.f;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) off += u < seg ? xTot[u * kD + cch] : 0.f;
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) la[ii] += off;          // la[] now holds g
+  }
+  // ---- 1b. decay factors for this thread's rows (each element once):
+  //          Kr = k exp(g - g_s), Qr = q exp(g - g_s), Kf = k exp(g_e - g),
+  //          all <= 1 in magnitude times the input. Per block and block pair:
+  //          exp(g_s), exp(g_C - g_e), D_IJ = exp(g_{s_I} - g_{e_J}) (<= 1 for
+  //          J < I), with g at a block's last row = sum of the block sums
+  //          up to it.
+#pragma unroll
+  for (int ii = 0; ii < 16; ++ii) {
+    const int i = 16 * seg + ii, o = R::at(i, cch);
+    const float fr = exp_f(la[ii] - la[0]);
+    const float fc = exp_f(la[15] - la[ii]);
+    const float kv = to_f(sK[o]);
+    sK[o] = from_f<E>(kv * fr);
+    sQ[o] = from_f<E>(to_f(sQ[o]) * fr);
+    sKf[o] = from_f<E>(kv * fc);
+  }
+  {
+    float ge[4];
+    ge[0] = xTot[cch];
+#pragma unroll
+    for (int J = 1; J < 4; ++J) ge[J] = ge[J - 1] + xTot[J * kD + cch];
+    sEs[seg * kD + cch] = exp_f(la[0]);
+    sEc[seg * kD + cch] = exp_f(ge[3] - la[15]);
+    if (seg == 3) GC[cch] = exp_f(ge[3]);
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+      if (J <= seg) sDf[pidx(seg, J) * kD + cch] = exp_f(fminf(la[0] - ge[J], 88.f));
+  }
+  lds_barrier();
+
+  // ---- 2. A_kk (strict) and A_qk (inclusive) on 16 x 16 blocks (I, J):
+  //         waves 0-3 (3, w); 4-5 (2, w-4); 6 (2,2)+(0,0); 7 (1,0)+(1,1).
+  //         Column factor of pair (I, J): Kf * D_IJ. A diagonal block whose
+  //         D could exceed e^44 is recomputed exactly from the raw inputs.
+  auto pair = [&](int u, int& I, int& J) {
+    if (w < 4) { I = u == 0 ? 3 : -1; J = w; }
+    else if (w < 6) { I = u == 0 ? 2 : -1; J = w - 4; }
+    else if (w == 6) { I = u == 0 ? 2 : 0; J = I; }
+    else { I = 1; J = u; }
+  };
+  floatx4 akk[2], aqk[2];
+  {
+    bool wide[2] = {false, false};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      akk[u] = zero4();
+      aqk[u] = zero4();
+      int I, J;
+      pair(u, I, J);
+      if (I < 0) continue;
+      const int Rw = 16 * I + r, i = 16 * J + r;
+      const float* D = sDf + pidx(I, J) * kD;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int c0 = 32 * kb + 8 * g;
+        Frag<E> fk, fq, fb;
+        if constexpr (sizeof(E) == 2) {
+          lds_frag(&sK[R::at(Rw, c0)], fk);
+          lds_frag(&sQ[R::at(Rw, c0)], fq);
+        } else {
+          float a8[8], b8[8];
+          load4(&sK[R::at(Rw, c0)], a8); load4(&sK[R::at(Rw, c0 + 4)], a8 + 4);
+          load4(&sQ[R::at(Rw, c0)], b8); load4(&sQ[R::at(Rw, c0 + 4)], b8 + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { fk.set(e, a8[e]); fq.set(e, b8[e]); }
+        }
+        float kf[8];
+        if constexpr (sizeof(E) == 2) {
+          load8(&sKf[R::at(i, c0)], kf);
+        } else {
+          load4(&sKf[R::at(i, c0)], kf); load4(&sKf[R::at(i, c0 + 4)], kf + 4);
+        }
+        const float4 d0 = *reinterpret_cast<const float4*>(D + c0);
+        const float4 d1 = *reinterpret_cast<const float4*>(D + c0 + 4);
+        const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (J == I && dd[e] > 1.2851e19f) wide[u] = true;   // e^44
+          fb.set(e, kf[e] * dd[e]);
+        }
+        akk[u] = mma(akk[u], fk, fb);
+        aqk[u] = mma(aqk[u], fq, fb);
+      }
+    }
+    // K'^T fragments (K'_i = k_i exp(g_C - g_i) = Kf_i exp(g_C - g_e)) for
+    // the sequential kernel: wave w owns channels [16 w, 16 w + 16), token
+    // index in the split order.
     {
-      const int c = t & 127, seg = t >> 7;
-      float acc = 0.f;
+      const int cc = 16 * w + r;
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        acc += sg[(16 * seg + ii) * kGS + c];
-        sg[(16 * seg + ii) * kGS + c] = acc;
-      }
-      lds_barrier();
-      float off = 0.f;
+      for (int kb = 0; kb < 2; ++kb) {
+        const float ec0 = sEc[(2 * kb) * kD + cc], ec1 = sEc[(2 * kb + 1) * kD + cc];
+        Frag<E> fkt;
 #pragma unroll
-      for (int u = 0; u < 3; ++u) off += u < seg ? sg[(16 * u + 15) * kGS + c] : 0.f;
-      lds_barrier();
-      if (seg > 0) {
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) sg[(16 * seg + ii) * kGS + c] += off;
+        for (int e = 0; e < 8; ++e) {
+          const int i = 32 * kb + split_k(g, e);
+          fkt.set(e, (e < 4 ? ec0 : ec1) * to_f(sKf[R::at(i, cc)]));
+        }
+        store_frag(KT + (w * 2 + kb) * kWave * 8, lane, fkt);
       }
     }
-    lds_barrier();
-
-    // ---- 1b. decay factors, each computed once. For row r in 16-row block
-    //          with start s and end e: row factor exp(g_r - g_s) <= 1 and
-    //          column factor exp(g_e - g_r) <= 1. The column factor of block
-    //          pair (I, J) is exp(g_{s_I} - g_r) = Kf_r * D_IJ with
-    //          D_IJ = exp(g_{s_I} - g_{e_J}): <= 1 for J < I; for J = I it
-    //          can be large, and past e^44 the block is recomputed exactly.
-    {
-      // eight consecutive channels of one row per step
-#pragma unroll 1
-      for (int u = 0; u < kC * kD / 8 / kIntraThreads; ++u) {
-        const int x = t + u * kIntraThreads, i = x >> 4, c0 = (x & 15) * 8;
-        const int s = i & ~15, e = s + 15;
-        float gi[8], gs[8], ge[8], kv[8], qv[8], fr[8], fc[8];
-        load8(&sg[i * kGS + c0], gi);
-        load8(&sg[s * kGS + c0], gs);
-        load8(&sg[e * kGS + c0], ge);
-        load8(&sK[i * RS + c0], kv);
-        load8(&sQ[i * RS + c0], qv);
 #pragma unroll
-        for (int z = 0; z < 8; ++z) {
-          fr[z] = exp_f(gi[z] - gs[z]);
-          fc[z] = exp_f(ge[z] - gi[z]);
-        }
-        Frag<E> a, b2, c2;
+    for (int u = 0; u < 2; ++u) {
+      int I, J;
+      pair(u, I, J);
+      if (I < 0 || J != I || !__ballot(wide[u])) continue;
+      // exact diagonal block: entries (Rr = 16 I + 4 g + e, i = 16 I + r),
+      // g differences summed from the raw log alphas
 #pragma unroll
-        for (int z = 0; z < 8; ++z) {
-          a.set(z, kv[z] * fr[z]);
-          b2.set(z, qv[z] * fr[z]);
-          c2.set(z, kv[z] * fc[z]);
-        }
-        store8(&sK[i * RS + c0], a);
-        store8(&sQ[i * RS + c0], b2);
-        store8(&sKf[i * RS + c0], c2);
-        if constexpr (kStageV) {
-          float vv[8];
-          load8(&sV[i * RS + c0], vv);
-          const float bi = sb[i];
-          Frag<E> d2;
-#pragma unroll
-          for (int z = 0; z < 8; ++z) d2.set(z, vv[z] * bi);
-          store8(&sV[i * RS + c0], d2);
-        }
-      }
-      if (t < kD) {
-        const int c = t;
-        const float gC = sg[(kC - 1) * kGS + c];
-        GC[c] = exp_f(gC);
-#pragma unroll
-        for (int bI = 0; bI < 4; ++bI) {
-          sEs[bI * kD + c] = exp_f(sg[(16 * bI) * kGS + c]);
-          sEc[bI * kD + c] = exp_f(gC - sg[(16 * bI + 15) * kGS + c]);
-        }
-      } else if (t < 2 * kD) {
-        const int c = t - kD;
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int J = 0; J <= I; ++J)
-            sDf[pidx(I, J) * kD + c] = exp_f(fminf(sg[(16 * I) * kGS + c] - sg[(16 * J + 15) * kGS + c], 88.f));
-      }
-    }
-    lds_barrier();
-
-    // ---- 2. A_kk (strict) and A_qk (inclusive) on 16 x 16 blocks (I, J):
-    //         waves 0-3 (3, w); 4-5 (2, w-4); 6 (2,2)+(0,0); 7 (1,0)+(1,1).
-    //         Accumulators stay in registers across the barrier that ends
-    //         the reads of Kf (whose storage becomes Ti / A_qk).
-    floatx4 akk[2], aqk[2];
-    {
-      auto pair = [&](int u, int& I, int& J) {
-        if (w < 4) { I = u == 0 ? 3 : -1; J = w; }
-        else if (w < 6) { I = u == 0 ? 2 : -1; J = w - 4; }
-        else if (w == 6) { I = u == 0 ? 2 : 0; J = I; }
-        else { I = 1; J = u; }
-      };
-      bool wide[2] = {false, false};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        akk[u] = zero4();
-        aqk[u] = zero4();
-        int I, J;
-        pair(u, I, J);
-        if (I < 0) continue;
-        const int R = 16 * I + r, i = 16 * J + r;
-        const float* D = sDf + pidx(I, J) * kD;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int c0 = 32 * kb + 8 * g;
-          Frag<E> fk, fq, fb;
-          lds_frag(&sK[R * RS + c0], fk);
-          lds_frag(&sQ[R * RS + c0], fq);
-          float kf[8];
-          load8(&sKf[i * RS + c0], kf);
-          const float4 d0 = *reinterpret_cast<const float4*>(D + c0);
-          const float4 d1 = *reinterpret_cast<const float4*>(D + c0 + 4);
-          const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (J == I && dd[e] > 1.2851e19f) wide[u] = true;   // e^44
-            fb.set(e, kf[e] * dd[e]);
-          }
-          akk[u] = mma(akk[u], fk, fb);
-          aqk[u] = mma(aqk[u], fq, fb);
-        }
-      }
-      // K'^T fragments for the sequential kernel, K'_i = k_i exp(g_C - g_i) =
-      // Kf_i exp(g_C - g_e): wave w owns key channels [16 w, 16 w + 16); token
-      // index in the split order the sequential kernel consumes.
-      {
-        const int m = w, cc = 16 * m + r;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const float ec0 = sEc[(2 * kb) * kD + cc], ec1 = sEc[(2 * kb + 1) * kD + cc];
-          Frag<E> fkt;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = 32 * kb + split_k(g, e);
-            fkt.set(e, (e < 4 ? ec0 : ec1) * to_f(sKf[i * RS + cc]));
-          }
-          store_frag(KT + (m * 2 + kb) * kWave * 8, lane, fkt);
-        }
-      }
-      lds_barrier();
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        int I, J;
-        pair(u, I, J);
-        if (I < 0) continue;
-        if (J == I && __ballot(wide[u])) {
-          // exact diagonal block from the raw inputs: entries
-          // (Rr = 16 I + 4 g + e, i = 16 I + r)
-          auto row = [&](int x) -> int64_t { return ((tok0 + x) * H + h) * (int64_t)kD; };
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int Rr = 16 * I + 4 * g + e, i = 16 * I + r;
-            float skk = 0.f, sqk = 0.f;
-            if (i <= Rr && Rr < len) {
-              for (int c = 0; c < kD; ++c) {
-                const float d = exp_f(sg[Rr * kGS + c] - sg[i * kGS + c]);
-                const float kic = to_f(k[row(i) + c]);
-                skk += to_f(k[row(Rr) + c]) * kic * d;
-                sqk += to_f(q[row(Rr) + c]) * kic * d;
-              }
-            }
-            akk[u][e] = skk;
-            aqk[u][e] = sqk;
+      for (int e = 0; e < 4; ++e) {
+        const int Rr = 16 * I + 4 * g + e, i = 16 * I + r;
+        float skk = 0.f, sqk = 0.f;
+        if (i <= Rr && Rr < len) {
+          for (int c = 0; c < kD; ++c) {
+            float dg = 0.f;
+            for (int x = i + 1; x <= Rr; ++x) dg += log_alpha[row(x) + c];
+            const float d = exp_f(dg);
+            const float kic = to_f(k[row(i) + c]);
+            skk += to_f(k[row(Rr) + c]) * kic * d;
+            sqk += to_f(q[row(Rr) + c]) * kic * d;
           }
         }
+        akk[u][e] = skk;
+        aqk[u][e] = sqk;
       }
     }
-    // upper 16 x 16 blocks of Ti and L (later P) must read as zero; A_qk's
-    // upper blocks are never read
-    for (int x = t; x < 6 * 256; x += kIntraThreads) {
-      const int blkid = x >> 8, e = x & 255;
-      const int I = blkid < 3 ? 0 : (blkid < 5 ? 1 : 2);
-      const int J = blkid < 3 ? blkid + 1 : (blkid < 5 ? blkid - 1 : 3);
-      const int o = (16 * I + (e >> 4)) * kLS + 16 * J + (e & 15);
-      sTi[o] = 0.f;
-      sL[o] = 0.f;
+  }
+  lds_barrier();   // Kf is dead: its storage becomes M1 / M2
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    int I, J;
+    pair(u, I, J);
+    if (I < 0) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int Rr = 16 * I + 4 * g + e, i = 16 * J + r;
+      if (i < Rr) M1[Rr * kLS + i] = sb[Rr] * akk[u][e];       // L
+      if (i <= Rr) M1[i * kLS + Rr] = aqk[u][e];                // A_qk^T
     }
-    lds_barrier();
-    {
-      auto pair = [&](int u, int& I, int& J) {
-        if (w < 4) { I = u == 0 ? 3 : -1; J = w; }
-        else if (w < 6) { I = u == 0 ? 2 : -1; J = w - 4; }
-        else if (w == 6) { I = u == 0 ? 2 : 0; J = I; }
-        else { I = 1; J = u; }
-      };
+  }
+  lds_barrier();
+
+  // ---- 3. Ti = (I + L)^{-1}: diagonal 16 x 16 blocks by forward
+  //         substitution (one column per lane, waves 0-3), then off-diagonal
+  //         blocks Ti_IJ = -Ti_II sum_{K=J}^{I-1} L_IK Ti_KJ level by level.
+  if (w < 4 && lane < 16) {
+    const int base = 16 * w, jj = lane;
+    float x[16];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        int I, J;
-        pair(u, I, J);
-        if (I < 0) continue;
+    for (int rr = 0; rr < 16; ++rr) {
+      asm volatile("" ::: "memory");   // row rr of L read just before use
+      float sacc = rr == jj ? 1.f : 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int Rr = 16 * I + 4 * g + e, i = 16 * J + r;
-          sL[Rr * kLS + i] = i < Rr ? sb[Rr] * akk[u][e] : 0.f;
-          sAqk[Rr * kLS + i] = i <= Rr ? aqk[u][e] : 0.f;
+      for (int ii = 0; ii < rr; ++ii) sacc -= M1[(base + rr) * kLS + base + ii] * x[ii];
+      x[rr] = sacc;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      if (rr > jj) M2[(base + rr) * kLS + base + jj] = x[rr];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int I = d + w, J = w;
+      floatx4 acc = zero4();
+      for (int K = J; K < I; ++K) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int kk = 4 * s4 + g;
+          acc = mma4(acc, M1[(16 * I + r) * kLS + 16 * K + kk],
+                     K == J ? ti_at(M2, 16 * K + kk, 16 * J + r) - (kk == r ? 0.f : 0.f)
+                            : M2[(16 * K + kk) * kLS + 16 * J + r]);
         }
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) stmp[w * 16 * kTS + (4 * g + e) * kTS + r] = acc[e];
     }
     lds_barrier();
-
-    // ---- 3. Ti = (I + L)^{-1}: diagonal 16 x 16 blocks by forward
-    //         substitution (one column per lane, waves 0-3), then the
-    //         off-diagonal blocks Ti_IJ = -Ti_II sum_{K=J}^{I-1} L_IK Ti_KJ,
-    //         level by level.
-    // (I + L_bb)^{-1} for a strictly lower 16 x 16 block: L_bb^16 = 0, so
-    // the inverse is exactly (I - L)(I + L^2)(I + L^4)(I + L^8). Wave w < 4
-    // inverts block w with six fp32 block products; the temporaries live in
-    // g's storage (dead after step 2) and only this wave touches them.
-    if (w < 4) {
-      float* tmp = rA + w * (4 * 16 * kTS);      // L2 | L4 | L8 | product
-      float* L2 = tmp;
-      float* L4 = tmp + 16 * kTS;
-      float* L8 = tmp + 2 * 16 * kTS;
-      float* X = tmp + 3 * 16 * kTS;
-      const float* Lb = &sL[(16 * w) * kLS + 16 * w];
-      auto put = [&](float* dst, int ld, floatx4 v4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(4 * g + e) * ld + r] = v4[e];
-      };
-      put(L2, kTS, blk16(zero4(), Lb, kLS, Lb, kLS, r, g));
-      put(L4, kTS, blk16(zero4(), L2, kTS, L2, kTS, r, g));
-      put(L8, kTS, blk16(zero4(), L4, kTS, L4, kTS, r, g));
-      // A = (I - L) + (I - L) L2
-      floatx4 a4 = zero4();
+    if (w < 4 - d) {
+      const int I = d + w, J = w;
+      floatx4 acc = zero4();
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const int kk = 4 * s4 + g;
-        const float av = (r == kk ? 1.f : 0.f) - Lb[r * kLS + kk];
-        a4 = mma4(a4, av, L2[kk * kTS + r]);
+        acc = mma4(acc, ti_at(M2, 16 * I + r, 16 * I + kk), stmp[w * 16 * kTS + kk * kTS + r]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = 4 * g + e;
-        a4[e] += (rr == r ? 1.f : 0.f) - Lb[rr * kLS + r];
-      }
-      put(X, kTS, a4);
-      // B = A + A L4, then Ti_bb = B + B L8
-      floatx4 b4 = blk16(zero4(), X, kTS, L4, kTS, r, g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b4[e] += a4[e];
-      put(X, kTS, b4);
-      floatx4 x4 = blk16(zero4(), X, kTS, L8, kTS, r, g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x4[e] += b4[e];
-      put(&sTi[(16 * w) * kLS + 16 * w], kLS, x4);
+      for (int e = 0; e < 4; ++e) M2[(16 * I + 4 * g + e) * kLS + 16 * J + r] = -acc[e];
     }
     lds_barrier();
-#pragma unroll
-    for (int d = 1; d < 4; ++d) {
-      if (w < 4 - d) {
-        const int I = d + w, J = w;
-        floatx4 acc = zero4();
-        for (int K = J; K < I; ++K)
-          acc = blk16(acc, &sL[(16 * I) * kLS + 16 * K], kLS, &sTi[(16 * K) * kLS + 16 * J], kLS, r, g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) stmp[w * 16 * kTS + (4 * g + e) * kTS + r] = acc[e];
-      }
-      lds_barrier();
-      if (w < 4 - d) {
-        const int I = d + w, J = w;
-        floatx4 acc = blk16(zero4(), &sTi[(16 * I) * kLS + 16 * I], kLS, &stmp[w * 16 * kTS], kTS, r, g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sTi[(16 * I + 4 * g + e) * kLS + 16 * J + r] = -acc[e];
-      }
-      lds_barrier();
-    }
+  }
 
-    // ---- 4. P = A_qk Ti (lower triangular) into sL's storage; 20 block
-    //         products over 7 waves: (3,0) | (3,1) | (2,0) | (3,2)+(0,0) |
-    //         (2,1)+(1,1) | (1,0)+(2,2) | (3,3). Then bf16 copies of Ti, P.
-    {
-      auto plan = [&](int u, int& I, int& J) {
-        switch (w) {
-          case 0: I = u == 0 ? 3 : -1; J = 0; break;
-          case 1: I = u == 0 ? 3 : -1; J = 1; break;
-          case 2: I = u == 0 ? 2 : -1; J = 0; break;
-          case 3: I = u == 0 ? 3 : 0; J = u == 0 ? 2 : 0; break;
-          case 4: I = u == 0 ? 2 : 1; J = u == 0 ? 1 : 1; break;
-          case 5: I = u == 0 ? 1 : 2; J = u == 0 ? 0 : 2; break;
-          case 6: I = u == 0 ? 3 : -1; J = 3; break;
-          default: I = -1; J = 0; break;
-        }
-      };
-      floatx4 acc[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        acc[u] = zero4();
-        int I, J;
-        plan(u, I, J);
-        if (I < 0) continue;
-        for (int K = J; K <= I; ++K)
-          acc[u] = blk16(acc[u], &sAqk[(16 * I) * kLS + 16 * K], kLS, &sTi[(16 * K) * kLS + 16 * J], kLS, r, g);
+  // ---- 4. P = A_qk Ti (lower triangular), stored transposed in M2's upper
+  //         part: 20 block products over 7 waves.
+  {
+    auto plan = [&](int u, int& I, int& J) {
+      switch (w) {
+        case 0: I = u == 0 ? 3 : -1; J = 0; break;
+        case 1: I = u == 0 ? 3 : -1; J = 1; break;
+        case 2: I = u == 0 ? 2 : -1; J = 0; break;
+        case 3: I = u == 0 ? 3 : 0; J = u == 0 ? 2 : 0; break;
+        case 4: I = u == 0 ? 2 : 1; J = 1; break;
+        case 5: I = u == 0 ? 1 : 2; J = u == 0 ? 0 : 2; break;
+        case 6: I = u == 0 ? 3 : -1; J = 3; break;
+        default: I = -1; J = 0; break;
       }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        int I, J;
-        plan(u, I, J);
-        if (I < 0) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sL[(16 * I + 4 * g + e) * kLS + 16 * J + r] = acc[u][e];
-      }
-    }
-    lds_barrier();
-    // the next item's inputs are fetched while steps 5-6 run (issued here
-    // rather than earlier to keep the registers they occupy off the peak)
-    if (item + gridDim.x < n_items) {
-      cp = chunk_pos(item + gridDim.x, H, cu, chunk_offset, n_seqs, T);
-      load_chunk<E>(in, cp, t, q, k, v, log_alpha, beta, H);
-    }
-    const float* sP = sL;
-    if constexpr (sizeof(E) == 2) {
-      {
-        const int i = t >> 3, c0 = (t & 7) * 8;   // 64 rows x 8 groups of 8
-        float a8[8], b8[8];
-        load8(&sTi[i * kLS + c0], a8);
-        load8(&sP[i * kLS + c0], b8);
-        Frag<bf16> fa8, fb8;
-#pragma unroll
-        for (int z = 0; z < 8; ++z) { fa8.set(z, a8[z]); fb8.set(z, b8[z]); }
-        store8(&sTib[i * kBS + c0], fa8);
-        store8(&sPb[i * kBS + c0], fb8);
-      }
-      lds_barrier();
-    }
-    // rows of Ti and P as operand fragments (bf16 copies or the fp32 originals)
-    auto mat_frag = [&](bool isP, int R, int k0, Frag<E>& f) {
-      if constexpr (sizeof(E) == 2) lds_frag((isP ? sPb : sTib) + R * kBS + k0, f);
-      else lds_frag((isP ? sP : sTi) + R * kLS + k0, f);
     };
+    floatx4 acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      acc[u] = zero4();
+      int I, J;
+      plan(u, I, J);
+      if (I < 0) continue;
+      for (int K = J; K <= I; ++K) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int kk = 4 * s4 + g;
+          // A_qk[16 I + r][16 K + kk] from its transposed storage (zero above
+          // the diagonal of a diagonal block)
+          const float a = (K < I || kk <= r) ? M1[(16 * K + kk) * kLS + 16 * I + r] : 0.f;
+          const float bm = K == J ? ti_at(M2, 16 * K + kk, 16 * J + r)
+                                  : M2[(16 * K + kk) * kLS + 16 * J + r];
+          acc[u] = mma4(acc[u], a, bm);
+        }
+      }
+    }
+    lds_barrier();   // every read of Ti's diagonal blocks precedes P's writes
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int I, J;
+      plan(u, I, J);
+      if (I < 0) continue;
+      // lane holds P[16 I + 4 g + e][16 J + r] -> M2[16 J + r][16 I + 4 g + e]
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (I > J || 4 * g + e >= r) M2[(16 * J + r) * kLS + 16 * I + 4 * g + e] = acc[u][e];
+    }
+  }
+  lds_barrier();
+  // Rows of Ti and P as operand fragments: bf16 copies (row-major,
+  // swizzled) for bf16 I/O, masked reads of M2 for fp32.
+  if constexpr (sizeof(E) == 2) {
+    const int i = t & 63, c0 = (t >> 6) * 8;
+    Frag<bf16> ft, fp;
+#pragma unroll
+    for (int z = 0; z < 8; ++z) {
+      const int c = c0 + z;
+      ft.set(z, ti_at(M2, i, c));
+      fp.set(z, c <= i ? M2[c * kLS + i] : 0.f);
+    }
+    lds_barrier();   // M1's storage (A_qk^T) is free once P is done
+    store8(&sTib[mat_at(i, c0)], ft);
+    store8(&sPb[mat_at(i, c0)], fp);
+    lds_barrier();
+  }
+  auto mat_frag = [&](bool isP, int Rr, int k0, Frag<E>& f) {
+    if constexpr (sizeof(E) == 2) {
+      lds_frag((isP ? sPb : sTib) + mat_at(Rr, k0), f);
+    } else {
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        const int c = k0 + z;
+        f.set(z, isP ? (c <= Rr ? M2[c * kLS + Rr] : 0.f) : ti_at(M2, Rr, c));
+      }
+    }
+  };
 
-    // ---- 5. [-W^T | Qt^T] = (-B1)^T [Ti^T | P^T] + [0 | (Gamma*Q)^T] with
-    //         B1 = Diag(beta)(Gamma*K) = Diag(beta) exp(g_s) Kr and
-    //         Gamma*Q = exp(g_s) Qr. Wave w owns key channels [16 w, 16 w + 16).
-    {
-      const int m = w, cc = 16 * m + r, c4 = 16 * m + 4 * g;
-      floatx4 acc[8];
+  // v rows for step 6, fetched now so step 5 hides the latency (rows past
+  // the end repeat the last row; step 6 multiplies them by beta = 0)
+  constexpr int kPerV = kC * R::kPieces / kIntraThreads;
+  Vec16<E> vvec[kPerV];
+#pragma unroll
+  for (int u = 0; u < kPerV; ++u) {
+    const int pc = t + u * kIntraThreads, i = pc / R::kPieces, c = (pc % R::kPieces) * R::kPer16;
+    vvec[u] = *reinterpret_cast<const Vec16<E>*>(v + row(min(i, len - 1)) + c);
+  }
+
+  // ---- 5. [-W^T | Qt^T] = (-B1)^T [Ti^T | P^T] + [0 | (Gamma*Q)^T] with
+  //         B1 = Diag(beta) exp(g_s) Kr and Gamma*Q = exp(g_s) Qr. Wave w
+  //         owns key channels [16 w, 16 w + 16).
+  {
+    const int cc = 16 * w + r, c4 = 16 * w + 4 * g;
+    floatx4 acc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      acc[nt] = zero4();
+      if (nt < 4) continue;
+      const int Rr = 16 * (nt - 4) + r;
+      float qv[4];
+      load4(&sQ[R::at(Rr, c4)], qv);
+      const float4 es = *reinterpret_cast<const float4*>(&sEs[(Rr >> 4) * kD + c4]);
+      acc[nt][0] = es.x * qv[0];
+      acc[nt][1] = es.y * qv[1];
+      acc[nt][2] = es.z * qv[2];
+      acc[nt][3] = es.w * qv[3];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<E> fa;
+      const int i0 = 32 * kb + 8 * g;                 // standard order: one block
+      const float es = -sEs[(i0 >> 4) * kD + cc];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fa.set(e, sb[i0 + e] * es * to_f(sK[R::at(i0 + e, cc)]));
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        acc[nt] = zero4();
-        if (nt < 4) continue;
-        const int R = 16 * (nt - 4) + r;
-        float qv[4];
-        load4(&sQ[R * RS + c4], qv);
-        const float4 es = *reinterpret_cast<const float4*>(&sEs[(R >> 4) * kD + c4]);
-        acc[nt][0] = es.x * qv[0];
-        acc[nt][1] = es.y * qv[1];
-        acc[nt][2] = es.z * qv[2];
-        acc[nt][3] = es.w * qv[3];
+        Frag<E> fb;
+        mat_frag(nt >= 4, 16 * (nt & 3) + r, i0, fb);
+        acc[nt] = mma(acc[nt], fa, fb);
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        Frag<E> fa;
-        {
-          const int i0 = 32 * kb + 8 * g;                 // standard order: one block
-          const float es = -sEs[(i0 >> 4) * kD + cc];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) fa.set(e, sb[i0 + e] * es * to_f(sK[(i0 + e) * RS + cc]));
-        }
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          Frag<E> fb;
-          mat_frag(nt >= 4, 16 * (nt & 3) + r, 32 * kb + 8 * g, fb);
-          acc[nt] = mma(acc[nt], fa, fb);
-        }
-      }
-      // these 16 channels are slots 0-3 (even m) or 4-7 (odd m) of the
-      // sequential kernel's A-fragment (row tile nt, k-block m / 2)
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        store_half_frag(XA + (nt * 4 + (m >> 1)) * kWave * 8, lane, m & 1, acc[nt]);
     }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+      store_half_frag(XA + (nt * 4 + (w >> 1)) * kWave * 8, lane, w & 1, acc[nt]);
+  }
 
-    // ---- 6. U = Ti (beta V) (C-fragments, rows = token) and
-    //         Ut^T = (beta V)^T P^T (C-fragments, rows = value column); the
-    //         same (beta V) fragment is the B operand of one and the A operand
-    //         of the other. Wave w owns value columns [16 w, 16 w + 16).
-    {
-      const int jt = w, j = 16 * jt + r;
-      floatx4 acc[8];
+  // v takes Kr's storage once every wave is past step 5
+  lds_barrier();
+  E* const sV = sK;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
+  for (int u = 0; u < kPerV; ++u) {
+    const int pc = t + u * kIntraThreads, i = pc / R::kPieces, c = (pc % R::kPieces) * R::kPer16;
+    *reinterpret_cast<Vec16<E>*>(&sV[R::at(i, c)]) = vvec[u];
+  }
+  lds_barrier();
+
+  // ---- 6. U = Ti (beta V) (rows = token) and Ut^T = (beta V)^T P^T (rows =
+  //         value column); the same (beta V) fragment serves as B and as A.
+  //         Wave w owns value columns [16 w, 16 w + 16).
+  {
+    floatx4 acc[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        Frag<E> fv;
-        const int i0 = 32 * kb + 8 * g;
-        if constexpr (kStageV) {
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
 #pragma unroll
-          for (int e = 0; e < 8; ++e) fv.v[e] = sV[(i0 + e) * RS + j];
-        } else {
-          auto row = [&](int x) -> int64_t { return ((tok0 + x) * H + h) * (int64_t)kD; };
+    for (int kb = 0; kb < 2; ++kb) {
+      const int i0 = 32 * kb + 8 * g;
+      Frag<E> fv;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            fv.set(e, i0 + e < len ? sb[i0 + e] * to_f(v[row(i0 + e) + j]) : 0.f);
-        }
+      for (int e = 0; e < 8; ++e) fv.set(e, sb[i0 + e] * to_f(sV[R::at(i0 + e, 16 * w + r)]));
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          Frag<E> fm;
-          mat_frag(mt >= 4, 16 * (mt & 3) + r, i0, fm);
-          acc[mt] = mt < 4 ? mma(acc[mt], fm, fv) : mma(acc[mt], fv, fm);
-        }
+      for (int mt = 0; mt < 8; ++mt) {
+        Frag<E> fm;
+        mat_frag(mt >= 4, 16 * (mt & 3) + r, i0, fm);
+        acc[mt] = mt < 4 ? mma(acc[mt], fm, fv) : mma(acc[mt], fv, fm);
       }
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) store_c4(UC + (jt * 8 + mt) * kWave * 4, lane, acc[mt]);
     }
-    lds_barrier();   // every LDS read of this item precedes the next staging
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) store_c4(UC + (w * 8 + mt) * kWave * 4, lane, acc[mt]);
   }
 }
 
@@ -906,13 +823,7 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, const void* q, const void*
     if (err != hipSuccess) return err;
   }
   if ((phases & 2) && T > 0 && n_slots > 0) {
-    // persistent: one workgroup per CU (the kernel's LDS allows one), each
-    // looping over (chunk, head) items
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t items = n_slots * (int64_t)H;
-    const unsigned grid = (unsigned)std::min<int64_t>(items, std::max(cus, 1));
+    dim3 grid((unsigned)n_slots, (unsigned)H);
     if (bf16_io)
       intra_kernel<bf16><<<grid, kIntraThreads, 0, stream>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)v, log_alpha, beta, cu,
