@@ -40,11 +40,13 @@ template <>
 struct Frag<bf16> {
   bf16x8 v;
   __device__ void set(int e, float x) { v[e] = (bf16)x; }
+  __device__ float get(int e) const { return (float)v[e]; }
 };
 template <>
 struct Frag<float> {
   float v[8];
   __device__ void set(int e, float x) { v[e] = x; }
+  __device__ float get(int e) const { return v[e]; }
 };
 
 __device__ __forceinline__ floatx4 mma(floatx4 acc, const Frag<bf16>& a,
@@ -60,12 +62,96 @@ __device__ __forceinline__ floatx4 mma(floatx4 acc, const Frag<float>& a,
   return acc;
 }
 
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
 // One 16x16x4 fp32 step, for the small fp32 products of the UT transform.
 __device__ __forceinline__ floatx4 mma4(floatx4 acc, float a, float b) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+// Operand fragment of a K = 16 product: lane (r, g) supplies A[r][4 g + e]
+// and B[4 g + e][r], e < 4. This is also the accumulator layout, so an
+// accumulator tile of X is a ready B operand (and an A operand of X^T) for a
+// product that contracts over X's rows.
+template <class E>
+struct Frag16;
+template <>
+struct Frag16<bf16> {
+  bf16x4 v;
+  __device__ void set(int e, float x) { v[e] = (bf16)x; }
+  __device__ float get(int e) const { return (float)v[e]; }
+};
+template <>
+struct Frag16<float> {
+  float v[4];
+  __device__ void set(int e, float x) { v[e] = x; }
+  __device__ float get(int e) const { return v[e]; }
+};
+
+__device__ __forceinline__ floatx4 mma16(floatx4 acc, const Frag16<bf16>& a,
+                                         const Frag16<bf16>& b) {
+  typedef short short4_t __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a.v),
+                                                   __builtin_bit_cast(short4_t, b.v), acc, 0,
+                                                   0, 0);
+}
+__device__ __forceinline__ floatx4 mma16(floatx4 acc, const Frag16<float>& a,
+                                         const Frag16<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
+  return acc;
+}
+
+// 16 x 16 fp32 product C = A B from accumulator tiles: `at` holds A^T and
+// `b` holds B in the accumulator layout; C comes back in that layout.
+__device__ __forceinline__ floatx4 mm16(floatx4 at, floatx4 b) {
+  floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(at[s], b[s], c, 0, 0, 0);
+  return c;
+}
+
+template <class E>
+__device__ __forceinline__ Frag16<E> frag16(floatx4 x) {
+  Frag16<E> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.set(e, x[e]);
+  return f;
+}
+
+// Two K = 16 fragments as the two halves of a split-order K = 32 fragment.
+__device__ __forceinline__ Frag<bf16> join(const Frag16<bf16>& lo, const Frag16<bf16>& hi) {
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(lo.v, hi.v, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+__device__ __forceinline__ Frag<float> join(const Frag16<float>& lo, const Frag16<float>& hi) {
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = lo.v[e]; f.v[4 + e] = hi.v[e]; }
+  return f;
+}
+
+// Four consecutive I/O elements, kept in their I/O type.
+__device__ __forceinline__ Frag16<bf16> ld16(const bf16* p) {
+  Frag16<bf16> f;
+  f.v = *reinterpret_cast<const bf16x4*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag16<float> ld16(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  Frag16<float> f;
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  return f;
+}
+__device__ __forceinline__ void st16(bf16* p, const Frag16<bf16>& f) {
+  *reinterpret_cast<bf16x4*>(p) = f.v;
+}
+__device__ __forceinline__ void st16(float* p, const Frag16<float>& f) {
+  *reinterpret_cast<float4*>(p) = float4{f.v[0], f.v[1], f.v[2], f.v[3]};
+}
+
 
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_f(float x) {

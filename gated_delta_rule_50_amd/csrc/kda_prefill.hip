@@ -88,33 +88,27 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(
 }
 
 // ----------------------------------------------------------- intra-chunk
-// One workgroup per (chunk, head); two fit on a CU (LDS <= 80 KiB, <= 128
-// VGPRs), so one workgroup's loads overlap the other's compute.
-constexpr int kIntraThreads = 512;   // 8 waves
-constexpr int kLS = kC + 4;          // row stride (floats) of the 64 x 64 fp32 buffers
-constexpr int kTS = 20;              // row stride of 16 x 16 fp32 scratch blocks
-
-// Staged rows: 128 elements per row, no padding; 16-byte pieces are XOR
-// swizzled by the row (piece p of row i sits at p ^ (i & 15) for bf16, at
-// p ^ (i & 31) for fp32) so row reads, column gathers and row writes by
-// lanes of different rows hit different banks.
-template <class E>
-struct Rows {
-  static constexpr int kPer16 = 16 / (int)sizeof(E);   // elements per piece
-  static constexpr int kPieces = kD / kPer16;           // pieces per row
-  __device__ static int at(int i, int c) {               // element offset of (i, c)
-    const int p = (c / kPer16) ^ (i & (kPieces - 1));
-    return i * kD + p * kPer16 + c % kPer16;
-  }
-};
-
-// 64 x 64 bf16 matrix, 8 pieces per row, swizzled the same way.
-__device__ __forceinline__ int mat_at(int i, int c) {
-  return i * kC + (((c >> 3) ^ (i & 7)) << 3) + (c & 7);
-}
-
-template <class E>
-using Vec16 = typename std::conditional<sizeof(E) == 2, bf16x8, float4>::type;
+// One workgroup of four waves per (chunk, head). Wave I owns the 16-token
+// block I of the chunk and keeps its rows in registers in the "piece"
+// layout: lane (r, g) holds token 16 I + r and, for each 16-channel tile ct,
+// the channels 16 ct + 4 g .. 16 ct + 4 g + 3. Pieces 2 kb and 2 kb + 1 form
+// a split-order fragment of the 32-channel slice kb, and one piece is the
+// accumulator layout of a transposed 16 x 16 tile, so
+//   * the A tiles (contractions over channels) take row pieces directly,
+//   * a product with the identity turns row pieces into a token-major
+//     accumulator tile (a transpose on the matrix cores), and
+//   * every contraction over tokens uses accumulator tiles as operands:
+//     X in the accumulator layout is the B operand of (. X) and the A
+//     operand of (X^T .), so both orientations of a product come from the
+//     same registers with A and B swapped.
+// The triangular solve runs block by block: wave I inverts its diagonal
+// block in registers ((I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8) for
+// the nilpotent 16 x 16 N), then, after the blocks before it,
+//   [W_I | U_I] = Ti_II ([B_I | V'_I] - sum_{J<I} L_IJ [W_J | U_J]),
+// and finally Qt_I = Gamma Q_I - sum_{J<=I} A_qk,IJ W_J, Ut_I = sum A_qk,IJ U_J.
+// Only the column factors Kf (for the A tiles) and W_J | U_J (for the later
+// blocks) pass through LDS; four workgroup barriers per chunk.
+constexpr int kIntraThreads = 256;   // 4 waves
 
 // Workgroup barrier that waits for this wave's LDS traffic only (outstanding
 // global stores stay in flight).
@@ -125,52 +119,48 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Inclusive prefix sum over the 16 lanes r of each DPP row (lane l = r + 16 g).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_in_row(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_scan16(float x) {
+  x += dpp_in_row<0x111>(x);   // row_shr:1
+  x += dpp_in_row<0x112>(x);   // row_shr:2
+  x += dpp_in_row<0x114>(x);   // row_shr:4
+  x += dpp_in_row<0x118>(x);   // row_shr:8
+  return x;
+}
+
 // Eight consecutive elements as an MFMA fragment.
 __device__ __forceinline__ void lds_frag(const bf16* p, Frag<bf16>& f) {
   f.v = *reinterpret_cast<const bf16x8*>(p);
 }
 __device__ __forceinline__ void lds_frag(const float* p, Frag<float>& f) { load8(p, f.v); }
 
-// Element (r, k) of a 16 x 16 block of Ti, stored strictly lower in `M`
-// (row stride kLS) with an implied unit diagonal and zero upper part.
-__device__ __forceinline__ float ti_at(const float* M, int R, int K) {
-  return K < R ? M[R * kLS + K] : (K == R ? 1.f : 0.f);
-}
-
 template <class E>
-__global__ __launch_bounds__(kIntraThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void intra_kernel(
+__global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_offset,
     const int32_t* __restrict__ status, int32_t n_seqs, int64_t T, int32_t H,
     uint8_t* __restrict__ inter) {
-  using R = Rows<E>;
-  // LDS, by lifetime:
-  //   sK   k, then Kr = k exp(g - g_s)          (s = first row of the 16-row block)
-  //   sQ   q, then Qr = q exp(g - g_s)
-  //   rM   Kf = k exp(g_e - g) (e = last row of the block), until the A tiles
-  //        are done; then M1 = [L strictly lower | A_qk^T upper + diagonal]
-  //        and M2 = [Ti strictly lower | P^T upper + diagonal]; after P, M1's
-  //        storage takes the bf16 copies of Ti and P (bf16 I/O)
-  //   sF   per block / block-pair / channel factors
-  //   sX   per (block, channel) sums of log alpha, later 16 x 16 scratch
-  __shared__ __attribute__((aligned(16))) E sK[kC * kD];
-  __shared__ __attribute__((aligned(16))) E sQ[kC * kD];
-  __shared__ __attribute__((aligned(16))) float rM[2 * kC * kLS];
-  __shared__ __attribute__((aligned(16))) float sF[(4 + 4 + 10) * kD];
-  __shared__ __attribute__((aligned(16))) float sX[3 * 16 * kTS];
-  __shared__ float sb[kC];
-  E* const sKf = reinterpret_cast<E*>(rM);
-  float* const M1 = rM;
-  float* const M2 = rM + kC * kLS;
-  bf16* const sTib = reinterpret_cast<bf16*>(rM);
-  bf16* const sPb = reinterpret_cast<bf16*>(rM) + kC * kC;
-  float* const sEs = sF;              // exp(g_s[c]) per block
-  float* const sEc = sF + 4 * kD;     // exp(g_C[c] - g_e[c]) per block
-  float* const sDf = sF + 8 * kD;     // exp(g_{s_I}[c] - g_{e_J}[c]), J <= I
-  float* const xTot = sX;             // per-block sums of log alpha (4 x 128)
-  float* const stmp = sX;             // 3 scratch blocks (after the exchange)
+  // LDS:
+  //   sKf   Kf fragments of the four blocks [J][kb][lane][8]; once every wave
+  //         is past its A tiles, its two halves hold W | U of blocks 1 and 2
+  //   sWU0  W | U of block 0 as accumulator tiles [tile][lane][4]
+  //   sTot  per-block sums of log alpha; sE = exp(sum), sEi = exp(-sum)
+  //   sB    beta
+  //   sF    per-block channel factors (five rows per block)
+  constexpr int kWU = 16 * kWave * 4;
+  __shared__ __attribute__((aligned(16))) E sKf[4 * 4 * kWave * 8];
+  __shared__ __attribute__((aligned(16))) E sWU0[kWU];
+  __shared__ __attribute__((aligned(16))) float sTot[4 * kD];
+  __shared__ __attribute__((aligned(16))) float sE[4 * kD];
+  __shared__ __attribute__((aligned(16))) float sEi[4 * kD];
+  __shared__ __attribute__((aligned(16))) float sB[kC];
+  __shared__ __attribute__((aligned(16))) float sF[4 * 5 * kD];
+  auto wu_slot = [&](int J) -> E* { return J == 0 ? sWU0 : sKf + (J - 1) * kWU; };
 
   if (status[0] != 0) return;
   const int b = blockIdx.x, h = blockIdx.y;
@@ -185,10 +175,12 @@ void intra_kernel(
   const int64_t tok0 = seq_start + (int64_t)(b - chunk_offset[lo]) * kC;
   const int len = (int)min((int64_t)kC, seq_end - tok0);
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int lane = threadIdx.x & 63;
+  const int I = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // token block
   const int r = lane & 15, g = lane >> 4;
-  auto row = [&](int i) -> int64_t { return ((tok0 + i) * H + h) * (int64_t)kD; };
-  auto pidx = [](int I, int J) { return I * (I + 1) / 2 + J; };
+  const int i = 16 * I + r;
+  const bool valid = i < len;
+  auto row = [&](int x) -> int64_t { return ((tok0 + x) * H + h) * (int64_t)kD; };
 
   E* blk = reinterpret_cast<E*>(inter + ((int64_t)b * H + h) * Inter<E>::kBytes);
   E* XA = blk + Inter<E>::kXA;
@@ -196,406 +188,333 @@ void intra_kernel(
   E* UC = blk + Inter<E>::kUC;
   float* GC = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(blk) + Inter<E>::kGCByte);
 
-  // ---- 0. loads, all issued up front. k and q rows go to LDS; each thread
-  //         keeps one channel c of one 16-row block of log alpha.
-  const int cch = t & 127, seg = t >> 7;       // channel, 16-row block
-  float la[16];
+  // ---- 0. loads of k, q, log alpha and beta. Tokens past the end of the
+  //         sequence read the last valid row and become zeros (identity
+  //         tokens). v is loaded after the A tiles.
+  const int64_t ro = row(min(i, len - 1));
+  Frag16<E> zero;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) zero.set(e, 0.f);
+  Frag16<E> kx[8], qx[8];
+  float la[8][4];
+  float bt;
   {
-    constexpr int kPer = kC * R::kPieces / kIntraThreads;
-    Vec16<E> vk[kPer], vq[kPer];
-    const Vec16<E> zero16 = {};
-    // Rows past the sequence end (identity tokens) are loaded from the last
-    // valid row and replaced by zeros with a select: no branches, no
-    // out-of-range addresses (a chunk always has len >= 1).
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pc = t + u * kIntraThreads, i = pc / R::kPieces, c = (pc % R::kPieces) * R::kPer16;
-      const int ic = min(i, len - 1);
-      const Vec16<E> a = *reinterpret_cast<const Vec16<E>*>(k + row(ic) + c);
-      const Vec16<E> b2 = *reinterpret_cast<const Vec16<E>*>(q + row(ic) + c);
-      vk[u] = i < len ? a : zero16;
-      vq[u] = i < len ? b2 : zero16;
+    for (int ct = 0; ct < 8; ++ct) {
+      const int64_t o = ro + 16 * ct + 4 * g;
+      const Frag16<E> a = ld16(k + o), c = ld16(q + o);
+      const float4 l = *reinterpret_cast<const float4*>(log_alpha + o);
+      kx[ct] = valid ? a : zero;
+      qx[ct] = valid ? c : zero;
+      la[ct][0] = valid ? l.x : 0.f; la[ct][1] = valid ? l.y : 0.f;
+      la[ct][2] = valid ? l.z : 0.f; la[ct][3] = valid ? l.w : 0.f;
     }
-#pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-      const int i = 16 * seg + ii;
-      const float x = log_alpha[row(min(i, len - 1)) + cch];
-      la[ii] = i < len ? x : 0.f;
-    }
-    if (t < kC) {
-      const float x = beta[(tok0 + min(t, len - 1)) * H + h];
-      sb[t] = t < len ? x : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pc = t + u * kIntraThreads, i = pc / R::kPieces, c = (pc % R::kPieces) * R::kPer16;
-      *reinterpret_cast<Vec16<E>*>(&sK[R::at(i, c)]) = vk[u];
-      *reinterpret_cast<Vec16<E>*>(&sQ[R::at(i, c)]) = vq[u];
-    }
+    const float x = beta[(tok0 + min(i, len - 1)) * H + h];
+    bt = valid ? x : 0.f;
   }
 
-  // ---- 1. gate: in-register cumsum of this thread's 16 log alphas, block
-  //         offsets through LDS, then g_i for the thread's rows.
+  // ---- 1. gate: l_i = sum of log alpha over rows 16 I .. i (a scan across
+  //         the 16 lanes of a DPP row). The block sums and their
+  //         exponentials go to LDS for the other blocks. Row factors
+  //         Kr = k e^l, Qr = q e^l and column factors Kf = k e^{l_e - l}
+  //         (e = last row of the block) are all <= 1 times the input.
 #pragma unroll
-  for (int ii = 1; ii < 16; ++ii) la[ii] += la[ii - 1];
-  xTot[seg * kD + cch] = la[15];
-  lds_barrier();
-  {
-    float off = 0.f;
+  for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-    for (int u = 0; u < 3; ++u) off += u < seg ? xTot[u * kD + cch] : 0.f;
+    for (int e = 0; e < 4; ++e) la[ct][e] = row_scan16(la[ct][e]);
+  if (r == 15) {
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) la[ii] += off;          // la[] now holds g
+    for (int ct = 0; ct < 8; ++ct)
+      *reinterpret_cast<float4*>(&sTot[I * kD + 16 * ct + 4 * g]) =
+          float4{la[ct][0], la[ct][1], la[ct][2], la[ct][3]};
   }
-  // ---- 1b. decay factors for this thread's rows (each element once):
-  //          Kr = k exp(g - g_s), Qr = q exp(g - g_s), Kf = k exp(g_e - g),
-  //          all <= 1 in magnitude times the input. Per block and block pair:
-  //          exp(g_s), exp(g_C - g_e), D_IJ = exp(g_{s_I} - g_{e_J}) (<= 1 for
-  //          J < I), with g at a block's last row = sum of the block sums
-  //          up to it.
-#pragma unroll
-  for (int ii = 0; ii < 16; ++ii) {
-    const int i = 16 * seg + ii, o = R::at(i, cch);
-    const float fr = exp_f(la[ii] - la[0]);
-    const float fc = exp_f(la[15] - la[ii]);
-    const float kv = to_f(sK[o]);
-    sK[o] = from_f<E>(kv * fr);
-    sQ[o] = from_f<E>(to_f(sQ[o]) * fr);
-    sKf[o] = from_f<E>(kv * fc);
-  }
-  {
-    float ge[4];
-    ge[0] = xTot[cch];
-#pragma unroll
-    for (int J = 1; J < 4; ++J) ge[J] = ge[J - 1] + xTot[J * kD + cch];
-    sEs[seg * kD + cch] = exp_f(la[0]);
-    sEc[seg * kD + cch] = exp_f(ge[3] - la[15]);
-    if (seg == 3) GC[cch] = exp_f(ge[3]);
-#pragma unroll
-    for (int J = 0; J < 4; ++J)
-      if (J <= seg) sDf[pidx(seg, J) * kD + cch] = exp_f(fminf(la[0] - ge[J], 88.f));
-  }
-  lds_barrier();
-
-  // ---- 2. A_kk (strict) and A_qk (inclusive) on 16 x 16 blocks (I, J):
-  //         waves 0-3 (3, w); 4-5 (2, w-4); 6 (2,2)+(0,0); 7 (1,0)+(1,1).
-  //         Column factor of pair (I, J): Kf * D_IJ. A diagonal block whose
-  //         D could exceed e^44 is recomputed exactly from the raw inputs.
-  auto pair = [&](int u, int& I, int& J) {
-    if (w < 4) { I = u == 0 ? 3 : -1; J = w; }
-    else if (w < 6) { I = u == 0 ? 2 : -1; J = w - 4; }
-    else if (w == 6) { I = u == 0 ? 2 : 0; J = I; }
-    else { I = 1; J = u; }
-  };
-  floatx4 akk[2], aqk[2];
-  {
-    bool wide[2] = {false, false};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      akk[u] = zero4();
-      aqk[u] = zero4();
-      int I, J;
-      pair(u, I, J);
-      if (I < 0) continue;
-      const int Rw = 16 * I + r, i = 16 * J + r;
-      const float* D = sDf + pidx(I, J) * kD;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int c0 = 32 * kb + 8 * g;
-        Frag<E> fk, fq, fb;
-        if constexpr (sizeof(E) == 2) {
-          lds_frag(&sK[R::at(Rw, c0)], fk);
-          lds_frag(&sQ[R::at(Rw, c0)], fq);
-        } else {
-          float a8[8], b8[8];
-          load4(&sK[R::at(Rw, c0)], a8); load4(&sK[R::at(Rw, c0 + 4)], a8 + 4);
-          load4(&sQ[R::at(Rw, c0)], b8); load4(&sQ[R::at(Rw, c0 + 4)], b8 + 4);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) { fk.set(e, a8[e]); fq.set(e, b8[e]); }
-        }
-        float kf[8];
-        if constexpr (sizeof(E) == 2) {
-          load8(&sKf[R::at(i, c0)], kf);
-        } else {
-          load4(&sKf[R::at(i, c0)], kf); load4(&sKf[R::at(i, c0 + 4)], kf + 4);
-        }
-        const float4 d0 = *reinterpret_cast<const float4*>(D + c0);
-        const float4 d1 = *reinterpret_cast<const float4*>(D + c0 + 4);
-        const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (J == I && dd[e] > 1.2851e19f) wide[u] = true;   // e^44
-          fb.set(e, kf[e] * dd[e]);
-        }
-        akk[u] = mma(akk[u], fk, fb);
-        aqk[u] = mma(aqk[u], fq, fb);
-      }
-    }
-    // K'^T fragments (K'_i = k_i exp(g_C - g_i) = Kf_i exp(g_C - g_e)) for
-    // the sequential kernel: wave w owns channels [16 w, 16 w + 16), token
-    // index in the split order.
-    {
-      const int cc = 16 * w + r;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const float ec0 = sEc[(2 * kb) * kD + cc], ec1 = sEc[(2 * kb + 1) * kD + cc];
-        Frag<E> fkt;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 32 * kb + split_k(g, e);
-          fkt.set(e, (e < 4 ? ec0 : ec1) * to_f(sKf[R::at(i, cc)]));
-        }
-        store_frag(KT + (w * 2 + kb) * kWave * 8, lane, fkt);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      int I, J;
-      pair(u, I, J);
-      if (I < 0 || J != I || !__ballot(wide[u])) continue;
-      // exact diagonal block: entries (Rr = 16 I + 4 g + e, i = 16 I + r),
-      // g differences summed from the raw log alphas
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int Rr = 16 * I + 4 * g + e, i = 16 * I + r;
-        float skk = 0.f, sqk = 0.f;
-        if (i <= Rr && Rr < len) {
-          for (int c = 0; c < kD; ++c) {
-            float dg = 0.f;
-            for (int x = i + 1; x <= Rr; ++x) dg += log_alpha[row(x) + c];
-            const float d = exp_f(dg);
-            const float kic = to_f(k[row(i) + c]);
-            skk += to_f(k[row(Rr) + c]) * kic * d;
-            sqk += to_f(q[row(Rr) + c]) * kic * d;
-          }
-        }
-        akk[u][e] = skk;
-        aqk[u][e] = sqk;
-      }
-    }
-  }
-  lds_barrier();   // Kf is dead: its storage becomes M1 / M2
+  if (g == 0) sB[i] = bt;
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    int I, J;
-    pair(u, I, J);
-    if (I < 0) continue;
+    const int c = lane + 64 * u;
+    const float s = sTot[I * kD + c];
+    sE[I * kD + c] = exp_f(s);
+    sEi[I * kD + c] = exp_f(fminf(-s, 88.f));
+  }
+  Frag16<E> Kr[8], Qr[8];
+  Frag<E> kfI[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ct = 2 * kb + hh;
+      const floatx4 s = *reinterpret_cast<const floatx4*>(&sTot[I * kD + 16 * ct + 4 * g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float kv = kx[ct].get(e), fr = exp_f(la[ct][e]);
+        kfI[kb].set(4 * hh + e, kv * exp_f(s[e] - la[ct][e]));
+        Kr[ct].set(e, kv * fr);
+        Qr[ct].set(e, qx[ct].get(e) * fr);
+      }
+    }
+    store8(&sKf[((I * 4 + kb) * kWave + lane) * 8], kfI[kb]);
+  }
+  lds_barrier();
+
+  // ---- 2. per-channel factors of this block, with p_J = g before block J
+  //         and E_J = exp(block sum J):
+  //           exp(p_I) = prod_{K<I} E_K,  exp(g_C - p_{I+1}) = prod_{K>I} E_K,
+  //           D_IJ = exp(p_I - p_{J+1}) = prod_{J<K<I} E_K (<= 1, J < I),
+  //         two channels per lane into this wave's rows of sF.
+  float* const sFw = sF + I * 5 * kD;   // rows: exp(p_I), exp(g_C - p_{I+1}), D_I0..D_I2
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = lane + 64 * u;
+    float ev[4];
+#pragma unroll
+    for (int K = 0; K < 4; ++K) ev[K] = sE[K * kD + c];
+    float a = 1.f, bb = 1.f, d[3] = {1.f, 1.f, 1.f};
+#pragma unroll
+    for (int K = 0; K < 4; ++K) {
+      a *= K < I ? ev[K] : 1.f;
+      bb *= K > I ? ev[K] : 1.f;
+#pragma unroll
+      for (int J = 0; J < 3; ++J) d[J] *= (J < K && K < I) ? ev[K] : 1.f;
+    }
+    sFw[c] = a;
+    sFw[kD + c] = bb;
+#pragma unroll
+    for (int J = 0; J < 3; ++J) sFw[(2 + J) * kD + c] = d[J];
+    if (I == 0) GC[c] = ev[0] * ev[1] * ev[2] * ev[3];   // gamma_C = exp(g_C)
+  }
+  asm volatile("" ::: "memory");
+
+  // beta Gamma K and Gamma Q row pieces; K' = Kf exp(g_C - p_{I+1}) =
+  // k exp(g_C - g) becomes K'^T fragments for the sequential kernel: a K'
+  // row piece times the identity is the token-major tile (lane (r, g):
+  // K'[16I + 4g + e][16ct + r]), the half of the split-order fragment this
+  // block's tokens fill.
+  Frag16<E> idf;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) idf.set(e, 4 * g + e == r ? 1.f : 0.f);
+  Frag16<E> Bx[8], GQ[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const floatx4 gs = *reinterpret_cast<const floatx4*>(&sFw[16 * ct + 4 * g]);
+    const floatx4 ek = *reinterpret_cast<const floatx4*>(&sFw[kD + 16 * ct + 4 * g]);
+    Frag16<E> kp;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int Rr = 16 * I + 4 * g + e, i = 16 * J + r;
-      if (i < Rr) M1[Rr * kLS + i] = sb[Rr] * akk[u][e];       // L
-      if (i <= Rr) M1[i * kLS + Rr] = aqk[u][e];                // A_qk^T
+      Bx[ct].set(e, bt * gs[e] * Kr[ct].get(e));
+      GQ[ct].set(e, gs[e] * Qr[ct].get(e));
+      kp.set(e, kfI[ct >> 1].get(4 * (ct & 1) + e) * ek[e]);
     }
-  }
-  lds_barrier();
-
-  // ---- 3. Ti = (I + L)^{-1}: diagonal 16 x 16 blocks by forward
-  //         substitution (one column per lane, waves 0-3), then off-diagonal
-  //         blocks Ti_IJ = -Ti_II sum_{K=J}^{I-1} L_IK Ti_KJ level by level.
-  if (w < 4 && lane < 16) {
-    const int base = 16 * w, jj = lane;
-    float x[16];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      asm volatile("" ::: "memory");   // row rr of L read just before use
-      float sacc = rr == jj ? 1.f : 0.f;
-#pragma unroll
-      for (int ii = 0; ii < rr; ++ii) sacc -= M1[(base + rr) * kLS + base + ii] * x[ii];
-      x[rr] = sacc;
-    }
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-      if (rr > jj) M2[(base + rr) * kLS + base + jj] = x[rr];
-  }
-  lds_barrier();
-#pragma unroll
-  for (int d = 1; d < 4; ++d) {
-    if (w < 4 - d) {
-      const int I = d + w, J = w;
-      floatx4 acc = zero4();
-      for (int K = J; K < I; ++K) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int kk = 4 * s4 + g;
-          acc = mma4(acc, M1[(16 * I + r) * kLS + 16 * K + kk],
-                     K == J ? ti_at(M2, 16 * K + kk, 16 * J + r) - (kk == r ? 0.f : 0.f)
-                            : M2[(16 * K + kk) * kLS + 16 * J + r]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) stmp[w * 16 * kTS + (4 * g + e) * kTS + r] = acc[e];
-    }
-    lds_barrier();
-    if (w < 4 - d) {
-      const int I = d + w, J = w;
-      floatx4 acc = zero4();
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int kk = 4 * s4 + g;
-        acc = mma4(acc, ti_at(M2, 16 * I + r, 16 * I + kk), stmp[w * 16 * kTS + kk * kTS + r]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) M2[(16 * I + 4 * g + e) * kLS + 16 * J + r] = -acc[e];
-    }
-    lds_barrier();
+    store_half_frag(KT + (ct * 2 + (I >> 1)) * kWave * 8, lane, I & 1, mma16(zero4(), kp, idf));
   }
 
-  // ---- 4. P = A_qk Ti (lower triangular), stored transposed in M2's upper
-  //         part: 20 block products over 7 waves.
-  {
-    auto plan = [&](int u, int& I, int& J) {
-      switch (w) {
-        case 0: I = u == 0 ? 3 : -1; J = 0; break;
-        case 1: I = u == 0 ? 3 : -1; J = 1; break;
-        case 2: I = u == 0 ? 2 : -1; J = 0; break;
-        case 3: I = u == 0 ? 3 : 0; J = u == 0 ? 2 : 0; break;
-        case 4: I = u == 0 ? 2 : 1; J = 1; break;
-        case 5: I = u == 0 ? 1 : 2; J = u == 0 ? 0 : 2; break;
-        case 6: I = u == 0 ? 3 : -1; J = 3; break;
-        default: I = -1; J = 0; break;
+  // v rows, needed from step 4 on
+  Frag16<E> vx[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const Frag16<E> d = ld16(v + ro + 16 * ct + 4 * g);
+    vx[ct] = valid ? d : zero;
+  }
+
+  // A tiles. For J < I, A_kk[i][j] = sum_c (Kr_i D_IJ) Kf_j (same for A_qk
+  // with Qr); the diagonal block uses D_II = exp(-block sum) >= 1, and where
+  // that could exceed e^44 the block is recomputed exactly below. Lane (r, g)
+  // accumulates akT[J][e] = A_kk[16I + r][16J + 4g + e],
+  // aqT[J][e] = A_qk[16I + r][16J + 4g + e] and akD[e] = A_kk[16I + 4g + e][16I + r].
+  floatx4 akT[4], aqT[4], akD = zero4();
+  bool wide = false;
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    akT[J] = zero4();
+    aqT[J] = zero4();
+    if (J > I) continue;
+    const float* Drow = J < I ? sFw + (2 + (J < 3 ? J : 0)) * kD : sEi + I * kD;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const floatx4 d0 = *reinterpret_cast<const floatx4*>(&Drow[32 * kb + 4 * g]);
+      const floatx4 d1 = *reinterpret_cast<const floatx4*>(&Drow[32 * kb + 16 + 4 * g]);
+      Frag<E> fk, fq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        fk.set(e, Kr[2 * kb].get(e) * d0[e]);
+        fk.set(4 + e, Kr[2 * kb + 1].get(e) * d1[e]);
+        fq.set(e, Qr[2 * kb].get(e) * d0[e]);
+        fq.set(4 + e, Qr[2 * kb + 1].get(e) * d1[e]);
+      }
+      if (J < I) {
+        Frag<E> fa;
+        lds_frag(&sKf[((J * 4 + kb) * kWave + lane) * 8], fa);
+        akT[J] = mma(akT[J], fa, fk);
+        aqT[J] = mma(aqT[J], fa, fq);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wide |= d0[e] > 1.2851e19f || d1[e] > 1.2851e19f;  // e^44
+        akT[J] = mma(akT[J], kfI[kb], fk);
+        aqT[J] = mma(aqT[J], kfI[kb], fq);
+        akD = mma(akD, fk, kfI[kb]);
+      }
+    }
+  }
+
+  // exact diagonal block when its factors could overflow: g differences
+  // summed from the raw log alphas
+  if (__builtin_amdgcn_ballot_w64(wide)) {
+    auto exact = [&](int a, int c0, float& skk, float& sqk) {   // rows a >= c0
+      skk = sqk = 0.f;
+      if (a >= len || c0 > a) return;
+      for (int c = 0; c < kD; ++c) {
+        float dg = 0.f;
+        for (int x = c0 + 1; x <= a; ++x) dg += log_alpha[row(x) + c];
+        const float d = exp_f(dg);
+        const float kc = to_f(k[row(c0) + c]);
+        skk += to_f(k[row(a) + c]) * kc * d;
+        sqk += to_f(q[row(a) + c]) * kc * d;
       }
     };
-    floatx4 acc[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      acc[u] = zero4();
-      int I, J;
-      plan(u, I, J);
-      if (I < 0) continue;
-      for (int K = J; K <= I; ++K) {
+    for (int J = 0; J < 4; ++J) {
+      if (J != I) continue;
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int kk = 4 * s4 + g;
-          // A_qk[16 I + r][16 K + kk] from its transposed storage (zero above
-          // the diagonal of a diagonal block)
-          const float a = (K < I || kk <= r) ? M1[(16 * K + kk) * kLS + 16 * I + r] : 0.f;
-          const float bm = K == J ? ti_at(M2, 16 * K + kk, 16 * J + r)
-                                  : M2[(16 * K + kk) * kLS + 16 * J + r];
-          acc[u] = mma4(acc[u], a, bm);
+      for (int e = 0; e < 4; ++e) {
+        float skk, sqk, tkk, tqk;
+        exact(16 * I + r, 16 * I + 4 * g + e, skk, sqk);
+        exact(16 * I + 4 * g + e, 16 * I + r, tkk, tqk);
+        akT[J][e] = skk;
+        aqT[J][e] = sqk;
+        akD[e] = tkk;
+      }
+    }
+  }
+
+  // ---- 3. Ti_II = (I + N)^{-1}, N = strictly lower beta_i A_kk of the
+  //         diagonal block, held as TiT = Ti_II^T in the accumulator layout.
+  //         X = N^T; Ti_II^T = (I + X)^{-1} = (I - X)(I + X^2)(I + X^4)(I + X^8).
+  floatx4 Xc, Nc, Ic;
+  {
+    const float4 b4 = *reinterpret_cast<const float4*>(&sB[16 * I + 4 * g]);
+    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J != I) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Xc[e] = 4 * g + e < r ? bt * akT[J][e] : 0.f;       // N[r][4g+e]
+        Nc[e] = r < 4 * g + e ? bb[e] * akD[e] : 0.f;       // N[4g+e][r]
+        Ic[e] = 4 * g + e == r ? 1.f : 0.f;
+      }
+    }
+  }
+  Frag16<E> tiT;
+  {
+    const floatx4 X2 = mm16(Nc, Xc), X2T = mm16(Xc, Nc);
+    const floatx4 X4 = mm16(X2T, X2), X4T = mm16(X2, X2T);
+    const floatx4 X8 = mm16(X4T, X4);
+    const floatx4 P1 = Ic - Xc + X2 - mm16(Nc, X2);
+    const floatx4 P1T = Ic - Nc + X2T - mm16(X2, Nc);
+    const floatx4 P2 = P1 + mm16(P1T, X4), P2T = P1T + mm16(X4, P1T);
+    tiT = frag16<E>(P2 + mm16(P2T, X8));
+  }
+  // -L_IJ (J < I) as A operands, A_qk (J <= I, masked on the diagonal) and
+  // its negation as B operands, beta V row pieces
+  Frag16<E> nL[3], aq[4], naq[4], Vb[8];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = (J < I || 4 * g + e <= r) ? aqT[J][e] : 0.f;
+      aq[J].set(e, x);
+      naq[J].set(e, -x);
+      if (J < 3) nL[J].set(e, -bt * akT[J][e]);
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Vb[ct].set(e, bt * vx[ct].get(e));
+
+  // ---- 4. blocked forward substitution, one block per barrier interval.
+  Frag16<E> wu[16];   // W_I (tiles 0-7, key channels) | U_I (8-15, value columns)
+  for (int s = 0; s < I; ++s) lds_barrier();
+  {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      floatx4 M[8];
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) M[ct] = mma16(zero4(), hf ? Vb[ct] : Bx[ct], idf);
+#pragma unroll
+      for (int J = 0; J < 3; ++J) {
+        if (J >= I) continue;
+        const E* src = wu_slot(J) + (hf * 8 * kWave + lane) * 4;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          const Frag16<E> w = ld16(src + ct * kWave * 4);
+          M[ct] = mma16(M[ct], nL[J], w);
         }
       }
-    }
-    lds_barrier();   // every read of Ti's diagonal blocks precedes P's writes
+      floatx4 wt[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      int I, J;
-      plan(u, I, J);
-      if (I < 0) continue;
-      // lane holds P[16 I + 4 g + e][16 J + r] -> M2[16 J + r][16 I + 4 g + e]
+      for (int ct = 0; ct < 8; ++ct) {
+        const Frag16<E> mb = frag16<E>(M[ct]);
+        const floatx4 o = mma16(zero4(), tiT, mb);    // W_I / U_I tile, token-major
+        wu[hf * 8 + ct] = frag16<E>(o);
+        if (hf) store_c4(UC + (ct * 8 + I) * kWave * 4, lane, o);
+        else wt[ct] = mma16(zero4(), mb, tiT);        // W_I^T tile
+      }
+      if (!hf) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (I > J || 4 * g + e >= r) M2[(16 * J + r) * kLS + 16 * I + 4 * g + e] = acc[u][e];
+        for (int kb = 0; kb < 4; ++kb) {
+          Frag<E> f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { f.set(e, -wt[2 * kb][e]); f.set(4 + e, -wt[2 * kb + 1][e]); }
+          store_frag(XA + (I * 4 + kb) * kWave * 8, lane, f);
+        }
+      }
+      if (I < 3) {
+        E* dst = wu_slot(I) + (hf * 8 * kWave + lane) * 4;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) st16(dst + ct * kWave * 4, wu[hf * 8 + ct]);
+      }
     }
   }
-  lds_barrier();
-  // Rows of Ti and P as operand fragments: bf16 copies (row-major,
-  // swizzled) for bf16 I/O, masked reads of M2 for fp32.
-  if constexpr (sizeof(E) == 2) {
-    const int i = t & 63, c0 = (t >> 6) * 8;
-    Frag<bf16> ft, fp;
+  for (int s = I; s < 3; ++s) lds_barrier();
+
+  // ---- 5. Qt_I^T = (Gamma Q_I)^T - sum_{J<=I} W_J^T A_qk,IJ^T and
+  //         Ut_I^T = sum_{J<=I} U_J^T A_qk,IJ^T (rows = channel / value column).
 #pragma unroll
-    for (int z = 0; z < 8; ++z) {
-      const int c = c0 + z;
-      ft.set(z, ti_at(M2, i, c));
-      fp.set(z, c <= i ? M2[c * kLS + i] : 0.f);
+  for (int hf = 0; hf < 2; ++hf) {
+    floatx4 acc[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[ct][e] = hf ? 0.f : GQ[ct].get(e);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J > I) continue;
+      const Frag16<E>& bop = hf ? aq[J] : naq[J];
+      if (J < I) {
+        const E* src = wu_slot(J) + (hf * 8 * kWave + lane) * 4;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          const Frag16<E> w = ld16(src + ct * kWave * 4);
+          acc[ct] = mma16(acc[ct], w, bop);
+        }
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = mma16(acc[ct], wu[hf * 8 + ct], bop);
+      }
     }
-    lds_barrier();   // M1's storage (A_qk^T) is free once P is done
-    store8(&sTib[mat_at(i, c0)], ft);
-    store8(&sPb[mat_at(i, c0)], fp);
-    lds_barrier();
-  }
-  auto mat_frag = [&](bool isP, int Rr, int k0, Frag<E>& f) {
-    if constexpr (sizeof(E) == 2) {
-      lds_frag((isP ? sPb : sTib) + mat_at(Rr, k0), f);
+    if (!hf) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        Frag<E> f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f.set(e, acc[2 * kb][e]); f.set(4 + e, acc[2 * kb + 1][e]); }
+        store_frag(XA + ((4 + I) * 4 + kb) * kWave * 8, lane, f);
+      }
     } else {
 #pragma unroll
-      for (int z = 0; z < 8; ++z) {
-        const int c = k0 + z;
-        f.set(z, isP ? (c <= Rr ? M2[c * kLS + Rr] : 0.f) : ti_at(M2, Rr, c));
-      }
+      for (int ct = 0; ct < 8; ++ct) store_c4(UC + (ct * 8 + 4 + I) * kWave * 4, lane, acc[ct]);
     }
-  };
-
-  // v rows for step 6, fetched now so step 5 hides the latency (rows past
-  // the end repeat the last row; step 6 multiplies them by beta = 0)
-  constexpr int kPerV = kC * R::kPieces / kIntraThreads;
-  Vec16<E> vvec[kPerV];
-#pragma unroll
-  for (int u = 0; u < kPerV; ++u) {
-    const int pc = t + u * kIntraThreads, i = pc / R::kPieces, c = (pc % R::kPieces) * R::kPer16;
-    vvec[u] = *reinterpret_cast<const Vec16<E>*>(v + row(min(i, len - 1)) + c);
-  }
-
-  // ---- 5. [-W^T | Qt^T] = (-B1)^T [Ti^T | P^T] + [0 | (Gamma*Q)^T] with
-  //         B1 = Diag(beta) exp(g_s) Kr and Gamma*Q = exp(g_s) Qr. Wave w
-  //         owns key channels [16 w, 16 w + 16).
-  {
-    const int cc = 16 * w + r, c4 = 16 * w + 4 * g;
-    floatx4 acc[8];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      acc[nt] = zero4();
-      if (nt < 4) continue;
-      const int Rr = 16 * (nt - 4) + r;
-      float qv[4];
-      load4(&sQ[R::at(Rr, c4)], qv);
-      const float4 es = *reinterpret_cast<const float4*>(&sEs[(Rr >> 4) * kD + c4]);
-      acc[nt][0] = es.x * qv[0];
-      acc[nt][1] = es.y * qv[1];
-      acc[nt][2] = es.z * qv[2];
-      acc[nt][3] = es.w * qv[3];
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      Frag<E> fa;
-      const int i0 = 32 * kb + 8 * g;                 // standard order: one block
-      const float es = -sEs[(i0 >> 4) * kD + cc];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fa.set(e, sb[i0 + e] * es * to_f(sK[R::at(i0 + e, cc)]));
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        Frag<E> fb;
-        mat_frag(nt >= 4, 16 * (nt & 3) + r, i0, fb);
-        acc[nt] = mma(acc[nt], fa, fb);
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      store_half_frag(XA + (nt * 4 + (w >> 1)) * kWave * 8, lane, w & 1, acc[nt]);
-  }
-
-  // v takes Kr's storage once every wave is past step 5
-  lds_barrier();
-  E* const sV = sK;
-#pragma unroll
-  for (int u = 0; u < kPerV; ++u) {
-    const int pc = t + u * kIntraThreads, i = pc / R::kPieces, c = (pc % R::kPieces) * R::kPer16;
-    *reinterpret_cast<Vec16<E>*>(&sV[R::at(i, c)]) = vvec[u];
-  }
-  lds_barrier();
-
-  // ---- 6. U = Ti (beta V) (rows = token) and Ut^T = (beta V)^T P^T (rows =
-  //         value column); the same (beta V) fragment serves as B and as A.
-  //         Wave w owns value columns [16 w, 16 w + 16).
-  {
-    floatx4 acc[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int i0 = 32 * kb + 8 * g;
-      Frag<E> fv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fv.set(e, sb[i0 + e] * to_f(sV[R::at(i0 + e, 16 * w + r)]));
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        Frag<E> fm;
-        mat_frag(mt >= 4, 16 * (mt & 3) + r, i0, fm);
-        acc[mt] = mt < 4 ? mma(acc[mt], fm, fv) : mma(acc[mt], fv, fm);
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) store_c4(UC + (w * 8 + mt) * kWave * 4, lane, acc[mt]);
   }
 }
 
