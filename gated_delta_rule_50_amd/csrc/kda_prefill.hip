@@ -145,22 +145,29 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_offset,
     const int32_t* __restrict__ status, int32_t n_seqs, int64_t T, int32_t H,
     uint8_t* __restrict__ inter) {
-  // LDS:
-  //   sKf   Kf fragments of the four blocks [J][kb][lane][8]; once every wave
-  //         is past its A tiles, its two halves hold W | U of blocks 1 and 2
-  //   sWU0  W | U of block 0 as accumulator tiles [tile][lane][4]
-  //   sTot  per-block sums of log alpha; sE = exp(sum), sEi = exp(-sum)
-  //   sB    beta
-  //   sF    per-block channel factors (five rows per block)
-  constexpr int kWU = 16 * kWave * 4;
-  __shared__ __attribute__((aligned(16))) E sKf[4 * 4 * kWave * 8];
-  __shared__ __attribute__((aligned(16))) E sWU0[kWU];
-  __shared__ __attribute__((aligned(16))) float sTot[4 * kD];
-  __shared__ __attribute__((aligned(16))) float sE[4 * kD];
-  __shared__ __attribute__((aligned(16))) float sEi[4 * kD];
+  // LDS, one region reused across phases:
+  //   rows phase   sKf  Kf fragments of the four blocks [J][kb][lane][8]
+  //                sF   per-block channel factors (five rows per block)
+  //                sTot per-block sums of log alpha; sE = exp(sum), sEi = exp(-sum)
+  //   tiles phase  sX   per block, 16 token-major accumulator tiles
+  //                     [block][tile][lane][4]: beta Gamma K (tiles 0-7, key
+  //                     channels) and beta V (8-15, value columns), each
+  //                     replaced by W / U once solved
+  //                sNL  -L_IJ (J < I) A-operand tiles [I][J]; sTI Ti_II^T tiles
+  //   sB           beta (both phases)
+  constexpr int kTile = kWave * 4;                        // elements per tile
+  constexpr int kRowsBytes = 4 * 4 * kWave * 8 * (int)sizeof(E) + (5 + 3) * 4 * kD * 4;
+  constexpr int kTilesBytes = (4 * 16 + 12 + 4) * kTile * (int)sizeof(E);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRowsBytes > kTilesBytes ? kRowsBytes : kTilesBytes];
   __shared__ __attribute__((aligned(16))) float sB[kC];
-  __shared__ __attribute__((aligned(16))) float sF[4 * 5 * kD];
-  auto wu_slot = [&](int J) -> E* { return J == 0 ? sWU0 : sKf + (J - 1) * kWU; };
+  E* const sKf = reinterpret_cast<E*>(smem);
+  float* const sF = reinterpret_cast<float*>(smem + 4 * 4 * kWave * 8 * sizeof(E));
+  float* const sTot = sF + 4 * 5 * kD;
+  float* const sE = sTot + 4 * kD;
+  float* const sEi = sE + 4 * kD;
+  E* const sX = reinterpret_cast<E*>(smem);
+  E* const sNL = sX + 4 * 16 * kTile;
+  E* const sTI = sNL + 12 * kTile;
 
   if (status[0] != 0) return;
   const int b = blockIdx.x, h = blockIdx.y;
@@ -308,13 +315,10 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     store_half_frag(KT + (ct * 2 + (I >> 1)) * kWave * 8, lane, I & 1, mma16(zero4(), kp, idf));
   }
 
-  // v rows, needed from step 4 on
+  // v rows (identity tokens repeat the last valid row; beta = 0 zeroes them)
   Frag16<E> vx[8];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    const Frag16<E> d = ld16(v + ro + 16 * ct + 4 * g);
-    vx[ct] = valid ? d : zero;
-  }
+  for (int ct = 0; ct < 8; ++ct) vx[ct] = ld16(v + ro + 16 * ct + 4 * g);
 
   // A tiles. For J < I, A_kk[i][j] = sum_c (Kr_i D_IJ) Kf_j (same for A_qk
   // with Qr); the diagonal block uses D_II = exp(-block sum) >= 1, and where
@@ -414,9 +418,8 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     const floatx4 P2 = P1 + mm16(P1T, X4), P2T = P1T + mm16(X4, P1T);
     tiT = frag16<E>(P2 + mm16(P2T, X8));
   }
-  // -L_IJ (J < I) as A operands, A_qk (J <= I, masked on the diagonal) and
-  // its negation as B operands, beta V row pieces
-  Frag16<E> nL[3], aq[4], naq[4], Vb[8];
+  // A_qk (J <= I, masked on the diagonal) and its negation as B operands
+  Frag16<E> aq[4], naq[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
 #pragma unroll
@@ -424,61 +427,85 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
       const float x = (J < I || 4 * g + e <= r) ? aqT[J][e] : 0.f;
       aq[J].set(e, x);
       naq[J].set(e, -x);
-      if (J < 3) nL[J].set(e, -bt * akT[J][e]);
     }
   }
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Vb[ct].set(e, bt * vx[ct].get(e));
 
-  // ---- 4. blocked forward substitution, one block per barrier interval.
-  Frag16<E> wu[16];   // W_I (tiles 0-7, key channels) | U_I (8-15, value columns)
-  for (int s = 0; s < I; ++s) lds_barrier();
+  // ---- 4. publish this block's operands of the solve: token-major beta
+  //         Gamma K and beta V tiles (row pieces times the identity), -L_IJ
+  //         and Ti_II^T. The rows-phase LDS is dead once every wave is here.
+  lds_barrier();
   {
+    E* const x = sX + (I * 16) * kTile + lane * 4;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      floatx4 M[8];
+    for (int ct = 0; ct < 8; ++ct) {
+      Frag16<E> vb;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) M[ct] = mma16(zero4(), hf ? Vb[ct] : Bx[ct], idf);
+      for (int e = 0; e < 4; ++e) vb.set(e, bt * vx[ct].get(e));
+      st16(x + ct * kTile, frag16<E>(mma16(zero4(), Bx[ct], idf)));
+      st16(x + (8 + ct) * kTile, frag16<E>(mma16(zero4(), vb, idf)));
+    }
+#pragma unroll
+    for (int J = 0; J < 3; ++J) {
+      if (J >= I) continue;
+      Frag16<E> nl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nl.set(e, -bt * akT[J][e]);
+      st16(sNL + (I * 3 + J) * kTile + lane * 4, nl);
+    }
+    st16(sTI + I * kTile + lane * 4, tiT);
+  }
+  lds_barrier();
+
+  // ---- 5. blocked forward substitution by tiles: wave w solves tiles
+  //         4w .. 4w+3 of [W | U] for all four blocks in order,
+  //           [W | U]_I = Ti_II ([B | V']_I - sum_{J<I} L_IJ [W | U]_J),
+  //         keeping its own earlier blocks in registers (no barrier between
+  //         blocks), and overwrites each [B | V'] tile with the result.
+  {
+    const int w = I;
+    Frag16<E> sol[4][4];   // [block][tile]
+#pragma unroll
+    for (int Ib = 0; Ib < 4; ++Ib) {
+      E* const x = sX + (Ib * 16 + 4 * w) * kTile + lane * 4;
+      const Frag16<E> ti = ld16(sTI + Ib * kTile + lane * 4);
+      floatx4 M[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const Frag16<E> b0 = ld16(x + t * kTile);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) M[t][e] = b0.get(e);
+      }
 #pragma unroll
       for (int J = 0; J < 3; ++J) {
-        if (J >= I) continue;
-        const E* src = wu_slot(J) + (hf * 8 * kWave + lane) * 4;
+        if (J >= Ib) continue;
+        const Frag16<E> nl = ld16(sNL + (Ib * 3 + J) * kTile + lane * 4);
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          const Frag16<E> w = ld16(src + ct * kWave * 4);
-          M[ct] = mma16(M[ct], nL[J], w);
-        }
+        for (int t = 0; t < 4; ++t) M[t] = mma16(M[t], nl, sol[J][t]);
       }
-      floatx4 wt[8];
+      floatx4 wt[4];
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const Frag16<E> mb = frag16<E>(M[ct]);
-        const floatx4 o = mma16(zero4(), tiT, mb);    // W_I / U_I tile, token-major
-        wu[hf * 8 + ct] = frag16<E>(o);
-        if (hf) store_c4(UC + (ct * 8 + I) * kWave * 4, lane, o);
-        else wt[ct] = mma16(zero4(), mb, tiT);        // W_I^T tile
+      for (int t = 0; t < 4; ++t) {
+        const Frag16<E> mb = frag16<E>(M[t]);
+        const floatx4 o = mma16(zero4(), ti, mb);     // token-major W / U tile
+        sol[Ib][t] = frag16<E>(o);
+        st16(x + t * kTile, sol[Ib][t]);
+        if (w >= 2) store_c4(UC + ((4 * (w - 2) + t) * 8 + Ib) * kWave * 4, lane, o);
+        else wt[t] = mma16(zero4(), mb, ti);          // W^T tile
       }
-      if (!hf) {
+      if (w < 2) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kk = 0; kk < 2; ++kk) {
           Frag<E> f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { f.set(e, -wt[2 * kb][e]); f.set(4 + e, -wt[2 * kb + 1][e]); }
-          store_frag(XA + (I * 4 + kb) * kWave * 8, lane, f);
+          for (int e = 0; e < 4; ++e) { f.set(e, -wt[2 * kk][e]); f.set(4 + e, -wt[2 * kk + 1][e]); }
+          store_frag(XA + (Ib * 4 + 2 * w + kk) * kWave * 8, lane, f);
         }
-      }
-      if (I < 3) {
-        E* dst = wu_slot(I) + (hf * 8 * kWave + lane) * 4;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) st16(dst + ct * kWave * 4, wu[hf * 8 + ct]);
       }
     }
   }
-  for (int s = I; s < 3; ++s) lds_barrier();
+  lds_barrier();
 
-  // ---- 5. Qt_I^T = (Gamma Q_I)^T - sum_{J<=I} W_J^T A_qk,IJ^T and
+  // ---- 6. Qt_I^T = (Gamma Q_I)^T - sum_{J<=I} W_J^T A_qk,IJ^T and
   //         Ut_I^T = sum_{J<=I} U_J^T A_qk,IJ^T (rows = channel / value column).
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -491,17 +518,9 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     for (int J = 0; J < 4; ++J) {
       if (J > I) continue;
       const Frag16<E>& bop = hf ? aq[J] : naq[J];
-      if (J < I) {
-        const E* src = wu_slot(J) + (hf * 8 * kWave + lane) * 4;
+      const E* src = sX + (J * 16 + hf * 8) * kTile + lane * 4;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          const Frag16<E> w = ld16(src + ct * kWave * 4);
-          acc[ct] = mma16(acc[ct], w, bop);
-        }
-      } else {
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = mma16(acc[ct], wu[hf * 8 + ct], bop);
-      }
+      for (int ct = 0; ct < 8; ++ct) acc[ct] = mma16(acc[ct], ld16(src + ct * kTile), bop);
     }
     if (!hf) {
 #pragma unroll
@@ -519,104 +538,181 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
 }
 
 // ------------------------------------------------------- sequential carry
-// One wave per 16-column tile of the state. Per chunk:
-//   X[0..3] = U + [-W] S            pseudo-value (rows = token)
-//   X[4..7] = Ut^T + S^T Qt^T       O^T (rows = value column)
-//   S = Diag(gamma_C) S + K'^T X[0..3]
-// The state never leaves registers; its accumulator tiles feed the next
-// products directly in the split K order (as B operand for -W S and as A
-// operand for S^T Qt^T -- the two fragment layouts are the same).
+// One workgroup per (sequence, head, 16-column tile of the state), four
+// waves. Per chunk:
+//   state wave    X = U + [-W] S            pseudo-value (rows = token)
+//                 S = Diag(gamma_C) S + K'^T X
+//   output wave   O^T = Ut^T + S^T Qt^T     (rows = value column)
+//   loader waves  stream the state wave's operands into an LDS ring
+// Loader 1 also touches one word per 128-byte line of this tile's eighth of
+// the block six chunks ahead (buffer->LDS loads into a scratch slot, no
+// registers), so the loaders and the output wave find the blocks in L2
+// rather than waiting on HBM.
+// The state never leaves the state wave's registers; its accumulator tiles
+// feed the next products directly in the split K order. At the end of each
+// chunk the state wave also publishes the new state as bf16 operand
+// fragments in one of two LDS buffers, which the output wave uses in the
+// next chunk, so one workgroup barrier per chunk orders everything and only
+// 32 of the 48 products per chunk sit on the sequential path.
 //
-// bf16 intermediates: each workgroup has one compute wave and one loader
-// wave. The loader streams chunk b+2's block (fragments of [-W ; Qt], K'^T,
-// this tile's [U ; Ut^T] and gamma_C) into a three-deep LDS ring with
-// buffer->LDS DMA and waits only for its own loads; the compute wave never
-// waits on memory except LDS, so its output stores stay in flight. fp32
-// intermediates (twice the bytes; fp32 I/O only) are read from global memory
-// by the compute wave directly.
-constexpr int kRing = 3;
+// bf16 intermediates: the two loaders keep chunks b+2 and b+3 of [-W], K'^T,
+// this tile's U and gamma_C in flight (buffer->LDS DMA into a four-deep
+// ring, each loader below the hardware's outstanding-load limit); the state
+// wave reads chunk b+1's fragments into a second register set while it
+// computes chunk b; the output wave loads its Qt fragments and Ut^T from
+// global memory two chunks ahead. fp32 intermediates (fp32 I/O only) are
+// read from global memory by both compute waves without prefetch.
+constexpr int kRing = 4;
+constexpr int kCarryThreads = 256;
+constexpr int kTouchAhead = 6;   // chunks between the L2 touch and the use of a block
 
-template <class E>
-__device__ __forceinline__ void carry_chunk(floatx4 (&S)[8], const E* XA, const E* KT,
-                                            const E* UC, const float* GC, E* __restrict__ o,
-                                            int64_t tok0, int len, int H, int h, int lane,
-                                            int j0) {
-  const int g = lane >> 4;
-  // Operand fragments are fetched one k-block ahead of the products that
-  // use them, so LDS latency overlaps the matrix-core work.
-  Frag<E> fa[2][8];
-  floatx4 X[8];
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) load_frag(XA + (mt * 4 + 0) * kWave * 8, lane, fa[0][mt]);
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) X[mt] = load_c4(UC + mt * kWave * 4, lane);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    if (kb + 1 < 4) {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        load_frag(XA + (mt * 4 + kb + 1) * kWave * 8, lane, fa[(kb + 1) & 1][mt]);
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) load_frag(KT + (mt * 2 + 0) * kWave * 8, lane, fa[0][mt]);
-    }
-    Frag<E> fs;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { fs.set(e, S[2 * kb][e]); fs.set(4 + e, S[2 * kb + 1][e]); }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) X[mt] = mma(X[mt], fa[kb & 1][mt], fs);
-#pragma unroll
-    for (int mt = 4; mt < 8; ++mt) X[mt] = mma(X[mt], fs, fa[kb & 1][mt]);
-  }
-  // O^T: lane (i = 16 nt + r, j = j0 + 4 g .. +3) holds four consecutive
-  // outputs of one token, written as one 8-byte (bf16) store.
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int i = 16 * nt + (lane & 15);
-    if (i < len) store4_io(o + ((tok0 + i) * H + h) * kD + j0 + 4 * g, X[4 + nt]);
-  }
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const float4 gm = *reinterpret_cast<const float4*>(GC + 16 * mt + 4 * g);
-    S[mt][0] *= gm.x; S[mt][1] *= gm.y; S[mt][2] *= gm.z; S[mt][3] *= gm.w;
-  }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    if (kb == 0) {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) load_frag(KT + (mt * 2 + 1) * kWave * 8, lane, fa[1][mt]);
-    }
-    Frag<E> fv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { fv.set(e, X[2 * kb][e]); fv.set(4 + e, X[2 * kb + 1][e]); }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(S[mt], fa[kb][mt], fv);
-  }
-}
-
-// Workgroup barrier without a memory fence: the compute wave reads only
-// LDS that the loader wave has already waited for, and no wave writes LDS.
+// Workgroup barrier without a memory fence: no wave waits on another's
+// global memory traffic, and LDS hand-offs are fenced by lgkmcnt where
+// written.
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Staged bytes per chunk: [-W ; Qt] and K'^T (48 KiB), the tile's
-// [U ; Ut^T] (4 KiB), gamma_C (512 B, in a 1 KiB slot).
-constexpr int kStageShared = (kXAElems + kKTElems) * 2;
-constexpr int kStageUC = 8 * kWave * 4 * 2;
-constexpr int kStageBuf = kStageShared + kStageUC + 1024;
-constexpr int kStageDMA = kStageBuf / 1024;   // 1 KiB DMA instructions per chunk
+// Staged bytes per chunk: [-W] and K'^T fragments (32 KiB), the tile's U
+// (2 KiB), gamma_C (512 B, in a 1 KiB slot). Loader 0 moves [-W] and U
+// (18 KiB), loader 1 K'^T and gamma_C (17 KiB), 1 KiB per DMA instruction.
+constexpr int kStageW = kXAElems / 2 * 2;
+constexpr int kStageKT = kKTElems * 2;
+constexpr int kStageU = 4 * kWave * 4 * 2;
+constexpr int kStageBuf = kStageW + kStageKT + kStageU + 1024;
+constexpr int kDMA0 = (kStageW + kStageU) / 1024;
+constexpr int kDMA1 = kStageKT / 1024 + 1;
+
+// State wave operands of one chunk.
+template <class E>
+struct StateOps {
+  Frag<E> fw[4][4];   // [-W] fragments [token tile][k-slice]
+  Frag<E> fk[8][2];   // K'^T fragments [channel tile][k-slice]
+  Frag16<E> u[4];     // U accumulator tiles, in the I/O type
+  floatx4 gm[8];      // gamma_C of the rows 16 mt + 4 g .. + 3
+};
+template <class E>
+__device__ __forceinline__ void load_state_ops(StateOps<E>& p, const E* XW, const E* KT,
+                                               const E* UA, const float* GC, int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) p.u[mt] = ld16(UA + (mt * kWave + lane) * 4);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) p.gm[mt] = *reinterpret_cast<const floatx4*>(GC + 16 * mt + 4 * g);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) load_frag(XW + (mt * 4 + kb) * kWave * 8, lane, p.fw[mt][kb]);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) load_frag(KT + (mt * 2 + kb) * kWave * 8, lane, p.fk[mt][kb]);
+}
+
+// State wave, one chunk: S <- Diag(gamma) S + K'^T (U + [-W] S), with the
+// fragments of S (fs) in registers on entry and of the new S on exit.
+template <class E>
+__device__ __forceinline__ void carry_state(floatx4 (&S)[8], Frag<E> (&fs)[4],
+                                            const StateOps<E>& p) {
+  floatx4 X[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) X[mt] = zero4();
+  // pseudo-value tiles 0, 1 first: they feed the first half of the update
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) X[mt] = mma(X[mt], p.fw[mt][kb], fs[kb]);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int mt = 2; mt < 4; ++mt) X[mt] = mma(X[mt], p.fw[mt][kb], fs[kb]);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[mt][e] += p.u[mt].get(e);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) S[mt] *= p.gm[mt];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    Frag<E> fv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { fv.set(e, X[2 * kb][e]); fv.set(4 + e, X[2 * kb + 1][e]); }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(S[mt], p.fk[mt][kb], fv);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
+}
+
+// Output wave operands of one chunk: Qt fragments and this tile's Ut^T.
+template <class E>
+struct OutOps {
+  Frag<E> fq[4][4];
+  Frag16<E> ut[4];   // kept in the I/O type until used: no wait at load time
+};
+template <class E>
+__device__ __forceinline__ void load_out_ops(OutOps<E>& p, const E* blk, int jt, int lane) {
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      load_frag(blk + Inter<E>::kXA + ((4 + nt) * 4 + kb) * kWave * 8, lane, p.fq[nt][kb]);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+    p.ut[nt] = ld16(blk + Inter<E>::kUC + ((jt * 8 + 4 + nt) * kWave + lane) * 4);
+}
+
+// Output wave, one chunk: O^T = Ut^T + S^T Qt^T; lane (i = 16 nt + r,
+// j = j0 + 4 g .. +3) holds four consecutive outputs of one token. They go
+// to LDS in the I/O type; the state wave stores them to global memory.
+template <class E>
+__device__ __forceinline__ void carry_out(const OutOps<E>& p, const Frag<E> (&fs)[4],
+                                          E* sOb, int lane) {
+  floatx4 X[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[nt][e] = p.ut[nt].get(e);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) X[nt] = mma(X[nt], fs[kb], p.fq[nt][kb]);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) st16(sOb + (nt * kWave + lane) * 4, frag16<E>(X[nt]));
+}
+
+// Stores one chunk's O tile (16 columns) from LDS for the valid tokens.
+// Only the state wave issues global stores: it never waits on global loads,
+// so the stores' completion never stalls a load wait (on this architecture
+// one counter tracks both).
+template <class E>
+__device__ __forceinline__ void store_out(const E* sOb, E* __restrict__ o, int64_t tok0, int len,
+                                          int H, int h, int lane, int j0) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int i = 16 * nt + (lane & 15);
+    const Frag16<E> x = ld16(sOb + (nt * kWave + lane) * 4);
+    if (i < len) st16(o + ((tok0 + i) * H + h) * kD + j0 + 4 * g, x);
+  }
+}
 
 template <class E>
-__global__ __launch_bounds__(128) void carry_kernel(
-    const uint8_t* __restrict__ inter, const int32_t* __restrict__ cu,
+__global__ __launch_bounds__(kCarryThreads) void carry_kernel(
+    const uint8_t* inter,   // not restrict: prefetch loads stay ahead of the barriers
+    const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
     const float* __restrict__ h0, float* __restrict__ h_final, E* __restrict__ o,
     int32_t n_seqs, int64_t T, int32_t H) {
   constexpr bool kStaged = sizeof(E) == 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStaged ? kRing * kStageBuf : 16];
+  __shared__ __attribute__((aligned(16))) E sS[2 * 4 * kWave * 8];   // published state
+  __shared__ __attribute__((aligned(16))) int32_t sTouch[kWave];        // L2 touch sink
+  __shared__ __attribute__((aligned(16))) E sO[2 * 4 * kWave * 4];      // output tiles
 
   // XCD-aware order: consecutive ids go round-robin over the 8 XCDs; give the
   // 8 tiles of one (sequence, head) the same id % 8 so they share an L2.
@@ -626,98 +722,194 @@ __global__ __launch_bounds__(128) void carry_kernel(
   if (pair >= n_seqs * H) return;
   if (status[0] != 0) return;
   const int n = pair / H, h = pair % H;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;  // w 0: compute, 1: loader
+  const int lane = threadIdx.x & 63;
+  // wave 0: state, 1: output, 2 and 3: loaders
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int j = 16 * jt + (lane & 15);
   const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
   const int b0 = chunk_offset[n], b1 = chunk_offset[n + 1];
   auto block_of = [&](int b) { return inter + ((int64_t)b * H + h) * Inter<E>::kBytes; };
+  auto slot = [&](int b) { return lds + ((b - b0) & (kRing - 1)) * kStageBuf; };
+  auto publish = [&](const Frag<E> (&fs)[4], int b) {
+    E* dst = sS + ((b - b0) & 1) * 4 * kWave * 8;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) store8(dst + (kb * kWave + lane) * 8, fs[kb]);
+  };
 
-  floatx4 S[8];
+  // loader w = 2 moves [-W] and U, w = 3 moves K'^T and gamma_C
+  auto issue = [&](int b) {
+    const uint8_t* src = block_of(b);
+    uint8_t* dst = slot(b);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)src, 0, (int)Inter<E>::kBytes, 0x00020000);
+    if (w == 2) {
+#pragma unroll
+      for (int i = 0; i < kStageW / 1024; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, lane * 16,
+            (int)(Inter<E>::kXA * sizeof(E)) + i * 1024, 0, 0);
+      const int uc = (int)(Inter<E>::kUC * sizeof(E)) + jt * 8 * kWave * 4 * 2;
+#pragma unroll
+      for (int i = 0; i < kStageU / 1024; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + kStageW + kStageKT + i * 1024),
+            16, lane * 16, uc + i * 1024, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kStageKT / 1024; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + kStageW + i * 1024), 16,
+            lane * 16, (int)(Inter<E>::kKT * sizeof(E)) + i * 1024, 0, 0);
+      // gamma_C: 512 bytes; lanes >= 32 read past the block and get zeros
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + kStageW + kStageKT + kStageU),
+          16, lane * 16, (int)Inter<E>::kGCByte, 0, 0);
+    }
+  };
+  // L2 touch of chunk b by loader 1: one word per 128-byte line of lines
+  // [jt * kShare, (jt + 1) * kShare) of the block
+  constexpr int kLines = (int)((Inter<E>::kBytes + 127) / 128);
+  constexpr int kShare = (kLines + 7) / 8;
+  constexpr int kTouchOps = (kShare + kWave - 1) / kWave;
+  auto touch = [&](int b) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)block_of(b), 0, (int)Inter<E>::kBytes, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < kTouchOps; ++u) {
+      const int line = min(jt * kShare + u * kWave + lane, kLines - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)sTouch, 4, line * 128, 0, 0, 0);
+    }
+  };
+  // Iteration b: after issuing chunk b+3 (dma) and touching chunk b+6
+  // (tch), wait until chunk b+2 has landed. The memory counter retires in
+  // order, so the wait allows exactly the instructions issued after chunk
+  // b+2's: the previous iteration's touch (prev), this iteration's DMA and
+  // touch. Fewer allowed instructions only wait longer.
+  auto loader_wait = [&](bool dma, bool tch, bool prev) {
+    if (!dma) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if (w == 2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMA0) : "memory");
+    } else if (tch) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMA1 + 2 * kTouchOps) : "memory");
+    } else if (prev) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMA1 + kTouchOps) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMA1) : "memory");
+    }
+  };
+
+  // state operand sources of chunk b: the LDS ring (bf16) or the block (fp32)
+  auto w_src = [&](int b) -> const E* {
+    if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b));
+    else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kXA;
+  };
+  auto kt_src = [&](int b) -> const E* {
+    if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b) + kStageW);
+    else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kKT;
+  };
+  auto u_src = [&](int b) -> const E* {
+    if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b) + kStageW + kStageKT);
+    else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kUC + jt * 8 * kWave * 4;
+  };
+  auto gc_src = [&](int b) -> const float* {
+    if constexpr (kStaged)
+      return reinterpret_cast<const float*>(slot(b) + kStageW + kStageKT + kStageU);
+    else return reinterpret_cast<const float*>(block_of(b) + Inter<E>::kGCByte);
+  };
+
+  // Each role runs its own loop; all execute one barrier before the first
+  // chunk and one per chunk.
   if (w == 0) {
+    floatx4 S[8];
+    Frag<E> fs[4];
     const float* h0p = h0 ? h0 + (int64_t)pair * kD * kD : nullptr;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         S[mt][e] = h0p ? h0p[(16 * mt + 4 * g + e) * kD + j] : 0.f;
-  }
-
-  if constexpr (kStaged) {
-    // loader: one 1 KiB DMA per instruction; SGPR offsets, no VGPR math
-    auto issue = [&](int b) {
-      const uint8_t* src = block_of(b);
-      uint8_t* dst = lds + ((b - b0) % kRing) * kStageBuf;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)src, 0, (int)Inter<E>::kBytes, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < kStageShared / 1024; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, lane * 16,
-            i * 1024, 0, 0);
-      const int uc = (int)(Inter<E>::kUC * sizeof(E)) + jt * kStageUC;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < kStageUC / 1024; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + kStageShared + i * 1024), 16,
-            lane * 16, uc + i * 1024, 0, 0);
-      // gamma_C: 512 bytes; lanes >= 32 read past the block and get zeros
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(dst + kStageShared + kStageUC), 16,
-          lane * 16, (int)Inter<E>::kGCByte, 0, 0);
+      for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
+    publish(fs, b0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    ring_barrier();
+    StateOps<E> sa, sb;   // alternating chunks
+    auto fetch = [&](StateOps<E>& p, int b) {
+      load_state_ops(p, w_src(b), kt_src(b), u_src(b), gc_src(b), lane);
     };
-    if (w == 1) {
-      if (b0 < b1) issue(b0);
-      if (b0 + 1 < b1) {
-        issue(b0 + 1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageDMA) : "memory");
+    if (kStaged && b0 < b1) fetch(sa, b0);
+    auto out_of = [&](int b) {   // O of chunk b, written by the output wave
+      const int64_t tok0 = seq_start + (int64_t)(b - b0) * kC;
+      const int len = (int)min((int64_t)kC, seq_end - tok0);
+      store_out<E>(sO + ((b - b0) & 1) * 4 * kWave * 4, o, tok0, len, H, h, lane, 16 * jt);
+    };
+    auto step = [&](int b, StateOps<E>& cur, StateOps<E>& nxt) {
+      if constexpr (kStaged) {
+        if (b + 1 < b1) fetch(nxt, b + 1);
       } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        fetch(cur, b);
       }
+      if (b > b0) out_of(b - 1);
+      carry_state<E>(S, fs, cur);
+      publish(fs, b + 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      ring_barrier();
+    };
+    for (int b = b0; b < b1; b += 2) {
+      step(b, sa, sb);
+      if (b + 1 < b1) step(b + 1, sb, sa);
+    }
+    if (b0 < b1) out_of(b1 - 1);
+    if (h_final) {
+      float* hf = h_final + (int64_t)pair * kD * kD;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
+    }
+  } else if (w == 1) {
+    OutOps<E> oa, ob;     // alternating chunks
+    if (b0 < b1) load_out_ops(oa, reinterpret_cast<const E*>(block_of(b0)), jt, lane);
+    if (b0 + 1 < b1) load_out_ops(ob, reinterpret_cast<const E*>(block_of(b0 + 1)), jt, lane);
+    ring_barrier();
+    auto step = [&](int b, OutOps<E>& out) {
+      Frag<E> fsb[4];
+      const E* src = sS + ((b - b0) & 1) * 4 * kWave * 8;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) lds_frag(src + (kb * kWave + lane) * 8, fsb[kb]);
+      carry_out<E>(out, fsb, sO + ((b - b0) & 1) * 4 * kWave * 4, lane);
+      if (b + 2 < b1) load_out_ops(out, reinterpret_cast<const E*>(block_of(b + 2)), jt, lane);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // O tile written
+      ring_barrier();
+    };
+    for (int b = b0; b < b1; b += 2) {
+      step(b, oa);
+      if (b + 1 < b1) step(b + 1, ob);
+    }
+  } else {
+    if (kStaged) {
+      for (int b = b0; b < b0 + 3 && b < b1; ++b) issue(b);
+      loader_wait(b0 + 2 < b1, false, false);   // chunks b0, b0 + 1 landed
+      if (w == 3)
+        for (int b = b0 + 3; b < b0 + kTouchAhead && b < b1; ++b) touch(b);
     }
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
-      if (w == 0) {
-        const uint8_t* base = lds + ((b - b0) % kRing) * kStageBuf;
-        const int64_t tok0 = seq_start + (int64_t)(b - b0) * kC;
-        const int len = (int)min((int64_t)kC, seq_end - tok0);
-        carry_chunk<E>(S, reinterpret_cast<const E*>(base),
-                       reinterpret_cast<const E*>(base) + kXAElems,
-                       reinterpret_cast<const E*>(base + kStageShared),
-                       reinterpret_cast<const float*>(base + kStageShared + kStageUC), o, tok0,
-                       len, H, h, lane, 16 * jt);
-      } else {
-        // chunk b+2 goes into the slot chunk b-1 used; then make sure chunk
-        // b+1 (issued one iteration ago) has landed
-        if (b + 2 < b1) {
-          issue(b + 2);
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageDMA) : "memory");
-        } else {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
+      if (kStaged) {
+        const bool dma = b + 3 < b1;
+        const bool tch = w == 3 && b + kTouchAhead < b1;
+        const bool prev = w == 3 && b + kTouchAhead - 1 < b1;
+        if (dma) issue(b + 3);
+        if (tch) touch(b + kTouchAhead);
+        loader_wait(dma, tch, prev);
       }
       ring_barrier();
     }
-  } else {
-    if (w == 0) {
-      for (int b = b0; b < b1; ++b) {
-        const E* blk = reinterpret_cast<const E*>(block_of(b));
-        const int64_t tok0 = seq_start + (int64_t)(b - b0) * kC;
-        const int len = (int)min((int64_t)kC, seq_end - tok0);
-        carry_chunk<E>(S, blk + Inter<E>::kXA, blk + Inter<E>::kKT,
-                       blk + Inter<E>::kUC + jt * 8 * kWave * 4,
-                       reinterpret_cast<const float*>(
-                           reinterpret_cast<const uint8_t*>(blk) + Inter<E>::kGCByte),
-                       o, tok0, len, H, h, lane, 16 * jt);
-      }
-    }
-  }
-  if (w == 0 && h_final) {
-    float* hf = h_final + (int64_t)pair * kD * kD;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
   }
 }
 
@@ -758,10 +950,10 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, const void* q, const void*
   const int64_t pairs = (int64_t)n_seqs * H;
   const int64_t nblocks = ((pairs + 7) / 8) * 8 * 8;   // 8 column tiles per pair
   if (bf16_io)
-    carry_kernel<bf16><<<(unsigned)nblocks, 128, 0, stream>>>(
+    carry_kernel<bf16><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
         inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H);
   else
-    carry_kernel<float><<<(unsigned)nblocks, 128, 0, stream>>>(
+    carry_kernel<float><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
         inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H);
   return hipGetLastError();
 }
