@@ -674,13 +674,18 @@ __device__ __forceinline__ void carry_out(const OutOps<E>& p, const Frag<E> (&fs
                                           E* sOb, int lane) {
   floatx4 X[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) X[nt][e] = p.ut[nt].get(e);
+  for (int nt = 0; nt < 4; ++nt) X[nt] = zero4();
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) X[nt] = mma(X[nt], fs[kb], p.fq[nt][kb]);
+  // Ut^T joins after the products: converting it earlier would make the
+  // scheduler wait on the newest prefetch
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[nt][e] += p.ut[nt].get(e);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) st16(sOb + (nt * kWave + lane) * 4, frag16<E>(X[nt]));
 }
@@ -690,15 +695,14 @@ __device__ __forceinline__ void carry_out(const OutOps<E>& p, const Frag<E> (&fs
 // so the stores' completion never stalls a load wait (on this architecture
 // one counter tracks both).
 template <class E>
-__device__ __forceinline__ void store_out(const E* sOb, E* __restrict__ o, int64_t tok0, int len,
-                                          int H, int h, int lane, int j0) {
+__device__ __forceinline__ void store_out(const Frag16<E> (&x)[4], E* __restrict__ o,
+                                          int64_t tok0, int len, int H, int h, int lane, int j0) {
   const int g = lane >> 4;
+  E* const base = o + ((tok0 + (lane & 15)) * H + h) * kD + j0 + 4 * g;
+  const int64_t step16 = (int64_t)16 * H * kD;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int i = 16 * nt + (lane & 15);
-    const Frag16<E> x = ld16(sOb + (nt * kWave + lane) * 4);
-    if (i < len) st16(o + ((tok0 + i) * H + h) * kD + j0 + 4 * g, x);
-  }
+  for (int nt = 0; nt < 4; ++nt)
+    if (16 * nt + (lane & 15) < len) st16(base + nt * step16, x[nt]);
 }
 
 template <class E>
@@ -843,28 +847,53 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       load_state_ops(p, w_src(b), kt_src(b), u_src(b), gc_src(b), lane);
     };
     if (kStaged && b0 < b1) fetch(sa, b0);
-    auto out_of = [&](int b) {   // O of chunk b, written by the output wave
+    // O of chunk b, written to LDS by the output wave
+    auto read_out = [&](Frag16<E> (&x)[4], int b) {
+      const E* src = sO + ((b - b0) & 1) * 4 * kWave * 4;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) x[nt] = ld16(src + (nt * kWave + lane) * 4);
+    };
+    auto out_of = [&](const Frag16<E> (&x)[4], int b) {
       const int64_t tok0 = seq_start + (int64_t)(b - b0) * kC;
       const int len = (int)min((int64_t)kC, seq_end - tok0);
-      store_out<E>(sO + ((b - b0) & 1) * 4 * kWave * 4, o, tok0, len, H, h, lane, 16 * jt);
+      store_out<E>(x, o, tok0, len, H, h, lane, 16 * jt);
     };
     auto step = [&](int b, StateOps<E>& cur, StateOps<E>& nxt) {
+      Frag16<E> ob[4];
+      read_out(ob, b - 1);   // first, so its wait does not cover the prefetch
       if constexpr (kStaged) {
-        if (b + 1 < b1) fetch(nxt, b + 1);
+        fetch(nxt, min(b + 1, b1 - 1));
       } else {
         fetch(cur, b);
       }
-      if (b > b0) out_of(b - 1);
       carry_state<E>(S, fs, cur);
+      if constexpr (kStaged) {
+        // one prefetch read per product: a wave stalls once 16 LDS reads
+        // are outstanding, which would hold the products back
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        }
+      }
+      if (b > b0) out_of(ob, b - 1);
       publish(fs, b + 1);
       __builtin_amdgcn_s_waitcnt(0xC07F);
       ring_barrier();
     };
-    for (int b = b0; b < b1; b += 2) {
+    // pairs of chunks, then the odd one: every loop back edge follows both
+    // register sets' loads, so the compiler's counter waits stay exact
+    int b = b0;
+    for (; b + 1 < b1; b += 2) {
       step(b, sa, sb);
-      if (b + 1 < b1) step(b + 1, sb, sa);
+      step(b + 1, sb, sa);
     }
-    if (b0 < b1) out_of(b1 - 1);
+    if (b < b1) step(b, sa, sb);
+    if (b0 < b1) {
+      Frag16<E> ob[4];
+      read_out(ob, b1 - 1);
+      out_of(ob, b1 - 1);
+    }
     if (h_final) {
       float* hf = h_final + (int64_t)pair * kD * kD;
 #pragma unroll
@@ -873,23 +902,33 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
         for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
     }
   } else if (w == 1) {
-    OutOps<E> oa, ob;     // alternating chunks
-    if (b0 < b1) load_out_ops(oa, reinterpret_cast<const E*>(block_of(b0)), jt, lane);
-    if (b0 + 1 < b1) load_out_ops(ob, reinterpret_cast<const E*>(block_of(b0 + 1)), jt, lane);
-    ring_barrier();
     auto step = [&](int b, OutOps<E>& out) {
       Frag<E> fsb[4];
       const E* src = sS + ((b - b0) & 1) * 4 * kWave * 8;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) lds_frag(src + (kb * kWave + lane) * 8, fsb[kb]);
       carry_out<E>(out, fsb, sO + ((b - b0) & 1) * 4 * kWave * 4, lane);
-      if (b + 2 < b1) load_out_ops(out, reinterpret_cast<const E*>(block_of(b + 2)), jt, lane);
+      // unconditional (clamped) so every path issues the same loads and the
+      // compiler's counter waits stay exact
+      load_out_ops(out, reinterpret_cast<const E*>(block_of(min(b + 2, b1 - 1))), jt, lane);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // O tile written
       ring_barrier();
     };
-    for (int b = b0; b < b1; b += 2) {
-      step(b, oa);
-      if (b + 1 < b1) step(b + 1, ob);
+    if (b0 < b1) {
+      OutOps<E> oa, ob;   // alternating chunks, loaded two chunks ahead
+      load_out_ops(oa, reinterpret_cast<const E*>(block_of(b0)), jt, lane);
+      load_out_ops(ob, reinterpret_cast<const E*>(block_of(min(b0 + 1, b1 - 1))), jt, lane);
+      ring_barrier();
+      // pairs of chunks, then the odd one: every loop back edge follows both
+      // register sets' loads
+      int b = b0;
+      for (; b + 1 < b1; b += 2) {
+        step(b, oa);
+        step(b + 1, ob);
+      }
+      if (b < b1) step(b, oa);
+    } else {
+      ring_barrier();
     }
   } else {
     if (kStaged) {
