@@ -78,13 +78,13 @@ def _kernel_key(name):
     for k in ("intra", "carry", "decode", "chunk_map"):
         if k in name:
             return k
-    low = name.lower()
-    # torch's device-to-device copy kernel (not the runtime's host copies)
-    return "copy" if ("copy" in low and "rocclr" not in low) else None
+    # device-to-device copies (the runtime's blit kernel for torch's copy_)
+    return "copy" if "copy" in name.lower() else None
 
 
 def _pmc_means(run_dir, counter):
-    """Mean counter value (KiB) per dispatch of each kernel in one pmc run."""
+    """Mean counter value (KiB) per dispatch of each kernel in one pmc run;
+    for 'copy', the largest dispatch (the 1 GiB calibration copy)."""
     per = {}
     for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         for row in csv.DictReader(open(f)):
@@ -95,12 +95,12 @@ def _pmc_means(run_dir, counter):
                 continue
             per.setdefault(k, {}).setdefault(row["Dispatch_Id"], 0.0)
             per[k][row["Dispatch_Id"]] += float(row["Counter_Value"])
-    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+    return {k: (max(v.values()) if k == "copy" else sum(v.values()) / len(v))
+            for k, v in per.items()}
 
 
 def summarize_pmc(fetch_dir, write_dir):
     f, w = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
-    # the largest 'copy' dispatch is the 1 GiB calibration copy
     fr = COPY_BYTES / (f["copy"] * 1024.0)
     wr = COPY_BYTES / (w["copy"] * 1024.0)
     lines = [f"sources_sha256 = {sources_hash()}",
