@@ -556,13 +556,13 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
 // 32 of the 48 products per chunk sit on the sequential path.
 //
 // bf16 intermediates: the two loaders keep chunks b+2 and b+3 of [-W], K'^T,
-// this tile's U and gamma_C in flight (buffer->LDS DMA into a four-deep
+// this tile's U and gamma_C in flight (buffer->LDS DMA into a three-slot
 // ring, each loader below the hardware's outstanding-load limit); the state
 // wave reads chunk b+1's fragments into a second register set while it
-// computes chunk b; the output wave loads its Qt fragments and Ut^T from
+// computes chunk b, so chunk b's slot is free for chunk b+3 during chunk b; the output wave loads its Qt fragments and Ut^T from
 // global memory two chunks ahead. fp32 intermediates (fp32 I/O only) are
 // read from global memory by both compute waves without prefetch.
-constexpr int kRing = 4;
+constexpr int kRing = 3;
 constexpr int kCarryThreads = 256;
 constexpr int kTouchAhead = 6;   // chunks between the L2 touch and the use of a block
 
@@ -734,7 +734,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
   const int b0 = chunk_offset[n], b1 = chunk_offset[n + 1];
   auto block_of = [&](int b) { return inter + ((int64_t)b * H + h) * Inter<E>::kBytes; };
-  auto slot = [&](int b) { return lds + ((b - b0) & (kRing - 1)) * kStageBuf; };
+  auto slot = [&](int b) { return lds + ((b - b0) % kRing) * kStageBuf; };
   auto publish = [&](const Frag<E> (&fs)[4], int b) {
     E* dst = sS + ((b - b0) & 1) * 4 * kWave * 8;
 #pragma unroll
@@ -847,6 +847,9 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       load_state_ops(p, w_src(b), kt_src(b), u_src(b), gc_src(b), lane);
     };
     if (kStaged && b0 < b1) fetch(sa, b0);
+    // chunk b0's slot is read before the loaders reuse it for chunk b0 + 3
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    ring_barrier();
     // O of chunk b, written to LDS by the output wave
     auto read_out = [&](Frag16<E> (&x)[4], int b) {
       const E* src = sO + ((b - b0) & 1) * 4 * kWave * 4;
@@ -919,6 +922,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       load_out_ops(oa, reinterpret_cast<const E*>(block_of(b0)), jt, lane);
       load_out_ops(ob, reinterpret_cast<const E*>(block_of(min(b0 + 1, b1 - 1))), jt, lane);
       ring_barrier();
+      ring_barrier();
       // pairs of chunks, then the odd one: every loop back edge follows both
       // register sets' loads
       int b = b0;
@@ -929,6 +933,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       if (b < b1) step(b, oa);
     } else {
       ring_barrier();
+      ring_barrier();
     }
   } else {
     if (kStaged) {
@@ -937,6 +942,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       if (w == 3)
         for (int b = b0 + 3; b < b0 + kTouchAhead && b < b1; ++b) touch(b);
     }
+    ring_barrier();
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
       if (kStaged) {
