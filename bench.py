@@ -7,10 +7,12 @@ fp32 gates and state, h0 = 0) followed by one decode step on the decode
 workload (256 sequences x 32 heads, fp32 states of 512 MiB updated in place).
 Inputs are synthetic (seeded generators), resident in HBM before timing.
 
-Printed: ONE JSON line. ``value`` is prefill tokens/s (T / mean prefill time
-per call from HIP events on the launch stream); decode tokens/s is reported
-beside it. ``roofline`` describes the kernel with the longest mean duration
-per step; every kernel's figures are under ``kernels``.
+Printed: ONE JSON line. ``value`` is prefill tokens/s (T / mean prefill call
+time from HIP events on the caller's stream); decode tokens/s is reported
+beside it. After the timed steps the prefill's kernels are also launched one
+at a time (phase entry point, all chunks per launch) to measure each
+kernel's own duration; ``kernels`` holds those and the decode kernel's, and
+``roofline`` describes the one with the longest mean duration.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -216,34 +218,47 @@ def main():
     pairs = cfg4.n_seqs * cfg4.H
 
     def step(ev=None):
+        # one prefill call (pipelined inside the library) + one decode step
         if ev is not None:
             ev[0].record()
-        for ph in range(3):
-            pre.run_phase(ph)
-            if ev is not None:
-                ev[1 + ph].record()
+        pre.run()
+        if ev is not None:
+            ev[1].record()
         decode_step(dq, dk, dv, dla, db, S, o=do)
         if ev is not None:
-            ev[4].record()
+            ev[2].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [_events(torch, 5) for _ in range(args.steps)]
+    evs = [_events(torch, 3) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    prefill_ms = [ev[0].elapsed_time(ev[1]) for ev in evs]
+    decode_ms = [ev[1].elapsed_time(ev[2]) for ev in evs]
 
-    names = ["chunk_map", "intra", "carry", "decode"]
-    dur = {n: [] for n in names}
-    prefill_ms = []
-    for ev in evs:
-        for i, n in enumerate(names):
-            dur[n].append(ev[i].elapsed_time(ev[i + 1]))
-        prefill_ms.append(ev[0].elapsed_time(ev[3]))
+    # Per-kernel characterisation after the timed steps: the prefill's three
+    # kernels launched one at a time over all chunks (the phase entry point),
+    # so each kernel's own duration is measured on the launch stream.
+    for _ in range(args.warmup):
+        for ph in range(3):
+            pre.run_phase(ph)
+    torch.cuda.synchronize()
+    pevs = [_events(torch, 4) for _ in range(args.steps)]
+    for s in range(args.steps):
+        pevs[s][0].record()
+        for ph in range(3):
+            pre.run_phase(ph)
+            pevs[s][1 + ph].record()
+    torch.cuda.synchronize()
+
+    names = ["chunk_map", "intra", "carry"]
+    dur = {n: [ev[i].elapsed_time(ev[i + 1]) for ev in pevs] for i, n in enumerate(names)}
+    dur["decode"] = decode_ms
     mean = {n: float(np.mean(v)) for n, v in dur.items()}
     t_pre = float(np.mean(prefill_ms)) * 1e-3
     t_dec = mean["decode"] * 1e-3
@@ -309,6 +324,7 @@ def main():
                                f"fp32 states", "T": p.T, "H": p.H, "d": D, "chunk": C,
                    "decode_batch": cfg4.n_seqs},
         "decode_tokens_per_s": decode_tps,
+        "prefill_phases_us": sum(mean[n] for n in names) * 1e3,
         "roofline": roofline,
         "prefill_path": prefill_path,
         "kernels": kernels,
