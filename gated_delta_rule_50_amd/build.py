@@ -20,7 +20,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libkda.so"
 BUILD = ROOT / "_build"
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_recurrent.hip"]
 
 
 def hipcc() -> str:

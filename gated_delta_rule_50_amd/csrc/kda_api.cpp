@@ -17,6 +17,11 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, const void* q, const void*
                             int32_t* status, int32_t* chunk_offset, uint8_t* inter,
                             hipStream_t stream);
 size_t inter_block_bytes(bool bf16_io);
+hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, const void* q,
+                                const void* k, const void* v, const float* log_alpha,
+                                const float* beta, const void* h0, const int32_t* cu,
+                                int64_t seq_len, int64_t T, int32_t H, int64_t pairs,
+                                void* o, void* h_final, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -167,6 +172,45 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
   const hipError_t err = kda::launch_decode_step(io == KDA_IO_BF16, q, k, v, log_alpha,
                                                  beta, S_inout, o, pairs,
                                                  static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, const void* h0,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                             int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io,
+                             kda_state_dtype state_dtype, uint32_t flags, void* o,
+                             void* h_final, void* stream) {
+  const int64_t T = total_tokens;
+  if (T < 0 || n_seqs < 0 || heads < 1) return KDA_ERR_SHAPE;
+  if (dk != kDim || dv != kDim || !valid_io(io)) return KDA_ERR_UNSUPPORTED;
+  if (state_dtype != KDA_STATE_F32 && state_dtype != KDA_STATE_BF16) return KDA_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)KDA_FLAG_QK_L2NORM) return KDA_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return T == 0 ? KDA_OK : KDA_ERR_SHAPE;
+  if (cu_seqlens == nullptr && T % n_seqs != 0) return KDA_ERR_SHAPE;
+  if (cu_seqlens != nullptr && T > INT32_MAX) return KDA_ERR_SHAPE;
+  const int64_t pairs = (int64_t)n_seqs * heads;
+  if (pairs > ((int64_t)1 << 29)) return KDA_ERR_SHAPE;  // grid of 4 waves per pair
+  if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
+
+  const int64_t th = T * heads;
+  const int64_t eb = io_bytes(io);
+  const Range rq(q, th * kDim * eb), rk(k, th * kDim * eb), rv(v, th * kDim * eb);
+  const Range rla(log_alpha, th * kDim * 4), rb(beta, th * 4);
+  const Range ro(o, th * kDim * eb);
+  const int64_t state_bytes = pairs * kDim * kDim * (state_dtype == KDA_STATE_BF16 ? 2 : 4);
+  const Range rh0(h0, state_bytes), rhf(h_final, state_bytes);
+  const Range rcu(cu_seqlens, 4 * ((int64_t)n_seqs + 1));
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rh0, &rcu, &rhf})
+    if (overlap(ro, *in)) return KDA_ERR_ALIAS;
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rcu})
+    if (overlap(rhf, *in)) return KDA_ERR_ALIAS;
+  if (overlap(rhf, rh0) && rhf.lo != rh0.lo) return KDA_ERR_ALIAS;
+
+  const hipError_t err = kda::launch_recurrent_fwd(
+      io == KDA_IO_BF16, state_dtype == KDA_STATE_BF16, (flags & KDA_FLAG_QK_L2NORM) != 0, q,
+      k, v, log_alpha, beta, h0, cu_seqlens, cu_seqlens ? 0 : T / n_seqs, T, heads, pairs, o,
+      h_final, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -1,0 +1,290 @@
+// Fused multi-token recurrent forward for gfx950.
+//
+// Runs the recurrence token by token (the review's "Online Learning
+// Interpretation" form of Eq. 1, "Kimi Linear: An Expressive, Efficient
+// Attention Architecture", paper-graph-ui review):
+//   S~ = Diag(alpha_t) S,  e = S~^T k_t,  S <- S~ + beta_t k_t (v_t - e)^T,
+//   o_t = S^T q_t = S~^T q_t + beta_t (q_t . k_t) (v_t - e)
+// over every token of a sequence with the state held in registers: the state
+// is read from HBM once before the first token and written once after the
+// last, so a call over L tokens moves the state's bytes once, not L times.
+// This is the path the review's "FLOPs Accounting and Inference Strategy"
+// section gives short inputs (the recurrent kernel for generation); the
+// serving note of the "L2 Deep Distill" page routes q_len <= 64 to it.
+//
+// Optional pieces (both from the pages' serving notes):
+//  * q and k normalised to unit L2 norm inside the kernel (q <- q / ||q||,
+//    with ||x|| = sqrt(sum x^2 + 1e-6)), as the pages fuse it into the
+//    operator;
+//  * a bfloat16 state in HBM (1 MB per layer at 32 heads), widened to fp32 in
+//    registers and rounded to nearest even once when written back.
+//
+// Layout: one wave (one 64-lane workgroup) per (sequence, head, 32-column
+// slice of the value dimension). Lane l owns value columns
+// 32 w + 4 (l % 8) .. +3 and key rows 16 (l / 8) .. +15 of that slice, 64
+// fp32 state values. Both column reductions of a token (e and S~^T q) are
+// sums over the eight lanes that share a column quad (lane bits 3..5), done
+// with cross-lane moves inside the wave, so a token needs no workgroup
+// barrier. The per-token vectors (alpha k, alpha q, alpha, k) go through a
+// wave-private LDS row so each lane can read its 16 rows with four 16-byte
+// reads.
+#include "kda_device.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kSliceCols = 32;                 // value columns per wave
+constexpr int kSlices = kD / kSliceCols;       // waves per (sequence, head)
+constexpr int kRowPitch = 20;                  // LDS floats per 16-row group (bank spread)
+constexpr float kL2NormEps = 1e-6f;
+
+// Sum of x over lanes l and l ^ 8 (DPP rotate by 8 inside each 16-lane row).
+__device__ __forceinline__ float sum_xor8(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf,
+                                                        false));
+}
+// Sum over lanes l and (l +- 4) mod 16 inside a row (DPP rotate by 4).
+__device__ __forceinline__ float sum_ror4(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf,
+                                                        false));
+}
+// Sum over lanes l and l ^ 1, l and l ^ 2 (DPP quad permutations).
+__device__ __forceinline__ float sum_xor1(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf,
+                                                        false));
+}
+__device__ __forceinline__ float sum_xor2(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf,
+                                                        false));
+}
+// Sum over lanes l and l ^ 16: permlane16_swap with both operands x gives
+// each lane x from its own row and from the partner row.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over lanes l and l ^ 32 (permlane32_swap, same construction).
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over the whole wave, left in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+  return sum_xor32(sum_xor16(sum_xor1(sum_xor2(sum_ror4(sum_xor8(x))))));
+}
+// Sum over the eight lanes sharing lane bits 0..2 (l, l ^ 8, ..., l ^ 56).
+__device__ __forceinline__ float group_sum8(float x) {
+  return sum_xor32(sum_xor16(sum_xor8(x)));
+}
+
+// Two consecutive I/O elements kept raw until used.
+template <class IO> struct Raw2;
+template <> struct Raw2<float> {
+  typedef float __attribute__((ext_vector_type(2))) T;
+};
+template <> struct Raw2<bf16> {
+  typedef bf16 __attribute__((ext_vector_type(2))) T;
+};
+template <class IO> struct Raw4;
+template <> struct Raw4<float> { typedef floatx4 T; };
+template <> struct Raw4<bf16> { typedef bf16x4 T; };
+
+// State storage: four consecutive columns of one row.
+__device__ __forceinline__ float4 load_state4(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ float4 load_state4(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return float4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ void store_state4(float* p, float4 x) {
+  *reinterpret_cast<float4*>(p) = x;
+}
+__device__ __forceinline__ void store_state4(bf16* p, float4 x) {
+  bf16x4 v;
+  v[0] = (bf16)x.x; v[1] = (bf16)x.y; v[2] = (bf16)x.z; v[3] = (bf16)x.w;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+
+// Per-token inputs of one lane: channels 2 l, 2 l + 1 of q, k, log alpha;
+// the lane's four value columns of v; beta.
+template <class IO>
+struct TokenIn {
+  typename Raw2<IO>::T q, k;
+  float2 la;
+  typename Raw4<IO>::T v;
+  float b;
+};
+
+template <class IO>
+__device__ __forceinline__ void fetch_token(TokenIn<IO>& x, const IO* q, const IO* k,
+                                            const IO* v, const float* log_alpha,
+                                            const float* beta, int64_t row, int lane,
+                                            int col0) {
+  const int64_t base = row * kD;
+  x.q = *reinterpret_cast<const typename Raw2<IO>::T*>(q + base + 2 * lane);
+  x.k = *reinterpret_cast<const typename Raw2<IO>::T*>(k + base + 2 * lane);
+  x.la = *reinterpret_cast<const float2*>(log_alpha + base + 2 * lane);
+  x.v = *reinterpret_cast<const typename Raw4<IO>::T*>(v + base + col0);
+  x.b = beta[row];
+}
+
+}  // namespace
+
+template <class IO, class ST, bool kNorm>
+__global__ __launch_bounds__(64) void recurrent_fwd_kernel(
+    const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta, const ST* h0,
+    const int32_t* __restrict__ cu, int64_t seq_len, int64_t T, int32_t H, int64_t pairs,
+    IO* __restrict__ o, ST* h_final) {
+  // Block b runs on XCD b % 8 (round-robin dispatch); the four slices of a
+  // (sequence, head) pair get blocks on one XCD so the token vectors they
+  // all read come from that XCD's L2.
+  const int bid = blockIdx.x;
+  const int rest = bid >> 3;
+  const int w = rest & (kSlices - 1);
+  const int64_t p = (int64_t)(rest >> 2) * 8 + (bid & 7);
+  if (p >= pairs) return;
+  const int64_t n = p / H;
+  const int h = (int)(p - n * H);
+
+  int64_t bos, eos;
+  if (cu != nullptr) {
+    bos = min<int64_t>(max<int64_t>(cu[n], 0), T);
+    eos = min<int64_t>(max<int64_t>(cu[n + 1], bos), T);
+  } else {
+    bos = n * seq_len;
+    eos = bos + seq_len;
+  }
+
+  const int lane = threadIdx.x;
+  const int jq = lane & 7;        // column quad inside the slice
+  const int rl = lane >> 3;       // rows 16 rl .. 16 rl + 15
+  const int col0 = kSliceCols * w + 4 * jq;
+
+  // Wave-private token vectors, 16-row groups at a padded pitch.
+  __shared__ __align__(16) float s_ka[8 * kRowPitch], s_qa[8 * kRowPitch];
+  __shared__ __align__(16) float s_a[8 * kRowPitch], s_k[8 * kRowPitch];
+
+  float4 s[16];
+  const int64_t sbase = p * (int64_t)(kD * kD) + (int64_t)(16 * rl) * kD + col0;
+  if (h0 != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = load_state4(h0 + sbase + i * kD);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int widx = (lane >> 3) * kRowPitch + 2 * (lane & 7);  // channels 2 l, 2 l + 1
+  TokenIn<IO> nxt;
+  if (bos < eos) fetch_token(nxt, q, k, v, log_alpha, beta, bos * H + h, lane, col0);
+
+  for (int64_t t = bos; t < eos; ++t) {
+    const TokenIn<IO> cur = nxt;
+    // Next token's inputs (the last token fetches itself again: the load is
+    // unconditional so the counter waits stay exact).
+    const int64_t tn = t + 1 < eos ? t + 1 : t;
+    fetch_token(nxt, q, k, v, log_alpha, beta, tn * H + h, lane, col0);
+
+    float q0 = (float)cur.q[0], q1 = (float)cur.q[1];
+    float k0 = (float)cur.k[0], k1 = (float)cur.k[1];
+    const float a0 = exp_f(cur.la.x), a1 = exp_f(cur.la.y);
+    float qk = wave_sum(q0 * k0 + q1 * k1);
+    if constexpr (kNorm) {
+      const float kk = wave_sum(k0 * k0 + k1 * k1);
+      const float qq = wave_sum(q0 * q0 + q1 * q1);
+      const float rk = 1.f / sqrtf(kk + kL2NormEps), rq = 1.f / sqrtf(qq + kL2NormEps);
+      k0 *= rk; k1 *= rk; q0 *= rq; q1 *= rq;
+      qk *= rk * rq;
+    }
+    __syncthreads();  // the previous token's reads of the rows are done
+    *reinterpret_cast<float2*>(s_ka + widx) = float2{a0 * k0, a1 * k1};
+    *reinterpret_cast<float2*>(s_qa + widx) = float2{a0 * q0, a1 * q1};
+    *reinterpret_cast<float2*>(s_a + widx) = float2{a0, a1};
+    *reinterpret_cast<float2*>(s_k + widx) = float2{k0, k1};
+    __syncthreads();
+
+    // Partial column sums over this lane's 16 rows: e = S~^T k, pr = S~^T q.
+    float4 pe = {0.f, 0.f, 0.f, 0.f}, pr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float4 ka = *reinterpret_cast<const float4*>(s_ka + rl * kRowPitch + 4 * m);
+      const float4 qa = *reinterpret_cast<const float4*>(s_qa + rl * kRowPitch + 4 * m);
+      const float kav[4] = {ka.x, ka.y, ka.z, ka.w};
+      const float qav[4] = {qa.x, qa.y, qa.z, qa.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 x = s[4 * m + r];
+        pe.x += kav[r] * x.x; pe.y += kav[r] * x.y; pe.z += kav[r] * x.z; pe.w += kav[r] * x.w;
+        pr.x += qav[r] * x.x; pr.y += qav[r] * x.y; pr.z += qav[r] * x.z; pr.w += qav[r] * x.w;
+      }
+    }
+    pe.x = group_sum8(pe.x); pe.y = group_sum8(pe.y);
+    pe.z = group_sum8(pe.z); pe.w = group_sum8(pe.w);
+    // d = beta (v - e): the correction written along k.
+    float4 d;
+    d.x = cur.b * ((float)cur.v[0] - pe.x);
+    d.y = cur.b * ((float)cur.v[1] - pe.y);
+    d.z = cur.b * ((float)cur.v[2] - pe.z);
+    d.w = cur.b * ((float)cur.v[3] - pe.w);
+
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float4 a = *reinterpret_cast<const float4*>(s_a + rl * kRowPitch + 4 * m);
+      const float4 kv = *reinterpret_cast<const float4*>(s_k + rl * kRowPitch + 4 * m);
+      const float av[4] = {a.x, a.y, a.z, a.w};
+      const float kvv[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float4& x = s[4 * m + r];
+        x.x = av[r] * x.x + kvv[r] * d.x;
+        x.y = av[r] * x.y + kvv[r] * d.y;
+        x.z = av[r] * x.z + kvv[r] * d.z;
+        x.w = av[r] * x.w + kvv[r] * d.w;
+      }
+    }
+
+    pr.x = group_sum8(pr.x); pr.y = group_sum8(pr.y);
+    pr.z = group_sum8(pr.z); pr.w = group_sum8(pr.w);
+    if (rl == 0) {
+      floatx4 y = {pr.x + qk * d.x, pr.y + qk * d.y, pr.z + qk * d.z, pr.w + qk * d.w};
+      store4_io(o + (t * H + h) * kD + col0, y);
+    }
+  }
+
+  if (h_final != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) store_state4(h_final + sbase + i * kD, s[i]);
+  }
+}
+
+hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, const void* q,
+                                const void* k, const void* v, const float* log_alpha,
+                                const float* beta, const void* h0, const int32_t* cu,
+                                int64_t seq_len, int64_t T, int32_t H, int64_t pairs,
+                                void* o, void* h_final, hipStream_t stream) {
+  if (pairs == 0) return hipSuccess;
+  const int64_t blocks = (pairs + 7) / 8 * 8 * kSlices;
+  dim3 grid((unsigned)blocks), block(64);
+#define KDA_REC_LAUNCH(IO, ST, NORM)                                                         \
+  recurrent_fwd_kernel<IO, ST, NORM><<<grid, block, 0, stream>>>(                            \
+      (const IO*)q, (const IO*)k, (const IO*)v, log_alpha, beta, (const ST*)h0, cu, seq_len, \
+      T, H, pairs, (IO*)o, (ST*)h_final)
+#define KDA_REC_NORM(IO, ST)          \
+  if (l2norm) KDA_REC_LAUNCH(IO, ST, true); \
+  else KDA_REC_LAUNCH(IO, ST, false)
+  if (bf16_io) {
+    if (bf16_state) { KDA_REC_NORM(bf16, bf16); } else { KDA_REC_NORM(bf16, float); }
+  } else {
+    if (bf16_state) { KDA_REC_NORM(float, bf16); } else { KDA_REC_NORM(float, float); }
+  }
+#undef KDA_REC_NORM
+#undef KDA_REC_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace kda

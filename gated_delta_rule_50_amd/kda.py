@@ -16,11 +16,13 @@ LIB_PATH = Path(__file__).resolve().parent / "libkda.so"
 KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_UNSUPPORTED = 0, 1, 2, 3
 KDA_ERR_WORKSPACE, KDA_ERR_ALIAS, KDA_ERR_HIP = 4, 5, 6
 KDA_IO_F32, KDA_IO_BF16 = 0, 1
+KDA_STATE_F32, KDA_STATE_BF16 = 0, 1
+KDA_FLAG_QK_L2NORM = 1
 CHUNK = 64
 HEAD_DIM = 128
 
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_phase",
-           "kda_decode_step", "kda_status_string", "kda_version")
+           "kda_decode_step", "kda_recurrent_fwd", "kda_status_string", "kda_version")
 
 _LIB = None
 
@@ -50,6 +52,10 @@ def lib() -> ctypes.CDLL:
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                       ctypes.c_int, vp, vp]
         L.kda_decode_step.restype = ctypes.c_int
+        L.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp, vp,
+                                        vp]
+        L.kda_recurrent_fwd.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.restype = i32
@@ -67,6 +73,14 @@ def _io(dtype: torch.dtype) -> int:
     if dtype == torch.float32:
         return KDA_IO_F32
     raise TypeError(f"q/k/v must be bfloat16 or float32, got {dtype}")
+
+
+def _state(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return KDA_STATE_BF16
+    if dtype == torch.float32:
+        return KDA_STATE_F32
+    raise TypeError(f"states must be bfloat16 or float32, got {dtype}")
 
 
 def _ptr(t):
@@ -188,3 +202,60 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     if st != KDA_OK:
         raise KDAError(st, "kda_decode_step")
     return o
+
+
+class Recurrent:
+    """Device buffers of one fused recurrent call (kda_recurrent_fwd).
+
+    Same tensors as Prefill, without a workspace. With cu_seqlens None the
+    batch holds n_seqs sequences of T / n_seqs tokens each ([N, L, H, 128]
+    flattened to [T, H, 128]). h0 / h_final are [N, H, 128, 128] in
+    state_dtype (float32 or bfloat16); h_final may be h0 (in-place update).
+    qk_l2norm normalises q and k inside the kernel.
+    """
+
+    def __init__(self, q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, n_seqs=None,
+                 state_dtype=torch.float32, qk_l2norm=False, o=None, h_final=None,
+                 want_final=True):
+        dev = k.device
+        self.io = _io(k.dtype)
+        self.T, self.H = int(k.shape[0]), int(k.shape[1])
+        if cu_seqlens is not None:
+            self.N = int(cu_seqlens.shape[0]) - 1
+        else:
+            self.N = 1 if n_seqs is None else int(n_seqs)
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _check(t, n, k.dtype, dev)
+        _check(log_alpha, "log_alpha", torch.float32, dev)
+        _check(beta, "beta", torch.float32, dev)
+        _check(h0, "h0", state_dtype, dev)
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if o is None:
+            o = torch.empty((self.T, self.H, v.shape[2]), dtype=k.dtype, device=dev)
+        _check(o, "o", k.dtype, dev)
+        if h_final is None and want_final:
+            h_final = torch.empty((self.N, self.H, k.shape[2], v.shape[2]), dtype=state_dtype,
+                                  device=dev)
+        _check(h_final, "h_final", state_dtype, dev)
+        self.device = dev
+        self.o, self.h_final = o, h_final
+        self._keep = (q, k, v, log_alpha, beta, h0, cu_seqlens)
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                      _ptr(cu_seqlens), self.N, self.T, self.H, int(k.shape[2]),
+                      int(v.shape[2]), self.io, _state(state_dtype),
+                      KDA_FLAG_QK_L2NORM if qk_l2norm else 0, _ptr(o), _ptr(h_final))
+
+    def run(self, stream=None):
+        st = lib().kda_recurrent_fwd(*self._args, _stream(stream, self.device))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_recurrent_fwd")
+        return self.o, self.h_final
+
+
+def recurrent_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, n_seqs=None,
+                  state_dtype=torch.float32, qk_l2norm=False, o=None, h_final=None,
+                  want_final=True, stream=None):
+    """Fused token-by-token forward (see Recurrent). Returns (o, h_final or None)."""
+    return Recurrent(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs=n_seqs,
+                     state_dtype=state_dtype, qk_l2norm=qk_l2norm, o=o, h_final=h_final,
+                     want_final=want_final).run(stream)

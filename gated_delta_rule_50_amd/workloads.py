@@ -12,7 +12,9 @@ alpha in (0, 1] per channel, supplied here as its natural log.
 Recipe (numpy PCG64, ``default_rng(seed)``), in draw order:
   lengths (packed batches only) -> q -> k -> v -> beta -> log_alpha -> h0.
   q, k  ~ N(0,1) float32, L2-normalised per (token, head) in fp64, then
-        rounded to the I/O dtype (bf16: round-to-nearest-even).
+        rounded to the I/O dtype (bf16: round-to-nearest-even). With
+        qk="raw" the normalisation is skipped (inputs for the operator's
+        in-kernel L2Norm); the draws are the same.
   v     ~ N(0,1) float32, rounded to the I/O dtype.
   beta  = sigmoid(z), z ~ N(0,1), float32.
   log_alpha = log(sigmoid(z)) / 16 = -softplus(-z)/16, z ~ N(0,1), computed
@@ -59,9 +61,11 @@ def _normal_f32(rng, shape):
     return out
 
 
-def _unit_rows(rng, shape, io):
+def _unit_rows(rng, shape, io, normalise=True):
     """N(0,1) rows normalised along the last axis in fp64, rounded to io."""
     x = _normal_f32(rng, shape)
+    if not normalise:
+        return _to_io(x, io)
     flat = x.reshape(-1, shape[-1])
     for s in range(0, flat.shape[0], _BLOCK):
         e = min(s + _BLOCK, flat.shape[0])
@@ -119,15 +123,16 @@ class Prefill:
 
 
 def make_prefill(lengths, H, seed, io="bf16", decay="mild", h0_std=None,
-                 dk=D, dv=D) -> Prefill:
+                 dk=D, dv=D, qk="unit") -> Prefill:
     """Draws one packed batch with sequences of the given lengths."""
     rng = np.random.default_rng(seed)
     lengths = np.asarray(lengths, dtype=np.int64)
     T = int(lengths.sum())
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
-    q = _unit_rows(rng, (T, H, dk), io)
-    k = _unit_rows(rng, (T, H, dk), io)
+    unit = {"unit": True, "raw": False}[qk]
+    q = _unit_rows(rng, (T, H, dk), io, unit)
+    k = _unit_rows(rng, (T, H, dk), io, unit)
     v = _to_io(_normal_f32(rng, (T, H, dv)), io)
     beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
     la = _log_alpha(rng, T, H, dk, decay)
@@ -154,11 +159,12 @@ def make_decode_state(N, H, seed, std=0.02, dk=D, dv=D) -> np.ndarray:
     return (_normal_f32(rng, (N, H, dk, dv)) * np.float32(std)).astype(np.float32)
 
 
-def make_decode_step(N, H, seed, step, io="bf16", dk=D, dv=D) -> DecodeStep:
+def make_decode_step(N, H, seed, step, io="bf16", dk=D, dv=D, qk="unit") -> DecodeStep:
     """Fresh token inputs for decode step ``step`` (rng seeded [seed, step])."""
     rng = np.random.default_rng([seed, step])
-    q = _unit_rows(rng, (N, H, dk), io)
-    k = _unit_rows(rng, (N, H, dk), io)
+    unit = {"unit": True, "raw": False}[qk]
+    q = _unit_rows(rng, (N, H, dk), io, unit)
+    k = _unit_rows(rng, (N, H, dk), io, unit)
     v = _to_io(_normal_f32(rng, (N, H, dv)), io)
     beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((N, H))))).astype(np.float32)
     la = _log_alpha(rng, N, H, dk, "mild")

@@ -32,12 +32,13 @@
  *      log_alpha  [T, H, d_k]   float32: natural log of the per-channel decay
  *                               alpha_t in (0, 1], i.e. finite and <= 0
  *      beta       [T, H]        float32
- *      states     [N, H, d_k, d_v] float32, S[c][j]: row c = key channel,
+ *      states     [N, H, d_k, d_v] float32 (kda_recurrent_fwd also takes
+ *                               bfloat16), S[c][j]: row c = key channel,
  *                               column j = value channel
  *    For decode, T is replaced by the batch N (one token per sequence).
  *  - No query scaling is applied (o_t = S_t^T q_t as printed), q and k are
- *    used as given (callers L2-normalise them), and bf16 outputs are rounded
- *    to nearest even.
+ *    used as given (callers L2-normalise them; kda_recurrent_fwd can do it
+ *    in the kernel), and bf16 outputs are rounded to nearest even.
  *  - Unchecked preconditions (the device cannot report them synchronously):
  *    finite inputs, log_alpha <= 0, cu_seqlens non-decreasing with
  *    cu_seqlens[0] = 0 and cu_seqlens[N] = T. Violations give unspecified
@@ -198,6 +199,67 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            float *S_inout, int32_t n_seqs, int32_t heads,
                            int32_t dk, int32_t dv, kda_io_dtype io, void *o,
                            void *stream);
+
+typedef enum {
+  KDA_STATE_F32 = 0,  /* recurrent states are float32 */
+  KDA_STATE_BF16 = 1  /* recurrent states are bfloat16 (rounded to nearest even) */
+} kda_state_dtype;
+
+/* kda_recurrent_fwd flag bits */
+#define KDA_FLAG_QK_L2NORM 1u /* normalise q_t and k_t to unit L2 norm in the kernel */
+
+/*
+ * kda_recurrent_fwd - fused token-by-token forward over a packed batch.
+ *
+ * Computes exactly what kda_chunk_fwd computes (outputs o_t of every token and
+ * the state after each sequence's last token, from h0 or zeros), but runs the
+ * recurrence one token at a time with each state held on chip for the whole
+ * sequence: the state is read once and written once per call, whatever the
+ * sequence length. This is the recurrent kernel the review's "FLOPs
+ * Accounting and Inference Strategy" section gives generation, and the one
+ * the "L2 Deep Distill" page's serving note selects for inputs of at most 64
+ * new tokens per sequence (multi-token decode, speculative verification).
+ * Any length works; beyond a few dozen tokens kda_chunk_fwd is faster.
+ * Per token, with alpha = exp(log_alpha):
+ *   S~ = Diag(alpha) S,  e = S~^T k,  S <- S~ + beta k (v - e)^T,  o = S^T q.
+ *
+ *   q, k, v, o, log_alpha, beta  layouts as for kda_chunk_fwd ([T, H, 128],
+ *                   beta [T, H]); io selects float32 or bfloat16 q, k, v, o
+ *   h0, h_final     [N, H, 128, 128] in state_dtype; h0 NULL means zero
+ *                   states, h_final NULL skips the write; h_final may be the
+ *                   same pointer as h0 (in-place update, the decode case) but
+ *                   must not partially overlap it
+ *   cu_seqlens      device int32 [N + 1], or NULL: then every sequence has
+ *                   total_tokens / n_seqs tokens (q is [N, L, H, 128]) and
+ *                   total_tokens must be a multiple of n_seqs
+ *   state_dtype     KDA_STATE_F32, or KDA_STATE_BF16: states are widened to
+ *                   float32 on chip, so a call over L tokens rounds the state
+ *                   once, not L times (the pages' serving note keeps the
+ *                   state in BF16, 1 MB per layer)
+ *   flags           0 or KDA_FLAG_QK_L2NORM: q_t, k_t are replaced by
+ *                   x / sqrt(sum_c x_c^2 + 1e-6) before use (the pages' L2Norm
+ *                   of q and k, fused into the operator); other bits are
+ *                   rejected
+ *   n_seqs = 0 (with total_tokens = 0) does nothing. A sequence of length 0
+ *   copies h0 (or zeros) to h_final.
+ *   Errors: KDA_ERR_NULL (q, k, v, log_alpha, beta or o NULL when T > 0),
+ *   KDA_ERR_SHAPE (negative sizes, heads < 1, n_seqs = 0 with T > 0,
+ *   T not a multiple of n_seqs without cu_seqlens, T > INT32_MAX with
+ *   cu_seqlens, more than 2^29 (sequence, head) pairs),
+ *   KDA_ERR_UNSUPPORTED (d_k, d_v != 128, unknown dtype or flag bit),
+ *   KDA_ERR_ALIAS (o overlapping an input or h_final; h_final overlapping q,
+ *   k, v, log_alpha, beta, cu_seqlens; h_final partially overlapping h0),
+ *   KDA_ERR_HIP. With cu_seqlens, values outside [0, T] or decreasing are
+ *   clamped (unspecified results, no out-of-bounds access).
+ */
+kda_status kda_recurrent_fwd(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta,
+                             const void *h0, const int32_t *cu_seqlens,
+                             int32_t n_seqs, int64_t total_tokens,
+                             int32_t heads, int32_t dk, int32_t dv,
+                             kda_io_dtype io, kda_state_dtype state_dtype,
+                             uint32_t flags, void *o, void *h_final,
+                             void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *kda_status_string(kda_status s);

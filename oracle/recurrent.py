@@ -81,6 +81,23 @@ def forward(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, threads=None):
     return o, h_final
 
 
+L2NORM_EPS = 1e-6
+
+
+def l2norm(x, eps=L2NORM_EPS):
+    """Scales each vector along the last axis to unit Euclidean length,
+    x / sqrt(sum_c x_c^2 + eps), in fp64.
+
+    The pages apply L2Norm to q and k ("Kimi Linear" review, section
+    "Neural Parameterization": q and k are normalised to unit length so the
+    rank-1 Householder correction stays well behaved; the "L2 Deep Distill"
+    page fuses it into the operator). The pages give no epsilon; eps = 1e-6
+    keeps a zero vector at zero and changes a unit-scale vector by ~1e-7.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
 def decode_step(q, k, v, log_alpha, beta, S, threads=None):
     """One recurrent step for N sequences x H heads (one token each).
 

@@ -34,6 +34,9 @@ def lib():
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                   vp, vp]
     L.kda_decode_step.restype = ctypes.c_int
+    L.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp, vp, vp]
+    L.kda_recurrent_fwd.restype = ctypes.c_int
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_version.restype = i32
@@ -49,7 +52,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
-                     "kda_status_string"):
+                     "kda_recurrent_fwd", "kda_status_string"):
         assert required in names
 
 
@@ -191,6 +194,49 @@ def test_decode_argument_errors(lib):
 def test_decode_empty_batch_is_a_noop(lib):
     # returns before any HIP call
     assert call_decode(lib, N=0, q=None, S=None, o=None) == OK
+
+
+# ---------------------------------------------------- recurrent validation
+def call_recurrent(lib, **over):
+    a = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, la=BASE + 3 * MB, beta=BASE + 4 * MB,
+             h0=BASE + 64 * MB, cu=None, N=4, T=8, H=2, dk=128, dv=128, io=BF16, st=F32,
+             flags=0, o=BASE + 5 * MB, hf=BASE + 64 * MB, stream=None)
+    a.update(over)
+    return lib.kda_recurrent_fwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["h0"], a["cu"],
+                                 a["N"], a["T"], a["H"], a["dk"], a["dv"], a["io"], a["st"],
+                                 a["flags"], a["o"], a["hf"], a["stream"])
+
+
+def test_recurrent_argument_errors(lib):
+    assert call_recurrent(lib, T=-1) == SHAPE
+    assert call_recurrent(lib, N=-1) == SHAPE
+    assert call_recurrent(lib, H=0) == SHAPE
+    assert call_recurrent(lib, T=9) == SHAPE                    # 9 tokens over 4 sequences
+    assert call_recurrent(lib, N=0) == SHAPE                    # tokens but no sequence
+    assert call_recurrent(lib, N=1 << 28, T=1 << 28, H=4) == SHAPE   # grid limit
+    assert call_recurrent(lib, cu=BASE + 6 * MB, T=1 << 31) == SHAPE
+    assert call_recurrent(lib, dk=64) == UNSUP
+    assert call_recurrent(lib, io=2) == UNSUP
+    assert call_recurrent(lib, st=2) == UNSUP
+    assert call_recurrent(lib, flags=2) == UNSUP
+    assert call_recurrent(lib, v=None) == NULL
+    assert call_recurrent(lib, o=None) == NULL
+    assert call_recurrent(lib, o=BASE + 2 * MB + 512) == ALIAS      # o over v
+    assert call_recurrent(lib, o=BASE + 64 * MB + 4096) == ALIAS    # o inside the state
+    assert call_recurrent(lib, hf=BASE + 3 * MB) == ALIAS           # h_final over log_alpha
+    assert call_recurrent(lib, hf=BASE + 64 * MB + 2048) == ALIAS   # partial overlap of h0
+
+
+def test_recurrent_state_size_follows_state_dtype(lib):
+    # 4 x 2 states are 512 KiB in fp32 and 256 KiB in bf16; o starting just
+    # before either end overlaps (calls that pass every check would launch, so
+    # only rejected calls appear here)
+    assert call_recurrent(lib, st=F32, hf=None, o=BASE + 64 * MB + 512 * 1024 - 8) == ALIAS
+    assert call_recurrent(lib, st=BF16, hf=None, o=BASE + 64 * MB + 256 * 1024 - 8) == ALIAS
+
+
+def test_recurrent_empty_batch_is_a_noop(lib):
+    assert call_recurrent(lib, N=0, T=0, q=None, h0=None, o=None, hf=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

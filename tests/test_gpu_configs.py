@@ -79,3 +79,53 @@ def test_config4_decode_64_steps():
         assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1], (step, eo, es)
         assert torch.isfinite(o.float()).all()
     print(f"decode worst over 64 steps: o {worst_o:.3e}, state {worst_s:.3e}")
+
+
+@pytest.mark.parametrize("L", [4, 64])
+def test_recurrent_multi_token_full_size(L):
+    """kda_recurrent_fwd at the benchmark's multi-token shape: 256 sequences x
+    32 heads x L new tokens, bf16 I/O, fp32 states ~N(0, 0.02); every 32nd
+    sequence (all heads, all tokens) against the oracle."""
+    N, H = 256, 32
+    p = workloads.make_prefill([L] * N, H, seed=2000 + L, io="bf16", h0_std=0.02)
+    bf = torch.bfloat16
+    o, hf = kda.recurrent_fwd(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha),
+                              dev(p.beta), dev(p.h0), n_seqs=N)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(hf).all()
+    sample = np.arange(0, N, 32)
+    rows = (sample[:, None] * L + np.arange(L)[None, :]).ravel()
+    ro, rh = recurrent.forward(p.q[rows], p.k[rows], p.v[rows], p.log_alpha[rows],
+                               p.beta[rows], p.h0[sample],
+                               np.arange(len(sample) + 1) * L)
+    eo = rel_max_err(host(o[rows]), ro)
+    es = rel_fro_err(hf[sample].cpu().numpy().astype(np.float64), rh)
+    print(f"L={L}: o err {eo:.3e}, state err {es:.3e}")
+    assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]
+
+
+def test_config4_decode_64_steps_bf16_state():
+    """Config 4's 64 decode steps with the state stored in bf16 (rounded after
+    every step) through kda_recurrent_fwd, against the oracle's fp64 state:
+    the accumulated rounding must stay within the 1e-2 state tolerance."""
+    cfg = workloads.config(4)
+    N, H = cfg.n_seqs, cfg.H
+    S0 = workloads.round_bf16(workloads.make_decode_state(N, H, cfg.seed))
+    S = dev(S0, torch.bfloat16)
+    sample = np.arange(0, N, 16)
+    ref = S0[sample].astype(np.float64)
+    bf = torch.bfloat16
+    worst_o = worst_s = 0.0
+    for step in range(cfg.steps):
+        d = workloads.make_decode_step(N, H, cfg.seed, step, io=cfg.io)
+        o, _ = kda.recurrent_fwd(dev(d.q, bf), dev(d.k, bf), dev(d.v, bf), dev(d.log_alpha),
+                                 dev(d.beta), S, n_seqs=N, state_dtype=torch.bfloat16,
+                                 h_final=S)
+        torch.cuda.synchronize()
+        ro, ref = recurrent.decode_step(d.q[sample], d.k[sample], d.v[sample],
+                                        d.log_alpha[sample], d.beta[sample], ref)
+        eo = rel_max_err(host(o[sample]), ro)
+        es = rel_fro_err(S[sample].float().cpu().numpy().astype(np.float64), ref)
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1], (step, eo, es)
+    print(f"bf16-state decode worst over 64 steps: o {worst_o:.3e}, state {worst_s:.3e}")

@@ -281,3 +281,38 @@ def test_decode_step_is_one_token_recurrence():
                                    b[n:n + 1], S[n:n + 1])
         assert np.array_equal(o[n], on[0])
         assert np.array_equal(S1[n], hn[0])
+
+
+# --------------------------------------------------------- L2 normalisation
+def test_l2norm_worked_examples():
+    """(3, 4) has length 5; a zero vector stays zero (the epsilon only guards
+    the division); each vector along the last axis is scaled on its own."""
+    x = np.array([[3.0, 4.0], [0.0, 0.0], [-1e-3, 0.0]])
+    y = recurrent.l2norm(x)
+    np.testing.assert_allclose(y[0], [0.6, 0.8], rtol=0, atol=1e-7)
+    assert np.all(y[1] == 0.0)
+    np.testing.assert_allclose(y[2], [-1e-3 / np.sqrt(1e-6 + 1e-6), 0.0], rtol=1e-14)
+
+
+def test_l2norm_unit_length_and_scale_invariance():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((40, 3, 128))
+    y = recurrent.l2norm(x)
+    n2 = np.sum(x * x, axis=-1)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.sqrt(n2 / (n2 + 1e-6)),
+                               rtol=1e-14)
+    np.testing.assert_allclose(recurrent.l2norm(7.5 * x), y, rtol=0, atol=1e-8)
+    # the direction is kept: y is a positive multiple of x
+    ratio = y / x
+    np.testing.assert_allclose(ratio, np.broadcast_to(ratio[..., :1], ratio.shape), rtol=1e-13)
+    assert np.all(ratio > 0)
+
+
+def test_l2norm_feeds_exact_recall():
+    """Keys normalised by l2norm (up to the epsilon) satisfy the exact-recall
+    property of the Householder step: with beta = 1, S_t^T k_t = v_t."""
+    q, k, v, la, b, S0 = _inputs(5, T=40, dk=16, dv=8, la_scale=2.0)
+    kn = recurrent.l2norm(5.0 * np.random.default_rng(5).standard_normal(k.shape))
+    b[:] = 1.0
+    o, _ = recurrent.forward(kn, kn, v, la, b, S0)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-5)
