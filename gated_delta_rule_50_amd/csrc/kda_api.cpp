@@ -10,7 +10,7 @@ namespace kda {
 hipError_t launch_decode_step(bool bf16_io, const void* q, const void* k, const void* v,
                               const float* log_alpha, const float* beta, float* S,
                               void* o, int64_t pairs, hipStream_t stream);
-hipError_t launch_chunk_fwd(int phases, bool bf16_io, const void* q, const void* k,
+hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q, const void* k,
                             const void* v, const float* log_alpha, const float* beta,
                             const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
                             int32_t H, int64_t n_slots, void* o, float* h_final,
@@ -22,6 +22,8 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
                                 const float* beta, const void* h0, const int32_t* cu,
                                 int64_t seq_len, int64_t T, int32_t H, int64_t pairs,
                                 void* o, void* h_final, hipStream_t stream);
+hipError_t launch_rmsnorm_gate(bool bf16_io, const void* o, const void* g, const float* w,
+                               float eps, int64_t rows, void* y, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -83,12 +85,13 @@ namespace {
 kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta, const float* h0,
                           const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
-                          int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io, void* o,
-                          float* h_final, void* workspace, size_t workspace_bytes_given,
-                          void* stream) {
+                          int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io,
+                          uint32_t flags, void* o, float* h_final, void* workspace,
+                          size_t workspace_bytes_given, void* stream) {
   const int64_t T = total_tokens;
   if (T < 0 || n_seqs < 1 || heads < 1) return KDA_ERR_SHAPE;
   if (dk != kDim || dv != kDim || !valid_io(io) || heads > 65535) return KDA_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)KDA_FLAG_QK_L2NORM) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens == nullptr && n_seqs != 1) return KDA_ERR_NULL;
   if (cu_seqlens != nullptr && T > INT32_MAX) return KDA_ERR_SHAPE;
   if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
@@ -119,7 +122,8 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
   int32_t* chunk_offset = reinterpret_cast<int32_t*>(ws + 256);
   uint8_t* inter = ws + inter_offset(n_seqs);
   const hipError_t err = kda::launch_chunk_fwd(
-      phases, io == KDA_IO_BF16, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, T, heads,
+      phases, io == KDA_IO_BF16, (flags & KDA_FLAG_QK_L2NORM) != 0, q, k, v, log_alpha, beta,
+      h0, cu_seqlens, n_seqs, T, heads,
       chunk_slots(n_seqs, T), o, h_final, status, chunk_offset, inter,
       static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -132,22 +136,23 @@ extern "C" {
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* log_alpha, const float* beta, const float* h0,
                          const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
-                         int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io, void* o,
-                         float* h_final, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io,
+                         uint32_t flags, void* o, float* h_final, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl(7, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens,
-                        heads, dk, dv, io, o, h_final, workspace, workspace_bytes, stream);
+                        heads, dk, dv, io, flags, o, h_final, workspace, workspace_bytes,
+                        stream);
 }
 
 kda_status kda_chunk_fwd_phase(int32_t phase, const void* q, const void* k, const void* v,
                                const float* log_alpha, const float* beta, const float* h0,
                                const int32_t* cu_seqlens, int32_t n_seqs,
                                int64_t total_tokens, int32_t heads, int32_t dk, int32_t dv,
-                               kda_io_dtype io, void* o, float* h_final, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               kda_io_dtype io, uint32_t flags, void* o, float* h_final,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   if (phase < 0 || phase > 2) return KDA_ERR_SHAPE;
   return chunk_fwd_impl(1 << phase, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs,
-                        total_tokens, heads, dk, dv, io, o, h_final, workspace,
+                        total_tokens, heads, dk, dv, io, flags, o, h_final, workspace,
                         workspace_bytes, stream);
 }
 
@@ -214,6 +219,22 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v,
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_rmsnorm_gate(const void* o, const void* gate, const float* weight, float eps,
+                            int64_t rows, int32_t dv, kda_io_dtype io, void* y, void* stream) {
+  if (rows < 0 || !(eps >= 0.f) || eps > 3.0e38f) return KDA_ERR_SHAPE;
+  if (dv != kDim || !valid_io(io)) return KDA_ERR_UNSUPPORTED;
+  if (rows == 0) return KDA_OK;
+  if (rows > (int64_t)UINT32_MAX * 16) return KDA_ERR_SHAPE;
+  if (!o || !gate || !y) return KDA_ERR_NULL;
+  const int64_t bytes = rows * kDim * io_bytes(io);
+  const Range ro(o, bytes), rg(gate, bytes), rw(weight, kDim * 4), ry(y, bytes);
+  if (overlap(ry, ro) && ry.lo != ro.lo) return KDA_ERR_ALIAS;
+  if (overlap(ry, rg) || overlap(ry, rw)) return KDA_ERR_ALIAS;
+  const hipError_t err = kda::launch_rmsnorm_gate(io == KDA_IO_BF16, o, gate, weight, eps, rows,
+                                                  y, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 const char* kda_status_string(kda_status s) {
   switch (s) {
     case KDA_OK: return "ok";
@@ -227,6 +248,6 @@ const char* kda_status_string(kda_status s) {
   return "unknown status";
 }
 
-int32_t kda_version(void) { return 100; }
+int32_t kda_version(void) { return 200; }
 
 }  // extern "C"

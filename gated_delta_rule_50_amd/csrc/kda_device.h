@@ -153,6 +153,24 @@ __device__ __forceinline__ void st16(float* p, const Frag16<float>& f) {
 }
 
 
+// Cross-lane sums inside a wave (results in every lane).
+// Sum over lanes l and l ^ 16: permlane16_swap with both operands x gives
+// each lane x from its own 16-lane row and from the partner row.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over lanes l and l ^ 32 (permlane32_swap, same construction).
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The pages' L2Norm of q and k: x / sqrt(sum_c x_c^2 + kL2NormEps).
+constexpr float kL2NormEps = 1e-6f;
+
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_f(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);

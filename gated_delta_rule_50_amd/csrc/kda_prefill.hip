@@ -138,7 +138,7 @@ __device__ __forceinline__ void lds_frag(const bf16* p, Frag<bf16>& f) {
 }
 __device__ __forceinline__ void lds_frag(const float* p, Frag<float>& f) { load8(p, f.v); }
 
-template <class E>
+template <class E, bool kNorm>
 __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
@@ -160,6 +160,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   constexpr int kTilesBytes = (4 * 16 + 12 + 4) * kTile * (int)sizeof(E);
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRowsBytes > kTilesBytes ? kRowsBytes : kTilesBytes];
   __shared__ __attribute__((aligned(16))) float sB[kC];
+  __shared__ float sRk[kNorm ? kC : 1], sRq[kNorm ? kC : 1];   // L2Norm row scales
   E* const sKf = reinterpret_cast<E*>(smem);
   float* const sF = reinterpret_cast<float*>(smem + 4 * 4 * kWave * 8 * sizeof(E));
   float* const sTot = sF + 4 * 5 * kD;
@@ -219,6 +220,26 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     const float x = beta[(tok0 + min(i, len - 1)) * H + h];
     bt = valid ? x : 0.f;
   }
+  // optional L2Norm of the q and k rows: the row's 128 channels sit in the
+  // four lanes r + 16 g; the scales are applied where the rows are first
+  // used (in fp32), and kept in LDS for the exact diagonal path.
+  float rk = 1.f, rq = 1.f;
+  if constexpr (kNorm) {
+    float kk = 0.f, qq = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = kx[ct].get(e), c = qx[ct].get(e);
+        kk += a * a;
+        qq += c * c;
+      }
+    kk = sum_xor32(sum_xor16(kk));
+    qq = sum_xor32(sum_xor16(qq));
+    rk = 1.f / sqrtf(kk + kL2NormEps);
+    rq = 1.f / sqrtf(qq + kL2NormEps);
+    if (g == 0) { sRk[i] = rk; sRq[i] = rq; }
+  }
 
   // ---- 1. gate: l_i = sum of log alpha over rows 16 I .. i (a scan across
   //         the 16 lanes of a DPP row). The block sums and their
@@ -254,10 +275,10 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
       const floatx4 s = *reinterpret_cast<const floatx4*>(&sTot[I * kD + 16 * ct + 4 * g]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float kv = kx[ct].get(e), fr = exp_f(la[ct][e]);
+        const float kv = kx[ct].get(e) * rk, fr = exp_f(la[ct][e]);
         kfI[kb].set(4 * hh + e, kv * exp_f(s[e] - la[ct][e]));
         Kr[ct].set(e, kv * fr);
-        Qr[ct].set(e, qx[ct].get(e) * fr);
+        Qr[ct].set(e, qx[ct].get(e) * rq * fr);
       }
     }
     store8(&sKf[((I * 4 + kb) * kWave + lane) * 8], kfI[kb]);
@@ -373,6 +394,10 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
         const float kc = to_f(k[row(c0) + c]);
         skk += to_f(k[row(a) + c]) * kc * d;
         sqk += to_f(q[row(a) + c]) * kc * d;
+      }
+      if constexpr (kNorm) {
+        skk *= sRk[a] * sRk[c0];
+        sqk *= sRq[a] * sRk[c0];
       }
     };
 #pragma unroll
@@ -966,7 +991,7 @@ size_t inter_block_bytes(bool bf16_io) {
 
 // phases: bit 0 chunk map, bit 1 intra-chunk, bit 2 carry (all three, in
 // order on one stream, make one prefill call).
-hipError_t launch_chunk_fwd(int phases, bool bf16_io, const void* q, const void* k,
+hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q, const void* k,
                             const void* v, const float* log_alpha, const float* beta,
                             const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
                             int32_t H, int64_t n_slots, void* o, float* h_final,
@@ -980,14 +1005,16 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, const void* q, const void*
   }
   if ((phases & 2) && T > 0 && n_slots > 0) {
     dim3 grid((unsigned)n_slots, (unsigned)H);
-    if (bf16_io)
-      intra_kernel<bf16><<<grid, kIntraThreads, 0, stream>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)v, log_alpha, beta, cu,
-          chunk_offset, status, n_seqs, T, H, inter);
-    else
-      intra_kernel<float><<<grid, kIntraThreads, 0, stream>>>(
-          (const float*)q, (const float*)k, (const float*)v, log_alpha, beta, cu,
-          chunk_offset, status, n_seqs, T, H, inter);
+#define KDA_INTRA(E, NORM)                                                                  \
+  intra_kernel<E, NORM><<<grid, kIntraThreads, 0, stream>>>(                                \
+      (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, cu, chunk_offset, status, \
+      n_seqs, T, H, inter)
+    if (bf16_io) {
+      if (l2norm) KDA_INTRA(bf16, true); else KDA_INTRA(bf16, false);
+    } else {
+      if (l2norm) KDA_INTRA(float, true); else KDA_INTRA(float, false);
+    }
+#undef KDA_INTRA
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -37,7 +37,6 @@ namespace {
 constexpr int kSliceCols = 32;                 // value columns per wave
 constexpr int kSlices = kD / kSliceCols;       // waves per (sequence, head)
 constexpr int kRowPitch = 20;                  // LDS floats per 16-row group (bank spread)
-constexpr float kL2NormEps = 1e-6f;
 
 // Sum of x over lanes l and l ^ 8 (DPP rotate by 8 inside each 16-lane row).
 __device__ __forceinline__ float sum_xor8(float x) {
@@ -57,19 +56,6 @@ __device__ __forceinline__ float sum_xor1(float x) {
 __device__ __forceinline__ float sum_xor2(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf,
                                                         false));
-}
-// Sum over lanes l and l ^ 16: permlane16_swap with both operands x gives
-// each lane x from its own row and from the partner row.
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Sum over lanes l and l ^ 32 (permlane32_swap, same construction).
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 // Sum over the whole wave, left in every lane.
 __device__ __forceinline__ float wave_sum(float x) {

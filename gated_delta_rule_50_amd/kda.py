@@ -22,7 +22,8 @@ CHUNK = 64
 HEAD_DIM = 128
 
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_phase",
-           "kda_decode_step", "kda_recurrent_fwd", "kda_status_string", "kda_version")
+           "kda_decode_step", "kda_recurrent_fwd", "kda_rmsnorm_gate", "kda_status_string",
+           "kda_version")
 
 _LIB = None
 
@@ -45,7 +46,7 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
         L.kda_chunk_fwd_workspace_bytes.restype = sz
         L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
-                                    ctypes.c_int, vp, vp, vp, sz, vp]
+                                    ctypes.c_int, ctypes.c_uint32, vp, vp, vp, sz, vp]
         L.kda_chunk_fwd.restype = ctypes.c_int
         L.kda_chunk_fwd_phase.argtypes = [i32] + L.kda_chunk_fwd.argtypes
         L.kda_chunk_fwd_phase.restype = ctypes.c_int
@@ -56,6 +57,9 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp, vp,
                                         vp]
         L.kda_recurrent_fwd.restype = ctypes.c_int
+        L.kda_rmsnorm_gate.argtypes = [vp, vp, vp, ctypes.c_float, i64, i32, ctypes.c_int, vp,
+                                       vp]
+        L.kda_rmsnorm_gate.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.restype = i32
@@ -127,11 +131,12 @@ class Prefill:
     q, k [T, H, 128], v [T, H, 128] (bf16 or fp32, one dtype); log_alpha
     [T, H, 128] fp32; beta [T, H] fp32; h0 [N, H, 128, 128] fp32 or None;
     cu_seqlens int32 [N + 1] on the device or None (one sequence). h_final
-    may be passed as h0 to continue in place.
+    may be passed as h0 to continue in place. qk_l2norm normalises q and k
+    inside the kernel.
     """
 
     def __init__(self, q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
-                 h_final=None, want_final=True, workspace=None):
+                 h_final=None, want_final=True, workspace=None, qk_l2norm=False):
         dev = k.device
         self.io = _io(k.dtype)
         self.T, self.H = int(k.shape[0]), int(k.shape[1])
@@ -157,8 +162,8 @@ class Prefill:
         self._keep = (q, k, v, log_alpha, beta, h0, cu_seqlens)
         self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
                       _ptr(cu_seqlens), self.N, self.T, self.H, int(k.shape[2]),
-                      int(v.shape[2]), self.io, _ptr(o), _ptr(h_final), _ptr(workspace),
-                      workspace.numel())
+                      int(v.shape[2]), self.io, KDA_FLAG_QK_L2NORM if qk_l2norm else 0,
+                      _ptr(o), _ptr(h_final), _ptr(workspace), workspace.numel())
 
     def run(self, stream=None):
         st = lib().kda_chunk_fwd(*self._args, _stream(stream, self.device))
@@ -173,10 +178,11 @@ class Prefill:
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
-              h_final=None, want_final=True, workspace=None, stream=None):
+              h_final=None, want_final=True, workspace=None, qk_l2norm=False, stream=None):
     """Chunked prefill (see Prefill for shapes). Returns (o, h_final or None)."""
     return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
-                   want_final=want_final, workspace=workspace).run(stream)
+                   want_final=want_final, workspace=workspace,
+                   qk_l2norm=qk_l2norm).run(stream)
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
@@ -259,3 +265,26 @@ def recurrent_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, n_seqs=
     return Recurrent(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs=n_seqs,
                      state_dtype=state_dtype, qk_l2norm=qk_l2norm, o=o, h_final=h_final,
                      want_final=want_final).run(stream)
+
+
+def rmsnorm_gate(o, gate, weight=None, eps=1e-6, *, y=None, stream=None):
+    """Output epilogue y = sigmoid(gate) * RMSNorm(o) * weight per (token, head)
+    row of 128 channels. o, gate [..., 128] in one I/O dtype; weight [128]
+    float32 or None; y may be o (in place). Returns y."""
+    dev = o.device
+    io = _io(o.dtype)
+    _check(o, "o", None, dev)
+    _check(gate, "gate", o.dtype, dev)
+    _check(weight, "weight", torch.float32, dev)
+    if gate.shape != o.shape:
+        raise ValueError(f"gate shape {tuple(gate.shape)} != o shape {tuple(o.shape)}")
+    if y is None:
+        y = torch.empty_like(o)
+    _check(y, "y", o.dtype, dev)
+    dv = int(o.shape[-1])
+    rows = o.numel() // max(dv, 1)
+    st = lib().kda_rmsnorm_gate(_ptr(o), _ptr(gate), _ptr(weight), float(eps), rows, dv, io,
+                                _ptr(y), _stream(stream, dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_rmsnorm_gate")
+    return y

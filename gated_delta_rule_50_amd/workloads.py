@@ -172,6 +172,26 @@ def make_decode_step(N, H, seed, step, io="bf16", dk=D, dv=D, qk="unit") -> Deco
 
 
 @dataclass
+class Epilogue:
+    """Inputs of the output epilogue for `rows` (token, head) rows."""
+    o: np.ndarray        # [rows, dv] operator output stand-in, I/O dtype values
+    gate: np.ndarray     # [rows, dv] sigmoid-gate pre-activation, I/O dtype values
+    weight: np.ndarray   # [dv] float32 RMSNorm weight
+    io: str
+
+
+def make_epilogue(rows, seed, io="bf16", dv=D, o_std=0.3) -> Epilogue:
+    """o ~ N(0, o_std^2) (the operator's outputs on the workloads above have
+    this order of magnitude), gate ~ N(0, 1), weight = 1 + 0.1 N(0, 1):
+    draws in that order, o and gate rounded to the I/O dtype."""
+    rng = np.random.default_rng(seed)
+    o = _to_io(_normal_f32(rng, (rows, dv)) * np.float32(o_std), io)
+    gate = _to_io(_normal_f32(rng, (rows, dv)), io)
+    weight = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
+    return Epilogue(o, gate, weight, io)
+
+
+@dataclass
 class Config:
     """One of the five benchmark/parity configurations."""
     cid: int

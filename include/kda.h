@@ -37,8 +37,8 @@
  *                               column j = value channel
  *    For decode, T is replaced by the batch N (one token per sequence).
  *  - No query scaling is applied (o_t = S_t^T q_t as printed), q and k are
- *    used as given (callers L2-normalise them; kda_recurrent_fwd can do it
- *    in the kernel), and bf16 outputs are rounded to nearest even.
+ *    used as given unless KDA_FLAG_QK_L2NORM asks the kernel to normalise
+ *    them, and bf16 outputs are rounded to nearest even.
  *  - Unchecked preconditions (the device cannot report them synchronously):
  *    finite inputs, log_alpha <= 0, cu_seqlens non-decreasing with
  *    cu_seqlens[0] = 0 and cu_seqlens[N] = T. Violations give unspecified
@@ -73,6 +73,14 @@ typedef enum {
   KDA_IO_BF16 = 1  /* q, k, v, o are bfloat16 */
 } kda_io_dtype;
 
+/* Flag bits of kda_chunk_fwd and kda_recurrent_fwd. KDA_FLAG_QK_L2NORM
+ * replaces q_t and k_t by x / sqrt(sum_c x_c^2 + 1e-6) before use: the
+ * pages' L2Norm of queries and keys (review section "Neural
+ * Parameterization"), fused into the operator as the "L2 Deep Distill"
+ * page's serving note does. The pages give no epsilon; 1e-6 keeps zero
+ * vectors at zero. Unknown bits are rejected with KDA_ERR_UNSUPPORTED. */
+#define KDA_FLAG_QK_L2NORM 1u
+
 /*
  * kda_chunk_fwd_workspace_bytes
  *   Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if an
@@ -97,6 +105,7 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
  *
  *   q, k, v, o      see layouts above; io selects float32 or bfloat16
  *   log_alpha, beta float32
+ *   flags           0 or KDA_FLAG_QK_L2NORM (q, k normalised in the kernel)
  *   h0              [N, H, 128, 128] float32, or NULL for zero states
  *   cu_seqlens      device int32 [N + 1], or NULL for one sequence (N = 1)
  *   h_final         [N, H, 128, 128] float32, or NULL to skip; it may be the
@@ -110,7 +119,8 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
  *   Errors: KDA_ERR_NULL (q, k, v, log_alpha, beta or o NULL when T > 0;
  *   cu_seqlens NULL with n_seqs != 1), KDA_ERR_SHAPE (negative sizes,
  *   n_seqs < 1, heads < 1, T > INT32_MAX with cu_seqlens),
- *   KDA_ERR_UNSUPPORTED (d_k, d_v != 128, unknown dtype, heads > 65535),
+ *   KDA_ERR_UNSUPPORTED (d_k, d_v != 128, unknown dtype or flag bit,
+ *   heads > 65535),
  *   KDA_ERR_WORKSPACE (NULL, smaller than required, not 256-byte aligned),
  *   KDA_ERR_ALIAS (o overlapping an input; h_final overlapping q, k, v,
  *   log_alpha, beta or o; h_final partially overlapping h0), KDA_ERR_HIP.
@@ -153,9 +163,10 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          const float *log_alpha, const float *beta,
                          const float *h0, const int32_t *cu_seqlens,
                          int32_t n_seqs, int64_t total_tokens, int32_t heads,
-                         int32_t dk, int32_t dv, kda_io_dtype io, void *o,
-                         float *h_final, void *workspace,
-                         size_t workspace_bytes, void *stream);
+                         int32_t dk, int32_t dv, kda_io_dtype io,
+                         uint32_t flags, void *o, float *h_final,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * kda_chunk_fwd_phase - one of the three launches that make up kda_chunk_fwd,
@@ -174,8 +185,8 @@ kda_status kda_chunk_fwd_phase(int32_t phase, const void *q, const void *k,
                                const float *beta, const float *h0,
                                const int32_t *cu_seqlens, int32_t n_seqs,
                                int64_t total_tokens, int32_t heads, int32_t dk,
-                               int32_t dv, kda_io_dtype io, void *o,
-                               float *h_final, void *workspace,
+                               int32_t dv, kda_io_dtype io, uint32_t flags,
+                               void *o, float *h_final, void *workspace,
                                size_t workspace_bytes, void *stream);
 
 /*
@@ -205,9 +216,6 @@ typedef enum {
   KDA_STATE_BF16 = 1  /* recurrent states are bfloat16 (rounded to nearest even) */
 } kda_state_dtype;
 
-/* kda_recurrent_fwd flag bits */
-#define KDA_FLAG_QK_L2NORM 1u /* normalise q_t and k_t to unit L2 norm in the kernel */
-
 /*
  * kda_recurrent_fwd - fused token-by-token forward over a packed batch.
  *
@@ -236,10 +244,7 @@ typedef enum {
  *                   float32 on chip, so a call over L tokens rounds the state
  *                   once, not L times (the pages' serving note keeps the
  *                   state in BF16, 1 MB per layer)
- *   flags           0 or KDA_FLAG_QK_L2NORM: q_t, k_t are replaced by
- *                   x / sqrt(sum_c x_c^2 + 1e-6) before use (the pages' L2Norm
- *                   of q and k, fused into the operator); other bits are
- *                   rejected
+ *   flags           0 or KDA_FLAG_QK_L2NORM (q, k normalised in the kernel)
  *   n_seqs = 0 (with total_tokens = 0) does nothing. A sequence of length 0
  *   copies h0 (or zeros) to h_final.
  *   Errors: KDA_ERR_NULL (q, k, v, log_alpha, beta or o NULL when T > 0),
@@ -260,6 +265,37 @@ kda_status kda_recurrent_fwd(const void *q, const void *k, const void *v,
                              kda_io_dtype io, kda_state_dtype state_dtype,
                              uint32_t flags, void *o, void *h_final,
                              void *stream);
+
+/*
+ * kda_rmsnorm_gate - the output epilogue: head-wise RMSNorm times a sigmoid
+ * gate (FusedRMSNormGated).
+ *
+ * For every row r (one token of one head) of d_v = 128 channels:
+ *   y[r][j] = sigmoid(gate[r][j]) * o[r][j] / sqrt(mean_j o[r][j]^2 + eps)
+ *             * weight[j]
+ * Paper: "Kimi Linear" review, section "Neural Parameterization", output
+ * gate equation (a head-wise RMSNorm of the operator's output and a
+ * data-dependent sigmoid gate before the output projection); the "L2 Deep
+ * Distill" page's module list fuses the two. The pages give no eps and no
+ * form for the norm's weight: here eps is the caller's, and the weight is
+ * one vector of 128 entries shared by all heads, or NULL for ones.
+ *
+ *   o, gate, y  [rows, 128] in the I/O dtype; o is kda_chunk_fwd's or
+ *               kda_recurrent_fwd's output viewed as [T * H, 128], gate the
+ *               gate pre-activation in the same layout
+ *   weight      [128] float32, or NULL
+ *   eps         finite, >= 0
+ *   y may be the same pointer as o (in place) but must not partially
+ *   overlap it, nor overlap gate or weight. rows = 0 does nothing.
+ *   Errors: KDA_ERR_NULL (o, gate or y NULL with rows > 0), KDA_ERR_SHAPE
+ *   (rows < 0 or > 2^36, eps negative, NaN or infinite),
+ *   KDA_ERR_UNSUPPORTED (dv != 128, unknown dtype), KDA_ERR_ALIAS,
+ *   KDA_ERR_HIP.
+ */
+kda_status kda_rmsnorm_gate(const void *o, const void *gate,
+                            const float *weight, float eps, int64_t rows,
+                            int32_t dv, kda_io_dtype io, void *y,
+                            void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *kda_status_string(kda_status s);

@@ -7,8 +7,9 @@ path shares no code with it and never imports it.
 * ``recurrent``  oracle-R: the token-by-token recurrence (C, fp64, OpenMP).
 * ``chunkwise``  oracle-C: the chunkwise WY/UT form in numpy fp64, for small
   inputs and for intermediate values (g, A, T^{-1}, W, U, per-chunk states).
+* ``epilogue``   the output epilogue: head-wise RMSNorm times a sigmoid gate.
 
 Every function here is pinned by tests/test_oracle_pins.py against closed
 forms, hand-worked examples and special cases named on the pages.
 """
-from . import chunkwise, recurrent  # noqa: F401
+from . import chunkwise, epilogue, recurrent  # noqa: F401

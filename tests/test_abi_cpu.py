@@ -27,7 +27,7 @@ def lib():
     L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
     L.kda_chunk_fwd_workspace_bytes.restype = sz
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
-                                ctypes.c_int, vp, vp, vp, sz, vp]
+                                ctypes.c_int, ctypes.c_uint32, vp, vp, vp, sz, vp]
     L.kda_chunk_fwd.restype = ctypes.c_int
     L.kda_chunk_fwd_phase.argtypes = [i32] + L.kda_chunk_fwd.argtypes
     L.kda_chunk_fwd_phase.restype = ctypes.c_int
@@ -37,6 +37,8 @@ def lib():
     L.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp, vp, vp]
     L.kda_recurrent_fwd.restype = ctypes.c_int
+    L.kda_rmsnorm_gate.argtypes = [vp, vp, vp, ctypes.c_float, i64, i32, ctypes.c_int, vp, vp]
+    L.kda_rmsnorm_gate.restype = ctypes.c_int
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_version.restype = i32
@@ -70,7 +72,7 @@ def test_status_strings_and_version(lib):
     for s in range(7):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
-    assert lib.kda_version() >= 100
+    assert lib.kda_version() >= 200
 
 
 # ------------------------------------------------------------ workspace size
@@ -107,7 +109,7 @@ def prefill_args(lib, T=100, H=2, N=1, io=BF16, **over):
     a = dict(q=BASE, k=BASE + 1 * 64 * MB, v=BASE + 2 * 64 * MB, log_alpha=BASE + 3 * 64 * MB,
              beta=BASE + 4 * 64 * MB, h0=BASE + 5 * 64 * MB,
              cu=(BASE + 6 * 64 * MB) if N != 1 else None, N=N, T=T, H=H, dk=128, dv=128,
-             io=io, o=BASE + 7 * 64 * MB, h_final=BASE + 8 * 64 * MB,
+             io=io, flags=0, o=BASE + 7 * 64 * MB, h_final=BASE + 8 * 64 * MB,
              ws=BASE + 9 * 64 * MB, ws_bytes=None, stream=None)
     a.update(over)
     if a["ws_bytes"] is None:
@@ -120,7 +122,7 @@ def prefill_args(lib, T=100, H=2, N=1, io=BF16, **over):
 
 def call_prefill(lib, a, phase=None):
     args = (a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["h0"], a["cu"], a["N"],
-            a["T"], a["H"], a["dk"], a["dv"], a["io"], a["o"], a["h_final"], a["ws"],
+            a["T"], a["H"], a["dk"], a["dv"], a["io"], a["flags"], a["o"], a["h_final"], a["ws"],
             a["ws_bytes"], a["stream"])
     if phase is None:
         return lib.kda_chunk_fwd(*args)
@@ -135,6 +137,8 @@ def call_prefill(lib, a, phase=None):
     (dict(dv=256), UNSUP),
     (dict(io=5), UNSUP),
     (dict(H=70000), UNSUP),
+    (dict(flags=2), UNSUP),
+    (dict(flags=0x80000000), UNSUP),
     (dict(q=None), NULL),
     (dict(beta=None), NULL),
     (dict(o=None), NULL),
@@ -237,6 +241,32 @@ def test_recurrent_state_size_follows_state_dtype(lib):
 
 def test_recurrent_empty_batch_is_a_noop(lib):
     assert call_recurrent(lib, N=0, T=0, q=None, h0=None, o=None, hf=None) == OK
+
+
+# ------------------------------------------------------ epilogue validation
+def call_epilogue(lib, **over):
+    a = dict(o=BASE, g=BASE + MB, w=BASE + 2 * MB, eps=1e-6, rows=64, dv=128, io=BF16,
+             y=BASE + 3 * MB, stream=None)
+    a.update(over)
+    return lib.kda_rmsnorm_gate(a["o"], a["g"], a["w"], a["eps"], a["rows"], a["dv"], a["io"],
+                                a["y"], a["stream"])
+
+
+def test_epilogue_argument_errors(lib):
+    assert call_epilogue(lib, rows=-1) == SHAPE
+    assert call_epilogue(lib, eps=-1e-6) == SHAPE
+    assert call_epilogue(lib, eps=float("nan")) == SHAPE
+    assert call_epilogue(lib, eps=float("inf")) == SHAPE
+    assert call_epilogue(lib, rows=(1 << 36) + 16) == SHAPE
+    assert call_epilogue(lib, dv=64) == UNSUP
+    assert call_epilogue(lib, io=9) == UNSUP
+    assert call_epilogue(lib, o=None) == NULL
+    assert call_epilogue(lib, g=None) == NULL
+    assert call_epilogue(lib, y=None) == NULL
+    assert call_epilogue(lib, y=BASE + 256) == ALIAS            # partial overlap of o
+    assert call_epilogue(lib, y=BASE + MB - 256) == ALIAS       # over the gate
+    assert call_epilogue(lib, y=BASE + 2 * MB - 1024) == ALIAS  # over the weight
+    assert call_epilogue(lib, rows=0, o=None, g=None, y=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -129,3 +129,21 @@ def test_config4_decode_64_steps_bf16_state():
         worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
         assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1], (step, eo, es)
     print(f"bf16-state decode worst over 64 steps: o {worst_o:.3e}, state {worst_s:.3e}")
+
+
+def test_prefill_8k_in_kernel_l2norm():
+    """The 8K x 32-head prefill shape with un-normalised q, k and the L2Norm
+    flag; three heads against the oracle on l2norm(q), l2norm(k)."""
+    p = workloads.make_prefill([8192], 32, seed=2100, io="bf16", qk="raw")
+    bf = torch.bfloat16
+    o, hf = kda.chunk_fwd(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha),
+                          dev(p.beta), None, dev(p.cu_seqlens, torch.int32), qk_l2norm=True)
+    torch.cuda.synchronize()
+    heads = [0, 15, 31]
+    ro, rh = recurrent.forward(recurrent.l2norm(p.q[:, heads]), recurrent.l2norm(p.k[:, heads]),
+                               p.v[:, heads], p.log_alpha[:, heads], p.beta[:, heads], None,
+                               p.cu_seqlens)
+    eo = rel_max_err(host(o[:, heads]), ro)
+    es = rel_fro_err(hf[:, heads].cpu().numpy().astype(np.float64), rh)
+    print(f"8K L2Norm prefill: o err {eo:.3e}, state err {es:.3e}")
+    assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]

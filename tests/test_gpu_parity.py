@@ -90,6 +90,57 @@ def test_prefill_extreme_decay_exact_fallback(io):
     _check_prefill(p, o, hf)
 
 
+def _check_prefill_l2norm(p, o, hf):
+    ro, rh = recurrent.forward(recurrent.l2norm(p.q), recurrent.l2norm(p.k), p.v,
+                               p.log_alpha, p.beta, p.h0, p.cu_seqlens)
+    tol_o, tol_s = TOL[p.io]
+    eo, es = rel_max_err(o, ro), rel_fro_err(hf, rh)
+    print(f"o err {eo:.3e} (tol {tol_o}), state err {es:.3e} (tol {tol_s})")
+    assert np.isfinite(o).all() and np.isfinite(hf).all()
+    assert eo <= tol_o and es <= tol_s, (eo, es)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_prefill_in_kernel_l2norm(io):
+    """Un-normalised q, k (norm ~ 11) with the L2Norm flag against the oracle
+    on l2norm(q), l2norm(k) in fp64; packed, with ragged tails."""
+    p = workloads.make_prefill([70, 1, 130, 0, 64], H=2, seed=40, io=io, h0_std=0.05, qk="raw")
+    dt = io_dtype(p.io)
+    o, hf = kda.chunk_fwd(dev(p.q, dt), dev(p.k, dt), dev(p.v, dt), dev(p.log_alpha),
+                          dev(p.beta), dev(p.h0), dev(p.cu_seqlens, torch.int32),
+                          qk_l2norm=True)
+    torch.cuda.synchronize()
+    _check_prefill_l2norm(p, host(o), host(hf))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_prefill_l2norm_exact_fallback(io):
+    """The exact diagonal-block path (in-block decay ratios past e^44) with
+    the L2Norm flag: its re-read rows take the same scales."""
+    p = workloads.make_prefill([200], H=2, seed=41, io=io, h0_std=0.05, qk="raw")
+    p.log_alpha[:, :, :16] = -6.0
+    dt = io_dtype(p.io)
+    o, hf = kda.chunk_fwd(dev(p.q, dt), dev(p.k, dt), dev(p.v, dt), dev(p.log_alpha),
+                          dev(p.beta), dev(p.h0), dev(p.cu_seqlens, torch.int32),
+                          qk_l2norm=True)
+    torch.cuda.synchronize()
+    _check_prefill_l2norm(p, host(o), host(hf))
+
+
+def test_prefill_l2norm_flag_on_unit_inputs():
+    """On unit-norm inputs the flag changes results only at rounding level,
+    and the two forward paths agree with it set."""
+    p = workloads.make_prefill([150, 9], H=2, seed=42, io="f32", h0_std=0.05)
+    args = (dev(p.q), dev(p.k), dev(p.v), dev(p.log_alpha), dev(p.beta), dev(p.h0),
+            dev(p.cu_seqlens, torch.int32))
+    o1, h1 = kda.chunk_fwd(*args)
+    o2, h2 = kda.chunk_fwd(*args, qk_l2norm=True)
+    o3, h3 = kda.recurrent_fwd(*args, qk_l2norm=True)
+    torch.cuda.synchronize()
+    assert rel_max_err(host(o2), host(o1)) <= 1e-5 and rel_fro_err(host(h2), host(h1)) <= 1e-5
+    assert rel_max_err(host(o3), host(o2)) <= 1e-4 and rel_fro_err(host(h3), host(h2)) <= 1e-4
+
+
 def test_config0_tiny_fp32():
     p = workloads.config(0).prefill()
     o, hf = _run_prefill(p, cu=False)

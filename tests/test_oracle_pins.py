@@ -15,7 +15,7 @@ from pathlib import Path
 import numpy as np
 import pytest
 
-from oracle import chunkwise, recurrent
+from oracle import chunkwise, epilogue, recurrent
 
 GOLDEN = Path(__file__).parent / "golden"
 
@@ -316,3 +316,45 @@ def test_l2norm_feeds_exact_recall():
     b[:] = 1.0
     o, _ = recurrent.forward(kn, kn, v, la, b, S0)
     np.testing.assert_allclose(o, v, rtol=0, atol=1e-5)
+
+
+# ----------------------------------------------------- RMSNorm x sigmoid gate
+def test_sigmoid_closed_forms():
+    """sigmoid(0) = 1/2, sigmoid(log 3) = 3/4, sigmoid(x) + sigmoid(-x) = 1,
+    and no overflow far from zero."""
+    assert epilogue.sigmoid(0.0) == 0.5
+    np.testing.assert_allclose(epilogue.sigmoid(np.log(3.0)), 0.75, rtol=1e-15)
+    x = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(epilogue.sigmoid(x) + epilogue.sigmoid(-x), 1.0, rtol=1e-15)
+    big = epilogue.sigmoid(np.array([-800.0, 800.0]))
+    assert big[0] == 0.0 and big[1] == 1.0
+
+
+def test_rmsnorm_gate_worked_example():
+    """o = (3, 4): mean square 12.5, so RMSNorm(o) = o / sqrt(12.5); gate 0
+    halves it; weight (1, 2) scales the channels."""
+    y = epilogue.rmsnorm_gate(np.array([3.0, 4.0]), np.array([0.0, 0.0]),
+                              np.array([1.0, 2.0]), eps=0.0)
+    np.testing.assert_allclose(y, [0.5 * 3 / np.sqrt(12.5), 0.5 * 2 * 4 / np.sqrt(12.5)],
+                               rtol=1e-15)
+    # eps enters under the root: o = (1, 1), eps = 3 gives 1 / 2
+    y = epilogue.rmsnorm_gate(np.ones(2), np.full(2, 800.0), None, eps=3.0)
+    np.testing.assert_allclose(y, [0.5, 0.5], rtol=1e-15)
+
+
+def test_rmsnorm_gate_invariants():
+    """Per row: unit RMS after the norm (open gate, unit weight), invariance
+    to scaling o, rows normalised independently, gate applied elementwise."""
+    rng = np.random.default_rng(12)
+    o = rng.standard_normal((6, 4, 128)) * rng.uniform(0.1, 10, (6, 4, 1))
+    g = rng.standard_normal((6, 4, 128))
+    y_open = epilogue.rmsnorm_gate(o, np.full_like(o, 800.0), None, eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y_open ** 2, axis=-1)), 1.0, rtol=1e-13)
+    y = epilogue.rmsnorm_gate(o, g, None, eps=0.0)
+    np.testing.assert_allclose(epilogue.rmsnorm_gate(5.0 * o, g, None, eps=0.0), y, rtol=1e-13)
+    o2 = o.copy()
+    o2[0, 0] *= 3.0                      # one row changes, the others do not
+    y2 = epilogue.rmsnorm_gate(o2, g, None, eps=0.0)
+    np.testing.assert_array_equal(y2[1:], y[1:])
+    np.testing.assert_array_equal(y2[0, 1:], y[0, 1:])
+    np.testing.assert_allclose(y / y_open, epilogue.sigmoid(g), rtol=1e-13)
