@@ -14,6 +14,12 @@ at a time (phase entry point, all chunks per launch) to measure each
 kernel's own duration; ``kernels`` holds those and the decode kernel's, and
 ``roofline`` describes the one with the longest mean duration.
 
+``extensions`` times the operator's optional paths, each on its own
+workload with its own roofline: the fused multi-token recurrent call
+(256 sequences x 32 heads x L = 4 and 64 new tokens), the decode step with a
+bf16 state, the prefill with in-kernel q/k L2Norm, and the RMSNorm x
+sigmoid-gate epilogue over the prefill's 8192 x 32 output rows.
+
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -47,7 +53,17 @@ STATE_BYTES = D * D * 4
 FLOPS_EQ13 = 6 * D * D + 3 * C * D + C * C             # 126976 per token-head
 FLOPS_DENSE = 6 * D * D + 10 * C * D                   # 180224 per token-head
 # Decode, per (sequence, head): state read + write, q/k/v, log_alpha, beta, o.
-DECODE_BYTES = 2 * STATE_BYTES + 3 * 256 + 512 + 4 + 256   # 132612
+TOKEN_BYTES = 3 * 256 + 512 + 4 + 256                      # 1540 per token-head
+DECODE_BYTES = 2 * STATE_BYTES + TOKEN_BYTES               # 132612
+# Recurrent path, per token-head: S~^T k and S~^T q (2 d^2 each as FMAs),
+# the decay a*s (d^2) and the rank-1 correction (2 d^2).
+FLOPS_RECURRENT = 7 * D * D                                # 114688
+# fp32 VALU without packed-fp32 instructions: 256 CUs x 64 lanes x 2 flops
+# (one FMA per lane per cycle) x 2.4 GHz; the published 157.3 TFLOP/s
+# counts the packed forms, which this code is built without.
+FP32_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12             # 78.6
+# Epilogue, per row of 128 channels (bf16): o and gate read, y written.
+EPILOGUE_BYTES = 3 * 256
 
 
 def _parse():
@@ -59,6 +75,8 @@ def _parse():
                     help="skip the oracle timing on the host cores")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
+    ap.add_argument("--no-extensions", action="store_true",
+                    help="skip the timings of the optional paths (shorter counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy first (counter scale factor)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -77,7 +95,13 @@ def sources_hash() -> str:
 
 
 def _kernel_key(name):
-    for k in ("intra", "carry", "decode", "chunk_map"):
+    """Bench-step kernel a counter row belongs to. The counter passes run with
+    --no-extensions, so the only recurrent-kernel dispatches are the decode
+    step's (profilers print these template names mangled or demangled, and
+    not always faithfully, so only the base name is matched)."""
+    if "recurrent_fwd_kernel" in name:
+        return "decode"
+    for k in ("intra", "carry", "chunk_map"):
         if k in name:
             return k
     # device-to-device copies (the runtime's blit kernel for torch's copy_)
@@ -178,6 +202,78 @@ def cpu_baseline(p, seconds):
             "decode_value": cfg.n_seqs / ddt}
 
 
+def _time_calls(torch, fn, steps, warmup):
+    """Mean duration (us) of fn() from events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = _events(torch, steps + 1)
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])) * 1e3
+
+
+def _hbm(alg_bytes, us):
+    gbps = alg_bytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS}
+
+
+def extensions(torch, d, pre_args, steps, warmup):
+    """Timings of the optional paths (module docstring), inputs resident."""
+    from gated_delta_rule_50_amd import Prefill, Recurrent, rmsnorm_gate, workloads
+    bf = torch.bfloat16
+    out = {}
+    N, H = 256, 32
+    for L in (4, 64):
+        p = workloads.make_prefill([L] * N, H, seed=2000 + L, io="bf16", h0_std=0.02)
+        ins = (d(p.q, bf), d(p.k, bf), d(p.v, bf), d(p.log_alpha), d(p.beta))
+        S = d(p.h0)
+        rec = Recurrent(*ins, S, None, n_seqs=N, h_final=S)
+        us = _time_calls(torch, rec.run, steps, warmup)
+        alg = N * H * (2 * STATE_BYTES + L * TOKEN_BYTES)
+        tf = N * H * L * FLOPS_RECURRENT / (us * 1e-6) / 1e12
+        roof = _hbm(alg, us) if L <= 8 else {
+            "bound": "alu", "achieved": tf, "peak": FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / FP32_VALU_TFLOPS}
+        out[f"recurrent_L{L}"] = {
+            "workload": f"{N} sequences x {H} heads x {L} new tokens, bf16 q/k/v, fp32 states "
+                        f"~N(0,0.02) updated in place", "us": us,
+            "tokens_per_s": N * L / (us * 1e-6), "alg_bytes": alg,
+            "tflops": tf, "roofline": roof}
+        del p, ins, S, rec
+    cfg4 = workloads.config(4)
+    ds = workloads.make_decode_step(cfg4.n_seqs, cfg4.H, cfg4.seed, 0, io=cfg4.io)
+    Sb = d(workloads.make_decode_state(cfg4.n_seqs, cfg4.H, cfg4.seed), bf)
+    rec = Recurrent(d(ds.q, bf), d(ds.k, bf), d(ds.v, bf), d(ds.log_alpha), d(ds.beta), Sb,
+                    None, n_seqs=cfg4.n_seqs, state_dtype=bf, h_final=Sb)
+    us = _time_calls(torch, rec.run, steps, warmup)
+    alg = cfg4.n_seqs * cfg4.H * (STATE_BYTES + TOKEN_BYTES)
+    out["decode_bf16_state"] = {
+        "workload": f"decode step {cfg4.n_seqs}x{cfg4.H}, bf16 states updated in place",
+        "us": us, "tokens_per_s": cfg4.n_seqs / (us * 1e-6), "alg_bytes": alg,
+        "roofline": _hbm(alg, us)}
+    del Sb, rec
+    pre_n = Prefill(*pre_args, qk_l2norm=True)
+    us = _time_calls(torch, pre_n.run, steps, warmup)
+    out["prefill_qk_l2norm"] = {
+        "workload": "the 8K prefill with KDA_FLAG_QK_L2NORM", "us": us,
+        "tokens_per_s": pre_args[0].shape[0] / (us * 1e-6)}
+    o = pre_n.o
+    rows = o.shape[0] * o.shape[1]
+    e = workloads.make_epilogue(rows, seed=76, io="bf16")
+    gate, w = d(e.gate, bf).view(o.shape), d(e.weight)
+    y = torch.empty_like(o)
+    us = _time_calls(torch, lambda: rmsnorm_gate(o, gate, w, y=y), steps, warmup)
+    alg = rows * EPILOGUE_BYTES + D * 4
+    out["epilogue"] = {"workload": f"RMSNorm x sigmoid gate over {rows} rows of 128, bf16",
+                       "us": us, "alg_bytes": alg, "roofline": _hbm(alg, us)}
+    return out
+
+
 def main():
     args = _parse()
     if args.summarize_pmc:
@@ -207,8 +303,9 @@ def main():
     def d(x, dt=torch.float32):
         return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dt)
 
-    pre = Prefill(d(p.q, bf), d(p.k, bf), d(p.v, bf), d(p.log_alpha), d(p.beta), None,
-                  d(p.cu_seqlens, torch.int32))
+    pre_args = (d(p.q, bf), d(p.k, bf), d(p.v, bf), d(p.log_alpha), d(p.beta), None,
+                d(p.cu_seqlens, torch.int32))
+    pre = Prefill(*pre_args)
     cfg4 = workloads.config(4)
     S = d(workloads.make_decode_state(cfg4.n_seqs, cfg4.H, cfg4.seed))
     ds = workloads.make_decode_step(cfg4.n_seqs, cfg4.H, cfg4.seed, 0, io=cfg4.io)
@@ -329,6 +426,8 @@ def main():
         "prefill_path": prefill_path,
         "kernels": kernels,
     }
+    if not args.no_extensions:
+        out["extensions"] = extensions(torch, d, pre_args, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out))

@@ -3,5 +3,5 @@
 ``kda`` binds the C ABI of libkda.so (HIP kernels for gfx950);
 ``workloads`` draws the seeded synthetic inputs.
 """
-from .kda import (KDAError, Prefill, alloc_workspace, chunk_fwd,  # noqa: F401
-                  chunk_fwd_workspace_bytes, decode_step, lib)
+from .kda import (KDAError, Prefill, Recurrent, alloc_workspace, chunk_fwd,  # noqa: F401
+                  chunk_fwd_workspace_bytes, decode_step, lib, recurrent_fwd, rmsnorm_gate)

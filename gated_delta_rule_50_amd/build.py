@@ -20,8 +20,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libkda.so"
 BUILD = ROOT / "_build"
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_recurrent.hip",
-           "kda_epilogue.hip"]
+SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_recurrent.hip", "kda_epilogue.hip"]
 
 
 def hipcc() -> str:

@@ -7,9 +7,6 @@
 #include "kda.h"
 
 namespace kda {
-hipError_t launch_decode_step(bool bf16_io, const void* q, const void* k, const void* v,
-                              const float* log_alpha, const float* beta, float* S,
-                              void* o, int64_t pairs, hipStream_t stream);
 hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q, const void* k,
                             const void* v, const float* log_alpha, const float* beta,
                             const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
@@ -165,7 +162,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
   if (n_seqs == 0) return KDA_OK;
   if (!q || !k || !v || !log_alpha || !beta || !S_inout || !o) return KDA_ERR_NULL;
   const int64_t pairs = (int64_t)n_seqs * heads;
-  if (pairs > INT32_MAX) return KDA_ERR_SHAPE;
+  if (pairs > ((int64_t)1 << 29)) return KDA_ERR_SHAPE;  // grid of 4 waves per pair
   const int64_t eb = io_bytes(io);
   const Range rq(q, pairs * kDim * eb), rk(k, pairs * kDim * eb), rv(v, pairs * kDim * eb);
   const Range rla(log_alpha, pairs * kDim * 4), rb(beta, pairs * 4);
@@ -174,9 +171,10 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
     if (overlap(rs, *in)) return KDA_ERR_ALIAS;
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb})
     if (overlap(ro, *in)) return KDA_ERR_ALIAS;
-  const hipError_t err = kda::launch_decode_step(io == KDA_IO_BF16, q, k, v, log_alpha,
-                                                 beta, S_inout, o, pairs,
-                                                 static_cast<hipStream_t>(stream));
+  // one token per sequence through the fused recurrent kernel, state in place
+  const hipError_t err = kda::launch_recurrent_fwd(
+      io == KDA_IO_BF16, false, false, q, k, v, log_alpha, beta, S_inout, nullptr, 1, n_seqs,
+      heads, pairs, o, S_inout, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

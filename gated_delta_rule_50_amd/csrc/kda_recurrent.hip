@@ -10,7 +10,8 @@
 // last, so a call over L tokens moves the state's bytes once, not L times.
 // This is the path the review's "FLOPs Accounting and Inference Strategy"
 // section gives short inputs (the recurrent kernel for generation); the
-// serving note of the "L2 Deep Distill" page routes q_len <= 64 to it.
+// serving note of the "L2 Deep Distill" page routes q_len <= 64 to it. The
+// single-token decode step is this kernel with one token per sequence.
 //
 // Optional pieces (both from the pages' serving notes):
 //  * q and k normalised to unit L2 norm inside the kernel (q <- q / ||q||,
@@ -78,21 +79,23 @@ template <class IO> struct Raw4;
 template <> struct Raw4<float> { typedef floatx4 T; };
 template <> struct Raw4<bf16> { typedef bf16x4 T; };
 
-// State storage: four consecutive columns of one row.
+// State storage: four consecutive columns of one row. The state is touched
+// once per call, so its accesses are nontemporal (streamed past the caches).
 __device__ __forceinline__ float4 load_state4(const float* p) {
-  return *reinterpret_cast<const float4*>(p);
+  const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+  return float4{v[0], v[1], v[2], v[3]};
 }
 __device__ __forceinline__ float4 load_state4(const bf16* p) {
-  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(p));
   return float4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 __device__ __forceinline__ void store_state4(float* p, float4 x) {
-  *reinterpret_cast<float4*>(p) = x;
+  __builtin_nontemporal_store(floatx4{x.x, x.y, x.z, x.w}, reinterpret_cast<floatx4*>(p));
 }
 __device__ __forceinline__ void store_state4(bf16* p, float4 x) {
   bf16x4 v;
   v[0] = (bf16)x.x; v[1] = (bf16)x.y; v[2] = (bf16)x.z; v[3] = (bf16)x.w;
-  *reinterpret_cast<bf16x4*>(p) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<bf16x4*>(p));
 }
 
 // Per-token inputs of one lane: channels 2 l, 2 l + 1 of q, k, log alpha;
@@ -120,7 +123,8 @@ __device__ __forceinline__ void fetch_token(TokenIn<IO>& x, const IO* q, const I
 
 }  // namespace
 
-template <class IO, class ST, bool kNorm>
+// kSingle: exactly one token per sequence (the decode step), no token loop.
+template <class IO, class ST, bool kNorm, bool kSingle>
 __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const ST* h0,
@@ -138,7 +142,10 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
   const int h = (int)(p - n * H);
 
   int64_t bos, eos;
-  if (cu != nullptr) {
+  if constexpr (kSingle) {
+    bos = n;
+    eos = n + 1;
+  } else if (cu != nullptr) {
     bos = min<int64_t>(max<int64_t>(cu[n], 0), T);
     eos = min<int64_t>(max<int64_t>(cu[n + 1], bos), T);
   } else {
@@ -173,8 +180,10 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     const TokenIn<IO> cur = nxt;
     // Next token's inputs (the last token fetches itself again: the load is
     // unconditional so the counter waits stay exact).
-    const int64_t tn = t + 1 < eos ? t + 1 : t;
-    fetch_token(nxt, q, k, v, log_alpha, beta, tn * H + h, lane, col0);
+    if constexpr (!kSingle) {
+      const int64_t tn = t + 1 < eos ? t + 1 : t;
+      fetch_token(nxt, q, k, v, log_alpha, beta, tn * H + h, lane, col0);
+    }
 
     float q0 = (float)cur.q[0], q1 = (float)cur.q[1];
     float k0 = (float)cur.k[0], k1 = (float)cur.k[1];
@@ -256,13 +265,19 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
   if (pairs == 0) return hipSuccess;
   const int64_t blocks = (pairs + 7) / 8 * 8 * kSlices;
   dim3 grid((unsigned)blocks), block(64);
-#define KDA_REC_LAUNCH(IO, ST, NORM)                                                         \
-  recurrent_fwd_kernel<IO, ST, NORM><<<grid, block, 0, stream>>>(                            \
+  const bool single = cu == nullptr && seq_len == 1;
+#define KDA_REC_LAUNCH(IO, ST, NORM, ONE)                                                    \
+  recurrent_fwd_kernel<IO, ST, NORM, ONE><<<grid, block, 0, stream>>>(                       \
       (const IO*)q, (const IO*)k, (const IO*)v, log_alpha, beta, (const ST*)h0, cu, seq_len, \
       T, H, pairs, (IO*)o, (ST*)h_final)
-#define KDA_REC_NORM(IO, ST)          \
-  if (l2norm) KDA_REC_LAUNCH(IO, ST, true); \
-  else KDA_REC_LAUNCH(IO, ST, false)
+#define KDA_REC_NORM(IO, ST)                                   \
+  if (l2norm) {                                                \
+    if (single) KDA_REC_LAUNCH(IO, ST, true, true);            \
+    else KDA_REC_LAUNCH(IO, ST, true, false);                  \
+  } else {                                                     \
+    if (single) KDA_REC_LAUNCH(IO, ST, false, true);           \
+    else KDA_REC_LAUNCH(IO, ST, false, false);                 \
+  }
   if (bf16_io) {
     if (bf16_state) { KDA_REC_NORM(bf16, bf16); } else { KDA_REC_NORM(bf16, float); }
   } else {

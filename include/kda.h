@@ -201,7 +201,10 @@ kda_status kda_chunk_fwd_phase(int32_t phase, const void *q, const void *k,
  * read once and overwritten in place.
  *   q, k [N, H, 128], v [N, H, 128], o [N, H, 128]: I/O dtype
  *   log_alpha [N, H, 128], beta [N, H]: float32
- * n_seqs = 0 does nothing. Errors: KDA_ERR_NULL, KDA_ERR_SHAPE,
+ * It is kda_recurrent_fwd with one token per sequence, an fp32 state
+ * updated in place and no flags (same kernel, same results).
+ * n_seqs = 0 does nothing. Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (negative
+ * sizes, heads < 1, more than 2^29 (sequence, head) pairs),
  * KDA_ERR_UNSUPPORTED, KDA_ERR_ALIAS (S_inout or o overlapping an input, or
  * each other), KDA_ERR_HIP.
  */
