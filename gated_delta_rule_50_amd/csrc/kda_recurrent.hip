@@ -25,8 +25,9 @@
 // 32 w + 4 (l % 8) .. +3 and key rows 16 (l / 8) .. +15 of that slice, 64
 // fp32 state values. Both column reductions of a token (e and S~^T q) are
 // sums over the eight lanes that share a column quad (lane bits 3..5), done
-// with cross-lane moves inside the wave, so a token needs no workgroup
-// barrier. The per-token vectors (alpha k, alpha q, alpha, k) go through a
+// with cross-lane moves inside the wave as a reduce-scatter (each lane ends
+// with one column's sums) and a gather of the four corrections, so a token
+// needs no workgroup barrier. The per-token vectors (alpha k, alpha q, alpha, k) go through a
 // wave-private LDS row so each lane can read its 16 rows with four 16-byte
 // reads.
 #include "kda_device.h"
@@ -38,6 +39,8 @@ namespace {
 constexpr int kSliceCols = 32;                 // value columns per wave
 constexpr int kSlices = kD / kSliceCols;       // waves per (sequence, head)
 constexpr int kRowPitch = 20;                  // LDS floats per 16-row group (bank spread)
+constexpr int kStaticLds = 4 * 8 * kRowPitch * 4;   // the four token-vector rows, bytes
+constexpr int kLdsPerCu = 160 * 1024;               // gfx950 LDS per CU
 
 // Sum of x over lanes l and l ^ 8 (DPP rotate by 8 inside each 16-lane row).
 __device__ __forceinline__ float sum_xor8(float x) {
@@ -62,9 +65,32 @@ __device__ __forceinline__ float sum_xor2(float x) {
 __device__ __forceinline__ float wave_sum(float x) {
   return sum_xor32(sum_xor16(sum_xor1(sum_xor2(sum_ror4(sum_xor8(x))))));
 }
-// Sum over the eight lanes sharing lane bits 0..2 (l, l ^ 8, ..., l ^ 56).
-__device__ __forceinline__ float group_sum8(float x) {
-  return sum_xor32(sum_xor16(sum_xor8(x)));
+// Reduce-scatter steps: permlane32_swap(a, b) gives {a_lo, b_lo} and
+// {a_hi, b_hi} (lo = lanes 0-31, hi = 32-63), so their sum holds a summed
+// over lanes l, l ^ 32 in the lanes with bit 5 clear and b's sum in those
+// with bit 5 set. permlane16_swap does the same for bit 4.
+__device__ __forceinline__ float sum_pair32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_pair16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// All-gather steps: x from the lane with bit 5 (bit 4) clear and set.
+__device__ __forceinline__ void gather32(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void gather16(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
 }
 
 // Two consecutive I/O elements kept raw until used.
@@ -75,9 +101,6 @@ template <> struct Raw2<float> {
 template <> struct Raw2<bf16> {
   typedef bf16 __attribute__((ext_vector_type(2))) T;
 };
-template <class IO> struct Raw4;
-template <> struct Raw4<float> { typedef floatx4 T; };
-template <> struct Raw4<bf16> { typedef bf16x4 T; };
 
 // State storage: four consecutive columns of one row. The state is touched
 // once per call, so its accesses are nontemporal (streamed past the caches).
@@ -99,12 +122,12 @@ __device__ __forceinline__ void store_state4(bf16* p, float4 x) {
 }
 
 // Per-token inputs of one lane: channels 2 l, 2 l + 1 of q, k, log alpha;
-// the lane's four value columns of v; beta.
+// v of the one value column whose sums the lane finishes; beta.
 template <class IO>
 struct TokenIn {
   typename Raw2<IO>::T q, k;
   float2 la;
-  typename Raw4<IO>::T v;
+  IO v;
   float b;
 };
 
@@ -112,12 +135,12 @@ template <class IO>
 __device__ __forceinline__ void fetch_token(TokenIn<IO>& x, const IO* q, const IO* k,
                                             const IO* v, const float* log_alpha,
                                             const float* beta, int64_t row, int lane,
-                                            int col0) {
+                                            int vcol) {
   const int64_t base = row * kD;
   x.q = *reinterpret_cast<const typename Raw2<IO>::T*>(q + base + 2 * lane);
   x.k = *reinterpret_cast<const typename Raw2<IO>::T*>(k + base + 2 * lane);
   x.la = *reinterpret_cast<const float2*>(log_alpha + base + 2 * lane);
-  x.v = *reinterpret_cast<const typename Raw4<IO>::T*>(v + base + col0);
+  x.v = v[base + vcol];
   x.b = beta[row];
 }
 
@@ -157,6 +180,8 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
   const int jq = lane & 7;        // column quad inside the slice
   const int rl = lane >> 3;       // rows 16 rl .. 16 rl + 15
   const int col0 = kSliceCols * w + 4 * jq;
+  // after the column sums this lane holds column cq of its quad
+  const int cq = 2 * ((lane >> 4) & 1) + (lane >> 5);
 
   // Wave-private token vectors, 16-row groups at a padded pitch.
   __shared__ __align__(16) float s_ka[8 * kRowPitch], s_qa[8 * kRowPitch];
@@ -174,7 +199,7 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
 
   const int widx = (lane >> 3) * kRowPitch + 2 * (lane & 7);  // channels 2 l, 2 l + 1
   TokenIn<IO> nxt;
-  if (bos < eos) fetch_token(nxt, q, k, v, log_alpha, beta, bos * H + h, lane, col0);
+  if (bos < eos) fetch_token(nxt, q, k, v, log_alpha, beta, bos * H + h, lane, col0 + cq);
 
   for (int64_t t = bos; t < eos; ++t) {
     const TokenIn<IO> cur = nxt;
@@ -182,7 +207,7 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     // unconditional so the counter waits stay exact).
     if constexpr (!kSingle) {
       const int64_t tn = t + 1 < eos ? t + 1 : t;
-      fetch_token(nxt, q, k, v, log_alpha, beta, tn * H + h, lane, col0);
+      fetch_token(nxt, q, k, v, log_alpha, beta, tn * H + h, lane, col0 + cq);
     }
 
     float q0 = (float)cur.q[0], q1 = (float)cur.q[1];
@@ -218,14 +243,21 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
         pr.x += qav[r] * x.x; pr.y += qav[r] * x.y; pr.z += qav[r] * x.z; pr.w += qav[r] * x.w;
       }
     }
-    pe.x = group_sum8(pe.x); pe.y = group_sum8(pe.y);
-    pe.z = group_sum8(pe.z); pe.w = group_sum8(pe.w);
-    // d = beta (v - e): the correction written along k.
-    float4 d;
-    d.x = cur.b * ((float)cur.v[0] - pe.x);
-    d.y = cur.b * ((float)cur.v[1] - pe.y);
-    d.z = cur.b * ((float)cur.v[2] - pe.z);
-    d.w = cur.b * ((float)cur.v[3] - pe.w);
+    // Sums over the eight lanes of the quad (lane bits 3..5) as a
+    // reduce-scatter: every exchange pairs two of the lane's values, and the
+    // lane ends with e and pr of column cq = 2 bit4 + bit5 of its quad.
+    const float e01 = sum_pair32(pe.x, pe.y), e23 = sum_pair32(pe.z, pe.w);
+    const float p01 = sum_pair32(pr.x, pr.y), p23 = sum_pair32(pr.z, pr.w);
+    const float ec = sum_xor8(sum_pair16(e01, e23));
+    const float pc = sum_xor8(sum_pair16(p01, p23));
+    // d = beta (v - e), the correction written along k; every lane then
+    // gathers the quad's four d values.
+    const float dc = cur.b * ((float)cur.v - ec);
+    float d4[4], dlo, dhi;
+    gather32(dc, dlo, dhi);          // d of columns 2 bit4 and 2 bit4 + 1
+    gather16(dlo, d4[0], d4[2]);
+    gather16(dhi, d4[1], d4[3]);
+    const float4 d = {d4[0], d4[1], d4[2], d4[3]};
 
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -243,12 +275,7 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
       }
     }
 
-    pr.x = group_sum8(pr.x); pr.y = group_sum8(pr.y);
-    pr.z = group_sum8(pr.z); pr.w = group_sum8(pr.w);
-    if (rl == 0) {
-      floatx4 y = {pr.x + qk * d.x, pr.y + qk * d.y, pr.z + qk * d.z, pr.w + qk * d.w};
-      store4_io(o + (t * H + h) * kD + col0, y);
-    }
+    if ((lane & 8) == 0) o[(t * H + h) * kD + col0 + cq] = from_f<IO>(pc + qk * dc);
   }
 
   if (h_final != nullptr) {
@@ -266,8 +293,23 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
   const int64_t blocks = (pairs + 7) / 8 * 8 * kSlices;
   dim3 grid((unsigned)blocks), block(64);
   const bool single = cu == nullptr && seq_len == 1;
+  // Resident workgroups per CU. With one or a few tokens per sequence the
+  // kernel streams the states, and HBM serves that stream best with few
+  // waves in flight per CU: on 256 x 32 states, capping residency by padding
+  // each workgroup's LDS takes the fp32-state decode step from 200 to
+  // 175 us (5 per CU), the bf16-state one from 131 to 109 us (8 per CU),
+  // L = 2 and 4 from 193 / 199 to 178 / 187 us (8 / 10 per CU). From about
+  // 16 tokens on the token loop is VALU-bound and wants every wave it can
+  // get, so no cap.
+  const int64_t n_seqs = pairs / H;
+  const int64_t avg_len = n_seqs > 0 ? T / n_seqs : 0;
+  int cap = 0;
+  if (single) cap = bf16_state ? 8 : 5;
+  else if (avg_len <= 2) cap = 8;
+  else if (avg_len <= 4) cap = 10;
+  const size_t lds_pad = cap > 0 ? (size_t)(kLdsPerCu / cap - kStaticLds) : 0;
 #define KDA_REC_LAUNCH(IO, ST, NORM, ONE)                                                    \
-  recurrent_fwd_kernel<IO, ST, NORM, ONE><<<grid, block, 0, stream>>>(                       \
+  recurrent_fwd_kernel<IO, ST, NORM, ONE><<<grid, block, lds_pad, stream>>>(                 \
       (const IO*)q, (const IO*)k, (const IO*)v, log_alpha, beta, (const ST*)h0, cu, seq_len, \
       T, H, pairs, (IO*)o, (ST*)h_final)
 #define KDA_REC_NORM(IO, ST)                                   \
