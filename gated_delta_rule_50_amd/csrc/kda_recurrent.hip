@@ -27,9 +27,9 @@
 // sums over the eight lanes that share a column quad (lane bits 3..5), done
 // with cross-lane moves inside the wave as a reduce-scatter (each lane ends
 // with one column's sums) and a gather of the four corrections, so a token
-// needs no workgroup barrier. The per-token vectors (alpha k, alpha q, alpha, k) go through a
-// wave-private LDS row so each lane can read its 16 rows with four 16-byte
-// reads.
+// needs no workgroup barrier. The per-token vectors (alpha k, alpha q,
+// alpha, k) go through a wave-private LDS row so each lane can read its 16
+// rows with four 16-byte reads.
 #include "kda_device.h"
 
 namespace kda {
