@@ -142,9 +142,8 @@ template <class E, bool kNorm>
 __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_offset,
-    const int32_t* __restrict__ status, int32_t n_seqs, int64_t T, int32_t H,
-    uint8_t* __restrict__ inter) {
+    const int32_t* __restrict__ cu, int32_t* chunk_offset, int32_t* status, int32_t n_seqs,
+    int64_t T, int32_t H, uint8_t* __restrict__ inter, int32_t single) {
   // LDS, one region reused across phases:
   //   rows phase   sKf  Kf fragments of the four blocks [J][kb][lane][8]
   //                sF   per-block channel factors (five rows per block)
@@ -170,17 +169,38 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   E* const sNL = sX + 4 * 16 * kTile;
   E* const sTI = sNL + 12 * kTile;
 
-  if (status[0] != 0) return;
   const int b = blockIdx.x, h = blockIdx.y;
-  const int total = chunk_offset[n_seqs];
-  if (b >= total) return;
-  int lo = 0, hi = n_seqs;  // chunk_offset[lo] <= b < chunk_offset[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (chunk_offset[mid] <= b) lo = mid; else hi = mid;
+  int total, first;
+  int64_t seq_start, seq_end;
+  if (single) {
+    // one sequence: the chunk range and the cu_seqlens check need no chunk
+    // map; the first block records them in the workspace as the map would
+    const bool ok = cu == nullptr || (cu[0] == 0 && (int64_t)cu[1] == T);
+    total = (int)((T + kC - 1) / kC);
+    if (b == 0 && h == 0 && threadIdx.x == 0) {
+      status[0] = ok ? 0 : 1;
+      chunk_offset[0] = 0;
+      chunk_offset[1] = total;
+    }
+    if (!ok) return;
+    first = 0;
+    seq_start = 0;
+    seq_end = T;
+  } else {
+    if (status[0] != 0) return;
+    total = chunk_offset[n_seqs];
+    if (b >= total) return;
+    int lo = 0, hi = n_seqs;  // chunk_offset[lo] <= b < chunk_offset[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (chunk_offset[mid] <= b) lo = mid; else hi = mid;
+    }
+    first = chunk_offset[lo];
+    seq_start = cu ? cu[lo] : 0;
+    seq_end = cu ? cu[lo + 1] : T;
   }
-  const int64_t seq_start = cu ? cu[lo] : 0, seq_end = cu ? cu[lo + 1] : T;
-  const int64_t tok0 = seq_start + (int64_t)(b - chunk_offset[lo]) * kC;
+  if (b >= total) return;
+  const int64_t tok0 = seq_start + (int64_t)(b - first) * kC;
   const int len = (int)min((int64_t)kC, seq_end - tok0);
 
   const int lane = threadIdx.x & 63;
@@ -736,7 +756,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
     const float* __restrict__ h0, float* __restrict__ h_final, E* __restrict__ o,
-    int32_t n_seqs, int64_t T, int32_t H) {
+    int32_t n_seqs, int64_t T, int32_t H, int32_t single) {
   constexpr bool kStaged = sizeof(E) == 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStaged ? kRing * kStageBuf : 16];
   __shared__ __attribute__((aligned(16))) E sS[2 * 4 * kWave * 8];   // published state
@@ -749,7 +769,8 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   const int pair = (id & 7) + 8 * ((id >> 3) / 8);
   const int jt = (id >> 3) % 8;
   if (pair >= n_seqs * H) return;
-  if (status[0] != 0) return;
+  // one sequence (the full call skips the chunk map): check cu_seqlens here
+  if (single ? (cu != nullptr && (cu[0] != 0 || (int64_t)cu[1] != T)) : status[0] != 0) return;
   const int n = pair / H, h = pair % H;
   const int lane = threadIdx.x & 63;
   // wave 0: state, 1: output, 2 and 3: loaders
@@ -757,7 +778,8 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   const int g = lane >> 4;
   const int j = 16 * jt + (lane & 15);
   const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
-  const int b0 = chunk_offset[n], b1 = chunk_offset[n + 1];
+  const int b0 = single ? 0 : chunk_offset[n];
+  const int b1 = single ? (int)((T + kC - 1) / kC) : chunk_offset[n + 1];
   auto block_of = [&](int b) { return inter + ((int64_t)b * H + h) * Inter<E>::kBytes; };
   auto slot = [&](int b) { return lds + ((b - b0) % kRing) * kStageBuf; };
   auto publish = [&](const Frag<E> (&fs)[4], int b) {
@@ -998,7 +1020,10 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
                             int32_t* status, int32_t* chunk_offset, uint8_t* inter,
                             hipStream_t stream) {
   hipError_t err = hipSuccess;
-  if (phases & 1) {
+  // A full call on one sequence needs no chunk map: the two kernels derive
+  // the chunk range from T and check cu_seqlens themselves.
+  const int32_t single = phases == 7 && n_seqs == 1 && T > 0;
+  if ((phases & 1) && !single) {
     chunk_map_kernel<<<1, 256, 0, stream>>>(cu, n_seqs, T, n_slots, chunk_offset, status);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1008,7 +1033,7 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
 #define KDA_INTRA(E, NORM)                                                                  \
   intra_kernel<E, NORM><<<grid, kIntraThreads, 0, stream>>>(                                \
       (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, cu, chunk_offset, status, \
-      n_seqs, T, H, inter)
+      n_seqs, T, H, inter, single)
     if (bf16_io) {
       if (l2norm) KDA_INTRA(bf16, true); else KDA_INTRA(bf16, false);
     } else {
@@ -1023,10 +1048,10 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
   const int64_t nblocks = ((pairs + 7) / 8) * 8 * 8;   // 8 column tiles per pair
   if (bf16_io)
     carry_kernel<bf16><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
-        inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H);
+        inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single);
   else
     carry_kernel<float><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
-        inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H);
+        inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H, single);
   return hipGetLastError();
 }
 

@@ -351,6 +351,46 @@ def test_malformed_cu_seqlens_sets_status():
     assert bool((pre.o == 7.0).all())
 
 
+def test_malformed_single_sequence_cu_sets_status():
+    """One sequence: the full call runs without the chunk-map launch, so the
+    two kernels check cu_seqlens themselves; a wrong end offset still gives
+    status 1 and leaves o untouched."""
+    p = workloads.make_prefill([100], H=1, seed=41, io="bf16")
+    bf = torch.bfloat16
+    cu = dev(np.array([0, 95], np.int32), torch.int32)
+    pre = kda.Prefill(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha),
+                      dev(p.beta), None, cu)
+    pre.o.fill_(7.0)
+    pre.run()
+    torch.cuda.synchronize()
+    assert int(pre.workspace[:4].view(torch.int32)[0]) == 1
+    assert bool((pre.o == 7.0).all())
+
+
+@pytest.mark.parametrize("cu", [True, False])
+def test_single_sequence_phases_equal_full_call(cu):
+    """For one sequence the full call skips the chunk map; phase by phase
+    (which launches it) gives the same outputs, state and workspace words."""
+    p = workloads.make_prefill([333], H=3, seed=42, io="bf16", h0_std=0.05)
+    bf = torch.bfloat16
+    pre = kda.Prefill(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha),
+                      dev(p.beta), dev(p.h0), dev(p.cu_seqlens, torch.int32) if cu else None)
+    o1, h1 = (x.clone() for x in pre.run())
+    torch.cuda.synchronize()
+    words1 = pre.workspace[:512].clone()
+    pre.workspace[:512].fill_(0xEE)
+    for ph in range(3):
+        pre.run_phase(ph)
+    torch.cuda.synchronize()
+    assert torch.equal(pre.o, o1) and torch.equal(pre.h_final, h1)
+    w = pre.workspace[:512].view(torch.int32)
+    w1 = words1.view(torch.int32)
+    assert int(w[0]) == int(w1[0]) == 0                      # status
+    assert int(w[64]) == int(w1[64]) == 0                    # chunk_offset[0] at byte 256
+    assert int(w[65]) == int(w1[65]) == (333 + 63) // 64     # chunk_offset[1]
+    _check_prefill(p, host(o1), host(h1))
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_outputs_stay_inside_their_buffers(io):
     """Canaries around o and h_final survive a packed call with ragged tails."""
