@@ -222,3 +222,39 @@ def test_malformed_cu_seqlens_is_clamped():
     torch.cuda.synchronize()
     assert bool((o_buf[:pad] == 3.0).all()) and bool((o_buf[-pad:] == 3.0).all())
     assert torch.isfinite(hf).all()
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+@pytest.mark.parametrize("case", ["beta0", "alpha1", "kzero", "qzero"])
+def test_degenerate_cases(path, case):
+    """The method's special cases on both forward paths against the oracle
+    (pinned for them on the CPU): beta = 0 is pure per-channel decay,
+    alpha = 1 is DeltaNet, zero keys write nothing, zero queries read
+    exactly zero."""
+    p = workloads.make_prefill([70, 5, 64], H=2, seed=62, io="bf16", h0_std=0.05)
+    if case == "beta0":
+        p.beta[:] = 0.0
+    elif case == "alpha1":
+        p.log_alpha[:] = 0.0
+    elif case == "kzero":
+        p.k[:] = 0.0
+    else:
+        p.q[:] = 0.0
+    bf = torch.bfloat16
+    args = (dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta), dev(p.h0),
+            dev(p.cu_seqlens, torch.int32))
+    o, hf = (kda.chunk_fwd if path == "chunk" else kda.recurrent_fwd)(*args)
+    torch.cuda.synchronize()
+    o, hf = host(o), host(hf)
+    if case == "qzero":
+        assert not o.any()
+        _, rh = recurrent.forward(p.q, p.k, p.v, p.log_alpha, p.beta, p.h0, p.cu_seqlens)
+        assert rel_fro_err(hf, rh) <= TOL["bf16"][1]
+    else:
+        _check(p, o, hf)
+    if case in ("beta0", "kzero"):
+        # nothing is written along k: the final state is h0 decayed channel-wise
+        dec = np.stack([np.exp(p.log_alpha[p.cu_seqlens[n]:p.cu_seqlens[n + 1]]
+                               .astype(np.float64).sum(axis=0)) for n in range(3)])
+        want = dec[..., None] * p.h0.astype(np.float64)
+        assert rel_fro_err(hf, want) <= 1e-2
