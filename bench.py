@@ -17,8 +17,10 @@ kernel's own duration; ``kernels`` holds those and the decode kernel's, and
 ``extensions`` times the operator's optional paths, each on its own
 workload with its own roofline: the fused multi-token recurrent call
 (256 sequences x 32 heads x L = 4 and 64 new tokens), the decode step with a
-bf16 state, the prefill with in-kernel q/k L2Norm, and the RMSNorm x
-sigmoid-gate epilogue over the prefill's 8192 x 32 output rows.
+bf16 state, batch-1 decode (one sequence x 32 heads) launched step by step
+and replayed from a HIP graph, the prefill with in-kernel q/k L2Norm, and
+the RMSNorm x sigmoid-gate epilogue over the prefill's 8192 x 32 output
+rows.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -224,7 +226,7 @@ def _hbm(alg_bytes, us):
 
 def extensions(torch, d, pre_args, steps, warmup):
     """Timings of the optional paths (module docstring), inputs resident."""
-    from gated_delta_rule_50_amd import Prefill, Recurrent, rmsnorm_gate, workloads
+    from gated_delta_rule_50_amd import Prefill, Recurrent, decode_step, rmsnorm_gate, workloads
     bf = torch.bfloat16
     out = {}
     N, H = 256, 32
@@ -257,6 +259,37 @@ def extensions(torch, d, pre_args, steps, warmup):
         "us": us, "tokens_per_s": cfg4.n_seqs / (us * 1e-6), "alg_bytes": alg,
         "roofline": _hbm(alg, us)}
     del Sb, rec
+    # batch-1 decode (one sequence x 32 heads) is launch-bound: 64 steps
+    # launched one by one, and the same 64 steps replayed from a HIP graph
+    N1, steps1 = 1, 64
+    S1 = d(workloads.make_decode_state(N1, cfg4.H, cfg4.seed))
+    toks = []
+    for st in range(steps1):
+        t = workloads.make_decode_step(N1, cfg4.H, cfg4.seed, st, io=cfg4.io)
+        toks.append((d(t.q, bf), d(t.k, bf), d(t.v, bf), d(t.log_alpha), d(t.beta)))
+    o1 = torch.empty((N1, cfg4.H, D), dtype=bf, device="cuda")
+
+    def loop():
+        for t in toks:
+            decode_step(*t, S1, o=o1)
+    us_eager = _time_calls(torch, loop, steps, warmup) / steps1
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        loop()
+    us_graph = _time_calls(torch, graph.replay, steps, warmup) / steps1
+    alg = N1 * cfg4.H * DECODE_BYTES
+    out["decode_batch1"] = {
+        "workload": f"decode, 1 sequence x {cfg4.H} heads, fp32 state, {steps1} steps per "
+                    "launch sequence", "us_per_token_eager": us_eager,
+        "us_per_token_graph": us_graph, "tokens_per_s_graph": 1.0 / (us_graph * 1e-6),
+        "alg_bytes": alg, "roofline": _hbm(alg, us_graph)}
+    del S1, toks, graph
     pre_n = Prefill(*pre_args, qk_l2norm=True)
     us = _time_calls(torch, pre_n.run, steps, warmup)
     out["prefill_qk_l2norm"] = {
