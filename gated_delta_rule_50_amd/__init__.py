@@ -4,4 +4,5 @@
 ``workloads`` draws the seeded synthetic inputs.
 """
 from .kda import (KDAError, Prefill, Recurrent, alloc_workspace, chunk_fwd,  # noqa: F401
-                  chunk_fwd_workspace_bytes, decode_step, lib, recurrent_fwd, rmsnorm_gate)
+                  chunk_fwd_workspace_bytes, decode_step, forward, lib, recurrent_fwd,
+                  rmsnorm_gate)

@@ -288,3 +288,22 @@ def rmsnorm_gate(o, gate, weight=None, eps=1e-6, *, y=None, stream=None):
     if st != KDA_OK:
         raise KDAError(st, "kda_rmsnorm_gate")
     return y
+
+
+RECURRENT_MAX_LEN = 64
+
+
+def forward(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, max_seqlen, n_seqs=None,
+            qk_l2norm=False, o=None, h_final=None, stream=None):
+    """Mode switch of the "L2 Deep Distill" page's serving notes: sequences of
+    at most RECURRENT_MAX_LEN new tokens go through the fused recurrent
+    kernel, longer ones through the chunked prefill. max_seqlen is the longest sequence in the batch (the
+    caller knows it; cu_seqlens stays on the device). Same tensors as
+    chunk_fwd (fp32 states). Returns (o, h_final)."""
+    if max_seqlen <= RECURRENT_MAX_LEN:
+        return recurrent_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs=n_seqs,
+                             qk_l2norm=qk_l2norm, o=o, h_final=h_final, stream=stream)
+    if cu_seqlens is None and (n_seqs or 1) != 1:
+        raise ValueError("the chunked path needs cu_seqlens for more than one sequence")
+    return chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
+                     qk_l2norm=qk_l2norm, stream=stream)

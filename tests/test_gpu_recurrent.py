@@ -258,3 +258,16 @@ def test_degenerate_cases(path, case):
                                .astype(np.float64).sum(axis=0)) for n in range(3)])
         want = dec[..., None] * p.h0.astype(np.float64)
         assert rel_fro_err(hf, want) <= 1e-2
+
+
+@pytest.mark.parametrize("lens", [[64, 3, 40], [65, 200, 1]])
+def test_mode_switch_forward(lens):
+    """kda.forward picks the recurrent path for max length <= 64 and the
+    chunked one otherwise; both match the oracle."""
+    p = workloads.make_prefill(lens, H=2, seed=63, io="bf16", h0_std=0.05)
+    bf = torch.bfloat16
+    o, hf = kda.forward(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha),
+                        dev(p.beta), dev(p.h0), dev(p.cu_seqlens, torch.int32),
+                        max_seqlen=max(lens))
+    torch.cuda.synchronize()
+    _check(p, host(o), host(hf))
