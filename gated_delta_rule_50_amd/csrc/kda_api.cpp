@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/kda.h: argument validation,
 // workspace sizing and launch sequencing. No compute happens here; every
 // step of the operator runs in the HIP kernels.
+#include <initializer_list>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,6 +42,19 @@ bool overlap(const Range& a, const Range& b) {
 }
 
 bool valid_io(kda_io_dtype io) { return io == KDA_IO_F32 || io == KDA_IO_BF16; }
+
+// Tensor pointers the kernels read or write with 16-byte vectors must be
+// 16-byte aligned; NULL passes.
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if ((uintptr_t)p & 15u) return false;
+  return true;
+}
+bool aligned4(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if ((uintptr_t)p & 3u) return false;
+  return true;
+}
 
 int64_t io_bytes(kda_io_dtype io) { return io == KDA_IO_BF16 ? 2 : 4; }
 
@@ -92,6 +106,8 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
   if (cu_seqlens == nullptr && n_seqs != 1) return KDA_ERR_NULL;
   if (cu_seqlens != nullptr && T > INT32_MAX) return KDA_ERR_SHAPE;
   if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
+  if (!aligned16({q, k, v, log_alpha, h0, o, h_final}) || !aligned4({beta, cu_seqlens}))
+    return KDA_ERR_ALIGN;
   const size_t need = workspace_bytes(n_seqs, T, heads, io);
   if (need == 0) return KDA_ERR_SHAPE;
   if (!workspace || workspace_bytes_given < need || ((uintptr_t)workspace & 255u))
@@ -161,6 +177,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
   if (dk != kDim || dv != kDim || !valid_io(io)) return KDA_ERR_UNSUPPORTED;
   if (n_seqs == 0) return KDA_OK;
   if (!q || !k || !v || !log_alpha || !beta || !S_inout || !o) return KDA_ERR_NULL;
+  if (!aligned16({q, k, v, log_alpha, S_inout, o}) || !aligned4({beta})) return KDA_ERR_ALIGN;
   const int64_t pairs = (int64_t)n_seqs * heads;
   if (pairs > ((int64_t)1 << 29)) return KDA_ERR_SHAPE;  // grid of 4 waves per pair
   const int64_t eb = io_bytes(io);
@@ -195,6 +212,8 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v,
   const int64_t pairs = (int64_t)n_seqs * heads;
   if (pairs > ((int64_t)1 << 29)) return KDA_ERR_SHAPE;  // grid of 4 waves per pair
   if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
+  if (!aligned16({q, k, v, log_alpha, h0, o, h_final}) || !aligned4({beta, cu_seqlens}))
+    return KDA_ERR_ALIGN;
 
   const int64_t th = T * heads;
   const int64_t eb = io_bytes(io);
@@ -224,6 +243,7 @@ kda_status kda_rmsnorm_gate(const void* o, const void* gate, const float* weight
   if (rows == 0) return KDA_OK;
   if (rows > (int64_t)UINT32_MAX * 16) return KDA_ERR_SHAPE;
   if (!o || !gate || !y) return KDA_ERR_NULL;
+  if (!aligned16({o, gate, weight, y})) return KDA_ERR_ALIGN;
   const int64_t bytes = rows * kDim * io_bytes(io);
   const Range ro(o, bytes), rg(gate, bytes), rw(weight, kDim * 4), ry(y, bytes);
   if (overlap(ry, ro) && ry.lo != ro.lo) return KDA_ERR_ALIAS;
@@ -242,6 +262,7 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case KDA_ERR_ALIAS: return "an output overlaps an input it must not";
     case KDA_ERR_HIP: return "the HIP runtime reported a launch error";
+    case KDA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned (beta, cu_seqlens: 4)";
   }
   return "unknown status";
 }

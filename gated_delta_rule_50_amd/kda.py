@@ -14,7 +14,7 @@ import torch
 LIB_PATH = Path(__file__).resolve().parent / "libkda.so"
 
 KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_UNSUPPORTED = 0, 1, 2, 3
-KDA_ERR_WORKSPACE, KDA_ERR_ALIAS, KDA_ERR_HIP = 4, 5, 6
+KDA_ERR_WORKSPACE, KDA_ERR_ALIAS, KDA_ERR_HIP, KDA_ERR_ALIGN = 4, 5, 6, 7
 KDA_IO_F32, KDA_IO_BF16 = 0, 1
 KDA_STATE_F32, KDA_STATE_BF16 = 0, 1
 KDA_FLAG_QK_L2NORM = 1

@@ -26,6 +26,9 @@
  *    and launches nothing. A launch failure returns KDA_ERR_HIP. No C++
  *    exception crosses the ABI.
  *  - Only d_k = d_v = 128 is supported (the pages' head size).
+ *  - Tensor pointers are 16-byte aligned (beta and cu_seqlens: 4-byte), as
+ *    every torch allocation is; the kernels move 16-byte vectors. A
+ *    misaligned pointer returns KDA_ERR_ALIGN and launches nothing.
  *  - Tensor layouts are dense row-major with the last index fastest:
  *      q, k       [T, H, d_k]   I/O dtype
  *      v, o       [T, H, d_v]   I/O dtype
@@ -65,7 +68,8 @@ typedef enum {
   KDA_ERR_UNSUPPORTED = 3, /* d_k or d_v != 128, or unknown dtype          */
   KDA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned   */
   KDA_ERR_ALIAS = 5,       /* an output overlaps an input it must not      */
-  KDA_ERR_HIP = 6          /* the HIP runtime reported a launch error      */
+  KDA_ERR_HIP = 6,         /* the HIP runtime reported a launch error      */
+  KDA_ERR_ALIGN = 7        /* a tensor pointer is misaligned (see above)   */
 } kda_status;
 
 typedef enum {

@@ -14,7 +14,7 @@ ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "kda.h"
 LIB = ROOT / "gated_delta_rule_50_amd" / "libkda.so"
 
-OK, NULL, SHAPE, UNSUP, WS, ALIAS, HIPERR = range(7)
+OK, NULL, SHAPE, UNSUP, WS, ALIAS, HIPERR, ALIGN = range(8)
 F32, BF16 = 0, 1
 
 
@@ -69,7 +69,7 @@ def test_binding_names_match_header():
 
 
 def test_status_strings_and_version(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
     assert lib.kda_version() >= 200
@@ -151,6 +151,27 @@ def test_prefill_argument_errors(lib, over, expect):
     a = prefill_args(lib)
     a.update(over)
     assert call_prefill(lib, a) == expect
+
+
+@pytest.mark.parametrize("name,off", [("q", 8), ("k", 2), ("v", 4), ("log_alpha", 4),
+                                      ("h0", 8), ("o", 8), ("h_final", 4), ("beta", 2)])
+def test_prefill_misaligned_pointer(lib, name, off):
+    a = prefill_args(lib)
+    assert call_prefill(lib, dict(a, **{name: a[name] + off})) == ALIGN
+    assert call_prefill(lib, dict(a, N=2, cu=BASE + 6 * 64 * MB + 2)) == ALIGN
+
+
+def test_alignment_checked_on_every_entry_point(lib):
+    assert call_decode(lib, q=BASE + 8) == ALIGN
+    assert call_decode(lib, S=BASE + 64 * MB + 4) == ALIGN
+    assert call_decode(lib, beta=BASE + 4 * MB + 2) == ALIGN
+    assert call_recurrent(lib, h0=BASE + 64 * MB + 8) == ALIGN
+    assert call_recurrent(lib, cu=BASE + 6 * MB + 1) == ALIGN
+    assert call_recurrent(lib, o=BASE + 5 * MB + 8) == ALIGN
+    assert call_epilogue(lib, w=BASE + 2 * MB + 4) == ALIGN
+    assert call_epilogue(lib, y=BASE + 3 * MB + 8) == ALIGN
+    # 16-byte multiples pass the check (and then fail on the alias test)
+    assert call_epilogue(lib, y=BASE + 16) == ALIAS
 
 
 def test_prefill_alias_errors(lib):
@@ -235,8 +256,8 @@ def test_recurrent_state_size_follows_state_dtype(lib):
     # 4 x 2 states are 512 KiB in fp32 and 256 KiB in bf16; o starting just
     # before either end overlaps (calls that pass every check would launch, so
     # only rejected calls appear here)
-    assert call_recurrent(lib, st=F32, hf=None, o=BASE + 64 * MB + 512 * 1024 - 8) == ALIAS
-    assert call_recurrent(lib, st=BF16, hf=None, o=BASE + 64 * MB + 256 * 1024 - 8) == ALIAS
+    assert call_recurrent(lib, st=F32, hf=None, o=BASE + 64 * MB + 512 * 1024 - 16) == ALIAS
+    assert call_recurrent(lib, st=BF16, hf=None, o=BASE + 64 * MB + 256 * 1024 - 16) == ALIAS
 
 
 def test_recurrent_empty_batch_is_a_noop(lib):
