@@ -22,7 +22,10 @@ and replayed from a HIP graph, the prefill with in-kernel q/k L2Norm, and
 the RMSNorm x sigmoid-gate epilogue over the prefill's 8192 x 32 output
 rows.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+``--long-configs`` adds the prefill on the long single sequence
+(T = 131072) and on the 16-sequence packed batch.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--long-configs]
 """
 from __future__ import annotations
 
@@ -79,6 +82,9 @@ def _parse():
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--no-extensions", action="store_true",
                     help="skip the timings of the optional paths (shorter counter runs)")
+    ap.add_argument("--long-configs", action="store_true",
+                    help="also time the prefill on the long single sequence (T = 131072) and "
+                         "the 16-sequence packed batch (about a minute of input generation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy first (counter scale factor)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -307,6 +313,32 @@ def extensions(torch, d, pre_args, steps, warmup):
     return out
 
 
+def long_configs(torch, d, steps, warmup):
+    """Prefill throughput on the long-context and packed variable-length
+    workloads (parity cases of their own, timed here for their scaling)."""
+    from gated_delta_rule_50_amd import Prefill, workloads
+    bf = torch.bfloat16
+    out = {}
+    for cid, name in ((2, "long_T131072"), (3, "packed_16_sequences")):
+        p = workloads.config(cid).prefill()
+        lens = np.diff(p.cu_seqlens)
+        pre = Prefill(d(p.q, bf), d(p.k, bf), d(p.v, bf), d(p.log_alpha), d(p.beta),
+                      None if p.h0 is None else d(p.h0), d(p.cu_seqlens, torch.int32))
+        T, H, N = p.T, p.H, p.N
+        del p
+        us = _time_calls(torch, pre.run, max(2, steps // 4), max(1, warmup // 2))
+        alg = T * H * PREFILL_BYTES + 2 * N * H * STATE_BYTES
+        out[name] = {
+            "workload": f"{N} sequence(s), lengths {int(lens.min())}..{int(lens.max())}, "
+                        f"T={T}, H={H}, bf16 q/k/v, h0 ~N(0,0.02)",
+            "us": us, "tokens_per_s": T / (us * 1e-6), "alg_bytes": alg,
+            "longest_chain_chunks": int((lens.max() + C - 1) // C),
+            "roofline": _hbm(alg, us)}
+        del pre
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = _parse()
     if args.summarize_pmc:
@@ -461,6 +493,8 @@ def main():
     }
     if not args.no_extensions:
         out["extensions"] = extensions(torch, d, pre_args, args.steps, args.warmup)
+    if args.long_configs:
+        out["long_configs"] = long_configs(torch, d, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out))
