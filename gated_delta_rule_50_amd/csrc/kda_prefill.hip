@@ -590,7 +590,8 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
 
 // ------------------------------------------------------- sequential carry
 // One workgroup per (sequence, head, 16-column tile of the state), four
-// waves. Per chunk:
+// waves (or per two tiles when there are many pairs; see carry_kernel).
+// Per chunk:
 //   state wave    X = U + [-W] S            pseudo-value (rows = token)
 //                 S = Diag(gamma_C) S + K'^T X
 //   output wave   O^T = Ut^T + S^T Qt^T     (rows = value column)
@@ -610,11 +611,13 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
 // this tile's U and gamma_C in flight (buffer->LDS DMA into a three-slot
 // ring, each loader below the hardware's outstanding-load limit); the state
 // wave reads chunk b+1's fragments into a second register set while it
-// computes chunk b, so chunk b's slot is free for chunk b+3 during chunk b; the output wave loads its Qt fragments and Ut^T from
-// global memory two chunks ahead. fp32 intermediates (fp32 I/O only) are
+// computes chunk b, so chunk b's slot is free for chunk b+3 during chunk b;
+// the output wave loads its Qt fragments and Ut^T from global memory two
+// chunks ahead. fp32 intermediates (fp32 I/O only) are
 // read from global memory by both compute waves without prefetch.
 constexpr int kRing = 3;
 constexpr int kCarryThreads = 256;
+constexpr int64_t kCarryRound = 256;   // carry workgroups resident at once (one per CU)
 constexpr int kTouchAhead = 6;   // chunks between the L2 touch and the use of a block
 
 // Workgroup barrier without a memory fence: no wave waits on another's
@@ -699,30 +702,35 @@ __device__ __forceinline__ void carry_state(floatx4 (&S)[8], Frag<E> (&fs)[4],
     for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
 }
 
-// Output wave operands of one chunk: Qt fragments and this tile's Ut^T.
-template <class E>
+// Output wave operands of one chunk: Qt fragments and the Ut^T of the
+// workgroup's kTiles column tiles.
+template <class E, int kTiles>
 struct OutOps {
   Frag<E> fq[4][4];
-  Frag16<E> ut[4];   // kept in the I/O type until used: no wait at load time
+  Frag16<E> ut[kTiles][4];   // kept in the I/O type until used: no wait at load time
 };
-template <class E>
-__device__ __forceinline__ void load_out_ops(OutOps<E>& p, const E* blk, int jt, int lane) {
+template <class E, int kTiles>
+__device__ __forceinline__ void load_out_ops(OutOps<E, kTiles>& p, const E* blk, int jt0,
+                                             int lane) {
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
       load_frag(blk + Inter<E>::kXA + ((4 + nt) * 4 + kb) * kWave * 8, lane, p.fq[nt][kb]);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-    p.ut[nt] = ld16(blk + Inter<E>::kUC + ((jt * 8 + 4 + nt) * kWave + lane) * 4);
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      p.ut[t][nt] = ld16(blk + Inter<E>::kUC + (((jt0 + t) * 8 + 4 + nt) * kWave + lane) * 4);
 }
 
-// Output wave, one chunk: O^T = Ut^T + S^T Qt^T; lane (i = 16 nt + r,
-// j = j0 + 4 g .. +3) holds four consecutive outputs of one token. They go
-// to LDS in the I/O type; the state wave stores them to global memory.
-template <class E>
-__device__ __forceinline__ void carry_out(const OutOps<E>& p, const Frag<E> (&fs)[4],
-                                          E* sOb, int lane) {
+// Output wave, one chunk and column tile t: O^T = Ut^T + S^T Qt^T; lane
+// (i = 16 nt + r, j = j0 + 4 g .. +3) holds four consecutive outputs of one
+// token. They go to LDS in the I/O type; the tile's state wave stores them
+// to global memory.
+template <class E, int kTiles>
+__device__ __forceinline__ void carry_out(const OutOps<E, kTiles>& p, int t,
+                                          const Frag<E> (&fs)[4], E* sOb, int lane) {
   floatx4 X[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) X[nt] = zero4();
@@ -736,13 +744,13 @@ __device__ __forceinline__ void carry_out(const OutOps<E>& p, const Frag<E> (&fs
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) X[nt][e] += p.ut[nt].get(e);
+    for (int e = 0; e < 4; ++e) X[nt][e] += p.ut[t][nt].get(e);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) st16(sOb + (nt * kWave + lane) * 4, frag16<E>(X[nt]));
 }
 
 // Stores one chunk's O tile (16 columns) from LDS for the valid tokens.
-// Only the state wave issues global stores: it never waits on global loads,
+// Only the state waves issue global stores: they never wait on global loads,
 // so the stores' completion never stalls a load wait (on this architecture
 // one counter tracks both).
 template <class E>
@@ -756,63 +764,80 @@ __device__ __forceinline__ void store_out(const Frag16<E> (&x)[4], E* __restrict
     if (16 * nt + (lane & 15) < len) st16(base + nt * step16, x[nt]);
 }
 
-template <class E>
+// One workgroup per (sequence, head, group of kTiles column tiles).
+//   kTiles = 1: waves 0 state, 1 output, 2 and 3 loaders (2 moves [-W] and
+//               U, 3 moves K'^T and gamma_C and touches L2);
+//   kTiles = 2: waves 0 and 1 state (one tile each, sharing the staged
+//               [-W] and K'^T), 2 output (both tiles), 3 the only loader.
+// Two tiles per workgroup halve the L2 traffic per column tile at the cost
+// of a longer chain per chunk; they pay when there are more (sequence,
+// head) pairs than one round of one-tile workgroups fills.
+template <class E, int kTiles>
 __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     const uint8_t* inter,   // not restrict: prefetch loads stay ahead of the barriers
     const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
     const float* __restrict__ h0, float* __restrict__ h_final, E* __restrict__ o,
     int32_t n_seqs, int64_t T, int32_t H, int32_t single) {
+  static_assert(kTiles == 1 || kTiles == 2, "one or two column tiles per workgroup");
   constexpr bool kStaged = sizeof(E) == 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStaged ? kRing * kStageBuf : 16];
-  __shared__ __attribute__((aligned(16))) E sS[2 * 4 * kWave * 8];   // published state
-  __shared__ __attribute__((aligned(16))) int32_t sTouch[kWave];        // L2 touch sink
-  __shared__ __attribute__((aligned(16))) E sO[2 * 4 * kWave * 4];      // output tiles
+  static_assert(kStaged || kTiles == 1, "fp32 intermediates: one tile per workgroup");
+  constexpr int kGroups = 8 / kTiles;                 // workgroups per (sequence, head)
+  constexpr int kUOff = kStageW + kStageKT;           // slot offset of the U tiles
+  constexpr int kGOff = kUOff + kTiles * kStageU;     // slot offset of gamma_C
+  constexpr int kBuf = kGOff + 1024;
+  constexpr int kSBuf = 4 * kWave * 8;                // one published state
+  constexpr int kOBuf = 4 * kWave * 4;                // one O tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStaged ? kRing * kBuf : 16];
+  __shared__ __attribute__((aligned(16))) E sS[kTiles * 2 * kSBuf];   // published states
+  __shared__ __attribute__((aligned(16))) int32_t sTouch[kWave];       // L2 touch sink
+  __shared__ __attribute__((aligned(16))) E sO[kTiles * 2 * kOBuf];   // output tiles
 
   // XCD-aware order: consecutive ids go round-robin over the 8 XCDs; give the
-  // 8 tiles of one (sequence, head) the same id % 8 so they share an L2.
+  // workgroups of one (sequence, head) the same id % 8 so they share an L2.
   const int id = blockIdx.x;
-  const int pair = (id & 7) + 8 * ((id >> 3) / 8);
-  const int jt = (id >> 3) % 8;
+  const int pair = (id & 7) + 8 * ((id >> 3) / kGroups);
+  const int jg = (id >> 3) % kGroups;
   if (pair >= n_seqs * H) return;
   // one sequence (the full call skips the chunk map): check cu_seqlens here
   if (single ? (cu != nullptr && (cu[0] != 0 || (int64_t)cu[1] != T)) : status[0] != 0) return;
   const int n = pair / H, h = pair % H;
   const int lane = threadIdx.x & 63;
-  // wave 0: state, 1: output, 2 and 3: loaders
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
-  const int j = 16 * jt + (lane & 15);
   const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
   const int b0 = single ? 0 : chunk_offset[n];
   const int b1 = single ? (int)((T + kC - 1) / kC) : chunk_offset[n + 1];
   auto block_of = [&](int b) { return inter + ((int64_t)b * H + h) * Inter<E>::kBytes; };
-  auto slot = [&](int b) { return lds + ((b - b0) % kRing) * kStageBuf; };
-  auto publish = [&](const Frag<E> (&fs)[4], int b) {
-    E* dst = sS + ((b - b0) & 1) * 4 * kWave * 8;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) store8(dst + (kb * kWave + lane) * 8, fs[kb]);
-  };
+  auto slot = [&](int b) { return lds + ((b - b0) % kRing) * kBuf; };
 
-  // loader w = 2 moves [-W] and U, w = 3 moves K'^T and gamma_C
+  // loader roles: kTiles = 1 splits a chunk's transfers over waves 2 and 3
+  const bool moves_w = kTiles == 1 ? w == 2 : w == 3;     // [-W] and U
+  const bool moves_kt = w == 3;                           // K'^T, gamma_C, touches
   auto issue = [&](int b) {
     const uint8_t* src = block_of(b);
     uint8_t* dst = slot(b);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)src, 0, (int)Inter<E>::kBytes, 0x00020000);
-    if (w == 2) {
+    if (moves_w) {
 #pragma unroll
       for (int i = 0; i < kStageW / 1024; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, lane * 16,
             (int)(Inter<E>::kXA * sizeof(E)) + i * 1024, 0, 0);
-      const int uc = (int)(Inter<E>::kUC * sizeof(E)) + jt * 8 * kWave * 4 * 2;
+      // U of the group's tiles (tile jt's U is the first half of its 4 KiB
+      // in the block; Ut^T follows it)
 #pragma unroll
-      for (int i = 0; i < kStageU / 1024; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + kStageW + kStageKT + i * 1024),
-            16, lane * 16, uc + i * 1024, 0, 0);
-    } else {
+      for (int t = 0; t < kTiles; ++t) {
+        const int uc = (int)(Inter<E>::kUC * sizeof(E)) + (jg * kTiles + t) * 8 * kWave * 4 * 2;
+#pragma unroll
+        for (int i = 0; i < kStageU / 1024; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(dst + kUOff + t * kStageU + i * 1024),
+              16, lane * 16, uc + i * 1024, 0, 0);
+      }
+    }
+    if (moves_kt) {
 #pragma unroll
       for (int i = 0; i < kStageKT / 1024; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -820,66 +845,78 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
             lane * 16, (int)(Inter<E>::kKT * sizeof(E)) + i * 1024, 0, 0);
       // gamma_C: 512 bytes; lanes >= 32 read past the block and get zeros
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(dst + kStageW + kStageKT + kStageU),
+          rs, (__attribute__((address_space(3))) void*)(dst + kGOff),
           16, lane * 16, (int)Inter<E>::kGCByte, 0, 0);
     }
   };
-  // L2 touch of chunk b by loader 1: one word per 128-byte line of lines
-  // [jt * kShare, (jt + 1) * kShare) of the block
+  // DMA instructions per chunk of each loader
+  constexpr int kDMAw = kTiles == 1 ? (kStageW + kStageU) / 1024
+                                    : (kStageW + kStageKT + kTiles * kStageU) / 1024 + 1;
+  constexpr int kDMAkt = kTiles == 1 ? kStageKT / 1024 + 1 : kDMAw;
+  // L2 touch of chunk b by wave 3: one word per 128-byte line of lines
+  // [jg * kShare, (jg + 1) * kShare) of the block
   constexpr int kLines = (int)((Inter<E>::kBytes + 127) / 128);
-  constexpr int kShare = (kLines + 7) / 8;
+  constexpr int kShare = (kLines + kGroups - 1) / kGroups;
   constexpr int kTouchOps = (kShare + kWave - 1) / kWave;
   auto touch = [&](int b) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)block_of(b), 0, (int)Inter<E>::kBytes, 0x00020000);
 #pragma unroll
     for (int u = 0; u < kTouchOps; ++u) {
-      const int line = min(jt * kShare + u * kWave + lane, kLines - 1);
+      const int line = min(jg * kShare + u * kWave + lane, kLines - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)sTouch, 4, line * 128, 0, 0, 0);
     }
   };
-  // Iteration b: after issuing chunk b+3 (dma) and touching chunk b+6
-  // (tch), wait until chunk b+2 has landed. The memory counter retires in
-  // order, so the wait allows exactly the instructions issued after chunk
-  // b+2's: the previous iteration's touch (prev), this iteration's DMA and
-  // touch. Fewer allowed instructions only wait longer.
+  // kTiles = 1, iteration b: after issuing chunk b+3 (dma) and touching
+  // chunk b+6 (tch), wait until chunk b+2 has landed. The memory counter
+  // retires in order, so the wait allows exactly the instructions issued
+  // after chunk b+2's: the previous iteration's touch (prev), this
+  // iteration's DMA and touch. Fewer allowed instructions only wait longer.
   auto loader_wait = [&](bool dma, bool tch, bool prev) {
     if (!dma) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else if (w == 2) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMA0) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMAw) : "memory");
     } else if (tch) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMA1 + 2 * kTouchOps) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMAkt + 2 * kTouchOps) : "memory");
     } else if (prev) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMA1 + kTouchOps) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMAkt + kTouchOps) : "memory");
     } else {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMA1) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDMAkt) : "memory");
     }
   };
 
-  // state operand sources of chunk b: the LDS ring (bf16) or the block (fp32)
-  auto w_src = [&](int b) -> const E* {
-    if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b));
-    else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kXA;
-  };
-  auto kt_src = [&](int b) -> const E* {
-    if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b) + kStageW);
-    else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kKT;
-  };
-  auto u_src = [&](int b) -> const E* {
-    if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b) + kStageW + kStageKT);
-    else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kUC + jt * 8 * kWave * 4;
-  };
-  auto gc_src = [&](int b) -> const float* {
-    if constexpr (kStaged)
-      return reinterpret_cast<const float*>(slot(b) + kStageW + kStageKT + kStageU);
-    else return reinterpret_cast<const float*>(block_of(b) + Inter<E>::kGCByte);
-  };
-
-  // Each role runs its own loop; all execute one barrier before the first
+  // Each role runs its own loop; all execute two barriers before the first
   // chunk and one per chunk.
-  if (w == 0) {
+  if (w < kTiles) {
+    // state wave of column tile jt
+    const int jt = jg * kTiles + w;
+    const int j = 16 * jt + (lane & 15);
+    E* const sSw = sS + w * 2 * kSBuf;
+    const E* const sOw = sO + w * 2 * kOBuf;
+    auto publish = [&](const Frag<E> (&fs)[4], int b) {
+      E* dst = sSw + ((b - b0) & 1) * kSBuf;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) store8(dst + (kb * kWave + lane) * 8, fs[kb]);
+    };
+    // operand sources of chunk b: the LDS ring (bf16) or the block (fp32)
+    auto w_src = [&](int b) -> const E* {
+      if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b));
+      else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kXA;
+    };
+    auto kt_src = [&](int b) -> const E* {
+      if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b) + kStageW);
+      else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kKT;
+    };
+    auto u_src = [&](int b) -> const E* {
+      if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b) + kUOff + w * kStageU);
+      else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kUC + jt * 8 * kWave * 4;
+    };
+    auto gc_src = [&](int b) -> const float* {
+      if constexpr (kStaged) return reinterpret_cast<const float*>(slot(b) + kGOff);
+      else return reinterpret_cast<const float*>(block_of(b) + Inter<E>::kGCByte);
+    };
     floatx4 S[8];
     Frag<E> fs[4];
     const float* h0p = h0 ? h0 + (int64_t)pair * kD * kD : nullptr;
@@ -905,7 +942,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     ring_barrier();
     // O of chunk b, written to LDS by the output wave
     auto read_out = [&](Frag16<E> (&x)[4], int b) {
-      const E* src = sO + ((b - b0) & 1) * 4 * kWave * 4;
+      const E* src = sOw + ((b - b0) & 1) * kOBuf;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) x[nt] = ld16(src + (nt * kWave + lane) * 4);
     };
@@ -957,23 +994,29 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
     }
-  } else if (w == 1) {
-    auto step = [&](int b, OutOps<E>& out) {
-      Frag<E> fsb[4];
-      const E* src = sS + ((b - b0) & 1) * 4 * kWave * 8;
+  } else if (w == kTiles) {
+    // output wave of the group's tiles
+    auto step = [&](int b, OutOps<E, kTiles>& out) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) lds_frag(src + (kb * kWave + lane) * 8, fsb[kb]);
-      carry_out<E>(out, fsb, sO + ((b - b0) & 1) * 4 * kWave * 4, lane);
+      for (int t = 0; t < kTiles; ++t) {
+        Frag<E> fsb[4];
+        const E* src = sS + (t * 2 + ((b - b0) & 1)) * kSBuf;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) lds_frag(src + (kb * kWave + lane) * 8, fsb[kb]);
+        carry_out<E, kTiles>(out, t, fsb, sO + (t * 2 + ((b - b0) & 1)) * kOBuf, lane);
+      }
       // unconditional (clamped) so every path issues the same loads and the
       // compiler's counter waits stay exact
-      load_out_ops(out, reinterpret_cast<const E*>(block_of(min(b + 2, b1 - 1))), jt, lane);
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // O tile written
+      load_out_ops(out, reinterpret_cast<const E*>(block_of(min(b + 2, b1 - 1))), jg * kTiles,
+                   lane);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // O tiles written
       ring_barrier();
     };
     if (b0 < b1) {
-      OutOps<E> oa, ob;   // alternating chunks, loaded two chunks ahead
-      load_out_ops(oa, reinterpret_cast<const E*>(block_of(b0)), jt, lane);
-      load_out_ops(ob, reinterpret_cast<const E*>(block_of(min(b0 + 1, b1 - 1))), jt, lane);
+      OutOps<E, kTiles> oa, ob;   // alternating chunks, loaded two chunks ahead
+      load_out_ops(oa, reinterpret_cast<const E*>(block_of(b0)), jg * kTiles, lane);
+      load_out_ops(ob, reinterpret_cast<const E*>(block_of(min(b0 + 1, b1 - 1))), jg * kTiles,
+                   lane);
       ring_barrier();
       ring_barrier();
       // pairs of chunks, then the odd one: every loop back edge follows both
@@ -988,7 +1031,8 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       ring_barrier();
       ring_barrier();
     }
-  } else {
+  } else if (kTiles == 1) {
+    // two loaders
     if (kStaged) {
       for (int b = b0; b < b0 + 3 && b < b1; ++b) issue(b);
       loader_wait(b0 + 2 < b1, false, false);   // chunks b0, b0 + 1 landed
@@ -1006,6 +1050,30 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
         if (tch) touch(b + kTouchAhead);
         loader_wait(dma, tch, prev);
       }
+      ring_barrier();
+    }
+  } else {
+    // one loader, kDMAw = 37 transfers per chunk: at most one chunk's
+    // transfers are in flight (the counter holds 63), so iteration b first
+    // waits for chunk b+2, issued in iteration b-1 and followed there only
+    // by that iteration's touch, and then issues chunk b+3.
+    if (b0 < b1) {
+      issue(b0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (b0 + 1 < b1) issue(b0 + 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunks b0, b0 + 1 landed
+      if (b0 + 2 < b1) issue(b0 + 2);
+      for (int b = b0 + 3; b < b0 + kTouchAhead && b < b1; ++b) touch(b);
+    }
+    ring_barrier();
+    ring_barrier();
+    for (int b = b0; b < b1; ++b) {
+      if (b > b0 && b + kTouchAhead - 1 < b1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTouchOps) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (b + 3 < b1) issue(b + 3);
+      if (b + kTouchAhead < b1) touch(b + kTouchAhead);
       ring_barrier();
     }
   }
@@ -1051,12 +1119,21 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
   }
   if (!(phases & 4)) return hipSuccess;
   const int64_t pairs = (int64_t)n_seqs * H;
-  const int64_t nblocks = ((pairs + 7) / 8) * 8 * 8;   // 8 column tiles per pair
-  if (bf16_io)
-    carry_kernel<bf16><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+  // Two column tiles per workgroup once one-tile workgroups (eight per pair)
+  // would not all be resident at once (one per CU on the 256-CU MI355X): on
+  // the 16-sequence packed batch the carry drops from 2.70 to 2.02 ms; a
+  // single round of one-tile workgroups keeps the shorter chain (1.06 against
+  // 1.28 us per chunk on the 8K workload).
+  const bool two = bf16_io && pairs * 8 > kCarryRound;
+  const int64_t nblocks = ((pairs + 7) / 8) * 8 * (two ? 4 : 8);   // column-tile groups
+  if (two)
+    carry_kernel<bf16, 2><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+        inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single);
+  else if (bf16_io)
+    carry_kernel<bf16, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
         inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single);
   else
-    carry_kernel<float><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+    carry_kernel<float, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
         inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H, single);
   return hipGetLastError();
 }

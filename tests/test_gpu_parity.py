@@ -190,6 +190,53 @@ def test_phases_equal_full_call_and_deterministic():
     assert torch.equal(o3, o1) and torch.equal(h3, h1)
 
 
+# ------------------------------------------- many (sequence, head) pairs
+# Once the one-tile carry workgroups (eight per pair) outnumber the 256 CUs,
+# the carry runs two column tiles per workgroup; these batches take that
+# path (more than 32 pairs), with ragged, one-token and empty sequences.
+def _many_pairs_batch(seed, io="bf16"):
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(1, 200, size=18)] + [0, 1, 64, 129]
+    return workloads.make_prefill(lengths, H=2, seed=seed, io=io, h0_std=0.05)
+
+
+def test_two_tile_carry_matches_oracle():
+    p = _many_pairs_batch(60)
+    assert p.N * p.H * 8 > 256
+    o, hf = _run_prefill(p)
+    _check_prefill(p, o, hf)
+    rh = recurrent.forward(p.q, p.k, p.v, p.log_alpha, p.beta, p.h0, p.cu_seqlens)[1]
+    for n in range(p.N):   # every sequence's final state, the empty ones included
+        assert rel_fro_err(hf[n], rh[n]) <= TOL[p.io][1], n
+
+
+def test_two_tile_carry_equals_one_tile_bitwise():
+    """Each sequence of the batch run alone (two pairs: one tile per
+    workgroup) gives bit-identical outputs and final states: the two-tile
+    workgroup does the same arithmetic per tile."""
+    p = _many_pairs_batch(61)
+    bf = torch.bfloat16
+    o_all, hf_all = kda.chunk_fwd(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha),
+                                  dev(p.beta), dev(p.h0), dev(p.cu_seqlens, torch.int32))
+    torch.cuda.synchronize()
+    for n in range(p.N):
+        a, b = int(p.cu_seqlens[n]), int(p.cu_seqlens[n + 1])
+        o_n, hf_n = kda.chunk_fwd(dev(p.q[a:b], bf), dev(p.k[a:b], bf), dev(p.v[a:b], bf),
+                                  dev(p.log_alpha[a:b]), dev(p.beta[a:b]), dev(p.h0[n:n + 1]),
+                                  None)
+        torch.cuda.synchronize()
+        assert torch.equal(o_n, o_all[a:b]), n
+        assert torch.equal(hf_n[0], hf_all[n]), n
+
+
+def test_two_tile_carry_single_sequence_many_heads():
+    """One sequence with 40 heads (320 one-tile workgroups): the two-tile
+    path without the chunk map."""
+    p = workloads.make_prefill([333], H=40, seed=62, io="bf16", h0_std=0.05)
+    o, hf = _run_prefill(p)
+    _check_prefill(p, o, hf, heads=[0, 17, 39])
+
+
 # -------------------------------------------------- intermediates & layout
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_workspace_intermediates_match_chunkwise_oracle(io):
