@@ -105,6 +105,8 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
   if (flags & ~(uint32_t)KDA_FLAG_QK_L2NORM) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens == nullptr && n_seqs != 1) return KDA_ERR_NULL;
   if (cu_seqlens != nullptr && T > INT32_MAX) return KDA_ERR_SHAPE;
+  // the carry grid has up to eight workgroups per (sequence, head) pair
+  if ((int64_t)n_seqs * heads > ((int64_t)1 << 27)) return KDA_ERR_SHAPE;
   if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
   if (!aligned16({q, k, v, log_alpha, h0, o, h_final}) || !aligned4({beta, cu_seqlens}))
     return KDA_ERR_ALIGN;

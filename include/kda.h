@@ -122,7 +122,8 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
  *   nothing but h_final.
  *   Errors: KDA_ERR_NULL (q, k, v, log_alpha, beta or o NULL when T > 0;
  *   cu_seqlens NULL with n_seqs != 1), KDA_ERR_SHAPE (negative sizes,
- *   n_seqs < 1, heads < 1, T > INT32_MAX with cu_seqlens),
+ *   n_seqs < 1, heads < 1, T > INT32_MAX with cu_seqlens, more than 2^27
+ *   (sequence, head) pairs),
  *   KDA_ERR_UNSUPPORTED (d_k, d_v != 128, unknown dtype or flag bit,
  *   heads > 65535),
  *   KDA_ERR_WORKSPACE (NULL, smaller than required, not 256-byte aligned),

@@ -189,6 +189,12 @@ def test_prefill_invalid_phase(lib):
     assert call_prefill(lib, a, phase=-1) == SHAPE
 
 
+def test_prefill_pair_limit(lib):
+    # 2^20 sequences x 256 heads: more (sequence, head) pairs than the carry grid takes
+    a = prefill_args(lib, N=2)
+    assert call_prefill(lib, dict(a, N=1 << 20, H=256, T=1 << 20)) == SHAPE
+
+
 def test_prefill_large_T_needs_int32_cu(lib):
     a = prefill_args(lib, N=2)
     a["T"] = 1 << 31
