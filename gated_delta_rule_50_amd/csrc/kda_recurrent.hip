@@ -210,15 +210,20 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
       fetch_token(nxt, q, k, v, log_alpha, beta, tn * H + h, lane, col0 + cq);
     }
 
-    float q0 = (float)cur.q[0], q1 = (float)cur.q[1];
-    float k0 = (float)cur.k[0], k1 = (float)cur.k[1];
+    const float q0 = (float)cur.q[0], q1 = (float)cur.q[1];
+    const float k0 = (float)cur.k[0], k1 = (float)cur.k[1];
     const float a0 = exp_f(cur.la.x), a1 = exp_f(cur.la.y);
     float qk = wave_sum(q0 * k0 + q1 * k1);
+    // L2Norm: the raw q and k are staged and their scales applied to the
+    // column sums and to the correction instead (e = rk S~^T k,
+    // S~^T q^ = rq S~^T q, the update adds k (rk d)^T), so the two norm
+    // reductions run beside the products instead of ahead of the staging
+    float rk = 1.f, rq = 1.f;
     if constexpr (kNorm) {
       const float kk = wave_sum(k0 * k0 + k1 * k1);
       const float qq = wave_sum(q0 * q0 + q1 * q1);
-      const float rk = 1.f / sqrtf(kk + kL2NormEps), rq = 1.f / sqrtf(qq + kL2NormEps);
-      k0 *= rk; k1 *= rk; q0 *= rq; q1 *= rq;
+      rk = 1.f / sqrtf(kk + kL2NormEps);
+      rq = 1.f / sqrtf(qq + kL2NormEps);
       qk *= rk * rq;
     }
     __syncthreads();  // the previous token's reads of the rows are done
@@ -248,13 +253,13 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     // lane ends with e and pr of column cq = 2 bit4 + bit5 of its quad.
     const float e01 = sum_pair32(pe.x, pe.y), e23 = sum_pair32(pe.z, pe.w);
     const float p01 = sum_pair32(pr.x, pr.y), p23 = sum_pair32(pr.z, pr.w);
-    const float ec = sum_xor8(sum_pair16(e01, e23));
-    const float pc = sum_xor8(sum_pair16(p01, p23));
+    const float ec = rk * sum_xor8(sum_pair16(e01, e23));
+    const float pc = rq * sum_xor8(sum_pair16(p01, p23));
     // d = beta (v - e), the correction written along k; every lane then
-    // gathers the quad's four d values.
+    // gathers the quad's four d values (times rk: the staged k is raw).
     const float dc = cur.b * ((float)cur.v - ec);
     float d4[4], dlo, dhi;
-    gather32(dc, dlo, dhi);          // d of columns 2 bit4 and 2 bit4 + 1
+    gather32(rk * dc, dlo, dhi);     // d of columns 2 bit4 and 2 bit4 + 1
     gather16(dlo, d4[0], d4[2]);
     gather16(dhi, d4[1], d4[3]);
     const float4 d = {d4[0], d4[1], d4[2], d4[3]};
