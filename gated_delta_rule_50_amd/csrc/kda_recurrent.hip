@@ -222,8 +222,10 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     if constexpr (kNorm) {
       const float kk = wave_sum(k0 * k0 + k1 * k1);
       const float qq = wave_sum(q0 * q0 + q1 * q1);
-      rk = 1.f / sqrtf(kk + kL2NormEps);
-      rq = 1.f / sqrtf(qq + kL2NormEps);
+      // hardware reciprocal square root (about 1 ulp): a correctly rounded
+      // sqrt and division would cost ~50 instructions per token
+      rk = __builtin_amdgcn_rsqf(kk + kL2NormEps);
+      rq = __builtin_amdgcn_rsqf(qq + kL2NormEps);
       qk *= rk * rq;
     }
     __syncthreads();  // the previous token's reads of the rows are done
