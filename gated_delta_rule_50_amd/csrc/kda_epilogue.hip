@@ -65,10 +65,13 @@ __global__ __launch_bounds__(256) void rmsnorm_gate_kernel(const IO* o, const IO
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
   ss = dpp_sum16(ss);
-  const float r = 1.f / sqrtf(ss * (1.f / kD) + eps);
+  // hardware reciprocal and reciprocal square root (about 1 ulp each, far
+  // below the output's rounding): correctly rounded divisions would double
+  // the kernel's instruction count
+  const float r = __builtin_amdgcn_rsqf(ss * (1.f / kD) + eps);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float sg = 1.f / (1.f + exp_f(-gv[e]));
+    const float sg = __builtin_amdgcn_rcpf(1.f + exp_f(-gv[e]));
     x[e] = x[e] * r * wv[e] * sg;
   }
   store8_io(y + base, x);
