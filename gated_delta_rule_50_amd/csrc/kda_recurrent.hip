@@ -29,15 +29,15 @@
 // with one column's sums) and a gather of the four corrections, so a token
 // needs no workgroup barrier. The per-token vectors (alpha k, alpha q,
 // alpha, k) go through a wave-private LDS row so each lane can read its 16
-// rows with four 16-byte reads.
+// rows with four 16-byte reads. A decode step on bf16 states uses 64-column
+// slices instead (lane: 16 rows more, the four lanes of a quad reduce), so
+// each state row piece of a wave is a whole 128-byte line.
 #include "kda_device.h"
 
 namespace kda {
 
 namespace {
 
-constexpr int kSliceCols = 32;                 // value columns per wave
-constexpr int kSlices = kD / kSliceCols;       // waves per (sequence, head)
 constexpr int kRowPitch = 20;                  // LDS floats per 16-row group (bank spread)
 constexpr int kStaticLds = 4 * 8 * kRowPitch * 4;   // the four token-vector rows, bytes
 constexpr int kLdsPerCu = 160 * 1024;               // gfx950 LDS per CU
@@ -147,19 +147,27 @@ __device__ __forceinline__ void fetch_token(TokenIn<IO>& x, const IO* q, const I
 }  // namespace
 
 // kSingle: exactly one token per sequence (the decode step), no token loop.
-template <class IO, class ST, bool kNorm, bool kSingle>
+// kWide: 64-column slices (lane: column quad lane % 16, rows
+// 32 (lane / 16) .. +31), so a lane's bf16 state row piece and the wave's
+// row of the slice fill whole 128-byte lines; 32-column slices otherwise
+// (lane: quad lane % 8, rows 16 (lane / 8) .. +15).
+template <class IO, class ST, bool kNorm, bool kSingle, bool kWide>
 __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const ST* h0,
     const int32_t* __restrict__ cu, int64_t seq_len, int64_t T, int32_t H, int64_t pairs,
     IO* __restrict__ o, ST* h_final) {
-  // Block b runs on XCD b % 8 (round-robin dispatch); the four slices of a
+  constexpr int kCols = kWide ? 64 : 32;          // value columns per wave
+  constexpr int kSl = kD / kCols;                  // waves per (sequence, head)
+  constexpr int kQuads = kCols / 4;                // column quads per slice
+  constexpr int kRows = kD / (64 / kQuads);        // key rows per lane
+  // Block b runs on XCD b % 8 (round-robin dispatch); the slices of a
   // (sequence, head) pair get blocks on one XCD so the token vectors they
   // all read come from that XCD's L2.
   const int bid = blockIdx.x;
   const int rest = bid >> 3;
-  const int w = rest & (kSlices - 1);
-  const int64_t p = (int64_t)(rest >> 2) * 8 + (bid & 7);
+  const int w = rest & (kSl - 1);
+  const int64_t p = (int64_t)(rest / kSl) * 8 + (bid & 7);
   if (p >= pairs) return;
   const int64_t n = p / H;
   const int h = (int)(p - n * H);
@@ -177,9 +185,9 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
   }
 
   const int lane = threadIdx.x;
-  const int jq = lane & 7;        // column quad inside the slice
-  const int rl = lane >> 3;       // rows 16 rl .. 16 rl + 15
-  const int col0 = kSliceCols * w + 4 * jq;
+  const int jq = lane % kQuads;   // column quad inside the slice
+  const int rl = lane / kQuads;   // rows kRows rl .. kRows rl + kRows - 1
+  const int col0 = kCols * w + 4 * jq;
   // after the column sums this lane holds column cq of its quad
   const int cq = 2 * ((lane >> 4) & 1) + (lane >> 5);
 
@@ -187,15 +195,20 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
   __shared__ __align__(16) float s_ka[8 * kRowPitch], s_qa[8 * kRowPitch];
   __shared__ __align__(16) float s_a[8 * kRowPitch], s_k[8 * kRowPitch];
 
-  float4 s[16];
-  const int64_t sbase = p * (int64_t)(kD * kD) + (int64_t)(16 * rl) * kD + col0;
+  float4 s[kRows];
+  const int64_t sbase = p * (int64_t)(kD * kD) + (int64_t)(kRows * rl) * kD + col0;
   if (h0 != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = load_state4(h0 + sbase + i * kD);
+    for (int i = 0; i < kRows; ++i) s[i] = load_state4(h0 + sbase + i * kD);
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = float4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kRows; ++i) s[i] = float4{0.f, 0.f, 0.f, 0.f};
   }
+  // LDS float offset of the token-vector rows 4 m .. 4 m + 3 of this lane
+  auto row4 = [&](int m) {
+    const int r0 = kRows * rl + 4 * m;
+    return (r0 >> 4) * kRowPitch + (r0 & 15);
+  };
 
   const int widx = (lane >> 3) * kRowPitch + 2 * (lane & 7);  // channels 2 l, 2 l + 1
   TokenIn<IO> nxt;
@@ -235,12 +248,12 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     *reinterpret_cast<float2*>(s_k + widx) = float2{k0, k1};
     __syncthreads();
 
-    // Partial column sums over this lane's 16 rows: e = S~^T k, pr = S~^T q.
+    // Partial column sums over this lane's rows: e = S~^T k, pr = S~^T q.
     float4 pe = {0.f, 0.f, 0.f, 0.f}, pr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float4 ka = *reinterpret_cast<const float4*>(s_ka + rl * kRowPitch + 4 * m);
-      const float4 qa = *reinterpret_cast<const float4*>(s_qa + rl * kRowPitch + 4 * m);
+    for (int m = 0; m < kRows / 4; ++m) {
+      const float4 ka = *reinterpret_cast<const float4*>(s_ka + row4(m));
+      const float4 qa = *reinterpret_cast<const float4*>(s_qa + row4(m));
       const float kav[4] = {ka.x, ka.y, ka.z, ka.w};
       const float qav[4] = {qa.x, qa.y, qa.z, qa.w};
 #pragma unroll
@@ -250,13 +263,19 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
         pr.x += qav[r] * x.x; pr.y += qav[r] * x.y; pr.z += qav[r] * x.z; pr.w += qav[r] * x.w;
       }
     }
-    // Sums over the eight lanes of the quad (lane bits 3..5) as a
-    // reduce-scatter: every exchange pairs two of the lane's values, and the
-    // lane ends with e and pr of column cq = 2 bit4 + bit5 of its quad.
+    // Sums over the lanes of the quad (lane bits 3..5, or 4..5 for wide
+    // slices) as a reduce-scatter: every exchange pairs two of the lane's
+    // values, and the lane ends with e and pr of column cq = 2 bit4 + bit5
+    // of its quad.
     const float e01 = sum_pair32(pe.x, pe.y), e23 = sum_pair32(pe.z, pe.w);
     const float p01 = sum_pair32(pr.x, pr.y), p23 = sum_pair32(pr.z, pr.w);
-    const float ec = rk * sum_xor8(sum_pair16(e01, e23));
-    const float pc = rq * sum_xor8(sum_pair16(p01, p23));
+    float ec = sum_pair16(e01, e23), pc = sum_pair16(p01, p23);
+    if constexpr (!kWide) {
+      ec = sum_xor8(ec);
+      pc = sum_xor8(pc);
+    }
+    ec *= rk;
+    pc *= rq;
     // d = beta (v - e), the correction written along k; every lane then
     // gathers the quad's four d values (times rk: the staged k is raw).
     const float dc = cur.b * ((float)cur.v - ec);
@@ -267,9 +286,9 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     const float4 d = {d4[0], d4[1], d4[2], d4[3]};
 
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float4 a = *reinterpret_cast<const float4*>(s_a + rl * kRowPitch + 4 * m);
-      const float4 kv = *reinterpret_cast<const float4*>(s_k + rl * kRowPitch + 4 * m);
+    for (int m = 0; m < kRows / 4; ++m) {
+      const float4 a = *reinterpret_cast<const float4*>(s_a + row4(m));
+      const float4 kv = *reinterpret_cast<const float4*>(s_k + row4(m));
       const float av[4] = {a.x, a.y, a.z, a.w};
       const float kvv[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
@@ -282,12 +301,13 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
       }
     }
 
-    if ((lane & 8) == 0) o[(t * H + h) * kD + col0 + cq] = from_f<IO>(pc + qk * dc);
+    // narrow slices: lanes l and l ^ 8 hold the same column
+    if (kWide || (lane & 8) == 0) o[(t * H + h) * kD + col0 + cq] = from_f<IO>(pc + qk * dc);
   }
 
   if (h_final != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) store_state4(h_final + sbase + i * kD, s[i]);
+    for (int i = 0; i < kRows; ++i) store_state4(h_final + sbase + i * kD, s[i]);
   }
 }
 
@@ -297,14 +317,17 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
                                 int64_t seq_len, int64_t T, int32_t H, int64_t pairs,
                                 void* o, void* h_final, hipStream_t stream) {
   if (pairs == 0) return hipSuccess;
-  const int64_t blocks = (pairs + 7) / 8 * 8 * kSlices;
-  dim3 grid((unsigned)blocks), block(64);
   const bool single = cu == nullptr && seq_len == 1;
+  // bf16 states in a decode step: 64-column slices, whole-line state rows
+  const bool wide = single && bf16_state;
+  const int64_t blocks = (pairs + 7) / 8 * 8 * (wide ? 2 : 4);
+  dim3 grid((unsigned)blocks), block(64);
   // Resident workgroups per CU. With one or a few tokens per sequence the
   // kernel streams the states, and HBM serves that stream best with few
   // waves in flight per CU: on 256 x 32 states, capping residency by padding
   // each workgroup's LDS takes the fp32-state decode step from 200 to
-  // 175 us (5 per CU), the bf16-state one from 131 to 109 us (8 per CU),
+  // 175 us (5 per CU), the bf16-state one from 131 to 109 us (8 per CU;
+  // 96 us with the 64-column slices, 6 or 8 per CU),
   // L = 2 and 4 from 193 / 199 to 178 / 187 us (8 / 10 per CU). From about
   // 16 tokens on the token loop is VALU-bound and wants every wave it can
   // get, so no cap.
@@ -315,22 +338,22 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
   else if (avg_len <= 2) cap = 8;
   else if (avg_len <= 4) cap = 10;
   const size_t lds_pad = cap > 0 ? (size_t)(kLdsPerCu / cap - kStaticLds) : 0;
-#define KDA_REC_LAUNCH(IO, ST, NORM, ONE)                                                    \
-  recurrent_fwd_kernel<IO, ST, NORM, ONE><<<grid, block, lds_pad, stream>>>(                 \
+#define KDA_REC_LAUNCH(IO, ST, NORM, ONE, WIDE)                                              \
+  recurrent_fwd_kernel<IO, ST, NORM, ONE, WIDE><<<grid, block, lds_pad, stream>>>(           \
       (const IO*)q, (const IO*)k, (const IO*)v, log_alpha, beta, (const ST*)h0, cu, seq_len, \
       T, H, pairs, (IO*)o, (ST*)h_final)
-#define KDA_REC_NORM(IO, ST)                                   \
+#define KDA_REC_NORM(IO, ST, WIDE)                             \
   if (l2norm) {                                                \
-    if (single) KDA_REC_LAUNCH(IO, ST, true, true);            \
-    else KDA_REC_LAUNCH(IO, ST, true, false);                  \
+    if (single) KDA_REC_LAUNCH(IO, ST, true, true, WIDE);      \
+    else KDA_REC_LAUNCH(IO, ST, true, false, false);           \
   } else {                                                     \
-    if (single) KDA_REC_LAUNCH(IO, ST, false, true);           \
-    else KDA_REC_LAUNCH(IO, ST, false, false);                 \
+    if (single) KDA_REC_LAUNCH(IO, ST, false, true, WIDE);     \
+    else KDA_REC_LAUNCH(IO, ST, false, false, false);          \
   }
   if (bf16_io) {
-    if (bf16_state) { KDA_REC_NORM(bf16, bf16); } else { KDA_REC_NORM(bf16, float); }
+    if (bf16_state) { KDA_REC_NORM(bf16, bf16, true); } else { KDA_REC_NORM(bf16, float, false); }
   } else {
-    if (bf16_state) { KDA_REC_NORM(float, bf16); } else { KDA_REC_NORM(float, float); }
+    if (bf16_state) { KDA_REC_NORM(float, bf16, true); } else { KDA_REC_NORM(float, float, false); }
   }
 #undef KDA_REC_NORM
 #undef KDA_REC_LAUNCH
