@@ -176,6 +176,31 @@ def test_one_token_equals_decode_step(io):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N,H", [(5, 3), (1, 1), (16, 8)])
+def test_one_token_bf16_state(io, N, H):
+    """A decode step on bf16 states (the 64-column-slice instance): against
+    the oracle from the bf16-rounded states, with padded pair counts, and
+    inside its output buffers."""
+    S0 = workloads.round_bf16(workloads.make_decode_state(N, H, seed=64, std=0.05))
+    d = workloads.make_decode_step(N, H, seed=64, step=0, io=io)
+    dt, bf = io_dtype(io), torch.bfloat16
+    pad = 4096
+    s_buf = torch.full((N * H * 128 * 128 + 2 * pad,), 5.0, dtype=bf, device="cuda")
+    o_buf = torch.full((N * H * 128 + 2 * pad,), 3.0, dtype=dt, device="cuda")
+    S = s_buf[pad:pad + N * H * 128 * 128].view(N, H, 128, 128)
+    S.copy_(dev(S0, bf))
+    o = o_buf[pad:pad + N * H * 128].view(N, H, 128)
+    kda.recurrent_fwd(dev(d.q, dt), dev(d.k, dt), dev(d.v, dt), dev(d.log_alpha),
+                      dev(d.beta), S, n_seqs=N, state_dtype=bf, o=o, h_final=S)
+    torch.cuda.synchronize()
+    assert bool((s_buf[:pad] == 5.0).all()) and bool((s_buf[-pad:] == 5.0).all())
+    assert bool((o_buf[:pad] == 3.0).all()) and bool((o_buf[-pad:] == 3.0).all())
+    ro, rs = recurrent.decode_step(d.q, d.k, d.v, d.log_alpha, d.beta, S0)
+    assert rel_max_err(host(o), ro) <= TOL[io][0]
+    assert rel_fro_err(host(S), rs) <= 1e-2
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_exact_recall(io):
     """|k| = 1, beta = 1, q = k: each token reads back its own value."""
     p = workloads.make_prefill([50, 14], H=2, seed=59, io=io, h0_std=0.05)
