@@ -596,10 +596,11 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
 //                 S = Diag(gamma_C) S + K'^T X
 //   output wave   O^T = Ut^T + S^T Qt^T     (rows = value column)
 //   loader waves  stream the state wave's operands into an LDS ring
-// Loader 1 also touches one word per 128-byte line of this tile's eighth of
-// the block six chunks ahead (buffer->LDS loads into a scratch slot, no
-// registers), so the loaders and the output wave find the blocks in L2
-// rather than waiting on HBM.
+// Wave 3 (a loader) also touches one word per 128-byte line of this
+// workgroup's share of the block six chunks ahead (an eighth, or a quarter
+// with two tiles; buffer->LDS loads into a scratch slot, no registers), so
+// the loaders and the output wave find the blocks in L2 rather than waiting
+// on HBM.
 // The state never leaves the state wave's registers; its accumulator tiles
 // feed the next products directly in the split K order. At the end of each
 // chunk the state wave also publishes the new state as bf16 operand
@@ -607,14 +608,14 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
 // next chunk, so one workgroup barrier per chunk orders everything and only
 // 32 of the 48 products per chunk sit on the sequential path.
 //
-// bf16 intermediates: the two loaders keep chunks b+2 and b+3 of [-W], K'^T,
-// this tile's U and gamma_C in flight (buffer->LDS DMA into a three-slot
-// ring, each loader below the hardware's outstanding-load limit); the state
+// bf16 intermediates: the loaders keep chunks b+2 and b+3 of [-W], K'^T,
+// the tiles' U and gamma_C in flight (buffer->LDS DMA into a three-slot
+// ring, each loader below the hardware's outstanding-load limit); a state
 // wave reads chunk b+1's fragments into a second register set while it
 // computes chunk b, so chunk b's slot is free for chunk b+3 during chunk b;
 // the output wave loads its Qt fragments and Ut^T from global memory two
-// chunks ahead. fp32 intermediates (fp32 I/O only) are
-// read from global memory by both compute waves without prefetch.
+// chunks ahead. fp32 intermediates (fp32 I/O only) are read from global
+// memory by the compute waves without prefetch.
 constexpr int kRing = 3;
 constexpr int kCarryThreads = 256;
 constexpr int64_t kCarryRound = 256;   // carry workgroups resident at once (one per CU)
