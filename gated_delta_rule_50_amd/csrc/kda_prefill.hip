@@ -262,8 +262,9 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
       }
     kk = sum_xor32(sum_xor16(kk));
     qq = sum_xor32(sum_xor16(qq));
-    rk = 1.f / sqrtf(kk + kL2NormEps);
-    rq = 1.f / sqrtf(qq + kL2NormEps);
+    // hardware reciprocal square root (about 1 ulp), as the recurrent kernel
+    rk = __builtin_amdgcn_rsqf(kk + kL2NormEps);
+    rq = __builtin_amdgcn_rsqf(qq + kL2NormEps);
     if (g == 0) { sRk[i] = rk; sRq[i] = rq; }
   }
 
