@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/kda.h: argument validation,
 // workspace sizing and launch sequencing. No compute happens here; every
 // step of the operator runs in the HIP kernels.
+#include <cstring>
 #include <initializer_list>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,7 +42,18 @@ bool overlap(const Range& a, const Range& b) {
   return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
 }
 
-bool valid_io(kda_io_dtype io) { return io == KDA_IO_F32 || io == KDA_IO_BF16; }
+// Enum arguments as integers. A C caller may pass any int; reading the
+// value through its object representation keeps an out-of-range one from
+// being an invalid load of the enum type.
+template <class Enum>
+int raw(const Enum& e) {
+  static_assert(sizeof(Enum) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool valid_io(int io) { return io == KDA_IO_F32 || io == KDA_IO_BF16; }
 
 // Tensor pointers the kernels read or write with 16-byte vectors must be
 // 16-byte aligned; NULL passes.
@@ -56,7 +68,7 @@ bool aligned4(std::initializer_list<const void*> ps) {
   return true;
 }
 
-int64_t io_bytes(kda_io_dtype io) { return io == KDA_IO_BF16 ? 2 : 4; }
+int64_t io_bytes(int io) { return io == KDA_IO_BF16 ? 2 : 4; }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -69,7 +81,7 @@ int64_t chunk_slots(int64_t n_seqs, int64_t T) {
 int64_t inter_offset(int64_t n_seqs) { return 256 + round_up(4 * (n_seqs + 1), 256); }
 
 // Returns 0 when the sizes are unusable.
-size_t workspace_bytes(int64_t n_seqs, int64_t T, int64_t heads, kda_io_dtype io) {
+size_t workspace_bytes(int64_t n_seqs, int64_t T, int64_t heads, int io) {
   if (n_seqs < 1 || T < 0 || heads < 1 || heads > 65535 || !valid_io(io)) return 0;
   const int64_t slots = chunk_slots(n_seqs, T);
   if (slots > INT32_MAX) return 0;
@@ -82,7 +94,8 @@ size_t workspace_bytes(int64_t n_seqs, int64_t T, int64_t heads, kda_io_dtype io
 extern "C" {
 
 size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t heads,
-                                     int32_t dk, int32_t dv, kda_io_dtype io) {
+                                     int32_t dk, int32_t dv, kda_io_dtype io_arg) {
+  const int io = raw(io_arg);
   if (dk != kDim || dv != kDim) return 0;
   return workspace_bytes(n_seqs, total_tokens, heads, io);
 }
@@ -96,7 +109,7 @@ namespace {
 kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta, const float* h0,
                           const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
-                          int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io,
+                          int32_t heads, int32_t dk, int32_t dv, int io,
                           uint32_t flags, void* o, float* h_final, void* workspace,
                           size_t workspace_bytes_given, void* stream) {
   const int64_t T = total_tokens;
@@ -155,7 +168,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          uint32_t flags, void* o, float* h_final, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl(7, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens,
-                        heads, dk, dv, io, flags, o, h_final, workspace, workspace_bytes,
+                        heads, dk, dv, raw(io), flags, o, h_final, workspace, workspace_bytes,
                         stream);
 }
 
@@ -167,14 +180,15 @@ kda_status kda_chunk_fwd_phase(int32_t phase, const void* q, const void* k, cons
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (phase < 0 || phase > 2) return KDA_ERR_SHAPE;
   return chunk_fwd_impl(1 << phase, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs,
-                        total_tokens, heads, dk, dv, io, flags, o, h_final, workspace,
+                        total_tokens, heads, dk, dv, raw(io), flags, o, h_final, workspace,
                         workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta, float* S_inout,
                            int32_t n_seqs, int32_t heads, int32_t dk, int32_t dv,
-                           kda_io_dtype io, void* o, void* stream) {
+                           kda_io_dtype io_arg, void* o, void* stream) {
+  const int io = raw(io_arg);
   if (n_seqs < 0 || heads < 1) return KDA_ERR_SHAPE;
   if (dk != kDim || dv != kDim || !valid_io(io)) return KDA_ERR_UNSUPPORTED;
   if (n_seqs == 0) return KDA_OK;
@@ -200,9 +214,10 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
 kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v,
                              const float* log_alpha, const float* beta, const void* h0,
                              const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
-                             int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io,
-                             kda_state_dtype state_dtype, uint32_t flags, void* o,
+                             int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io_arg,
+                             kda_state_dtype state_arg, uint32_t flags, void* o,
                              void* h_final, void* stream) {
+  const int io = raw(io_arg), state_dtype = raw(state_arg);
   const int64_t T = total_tokens;
   if (T < 0 || n_seqs < 0 || heads < 1) return KDA_ERR_SHAPE;
   if (dk != kDim || dv != kDim || !valid_io(io)) return KDA_ERR_UNSUPPORTED;
@@ -239,7 +254,9 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v,
 }
 
 kda_status kda_rmsnorm_gate(const void* o, const void* gate, const float* weight, float eps,
-                            int64_t rows, int32_t dv, kda_io_dtype io, void* y, void* stream) {
+                            int64_t rows, int32_t dv, kda_io_dtype io_arg, void* y,
+                            void* stream) {
+  const int io = raw(io_arg);
   if (rows < 0 || !(eps >= 0.f) || eps > 3.0e38f) return KDA_ERR_SHAPE;
   if (dv != kDim || !valid_io(io)) return KDA_ERR_UNSUPPORTED;
   if (rows == 0) return KDA_OK;
@@ -256,7 +273,7 @@ kda_status kda_rmsnorm_gate(const void* o, const void* gate, const float* weight
 }
 
 const char* kda_status_string(kda_status s) {
-  switch (s) {
+  switch (raw(s)) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_SHAPE: return "a size is negative or inconsistent";

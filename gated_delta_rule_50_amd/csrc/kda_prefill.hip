@@ -631,15 +631,11 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Staged bytes per chunk: [-W] and K'^T fragments (32 KiB), the tile's U
-// (2 KiB), gamma_C (512 B, in a 1 KiB slot). Loader 0 moves [-W] and U
-// (18 KiB), loader 1 K'^T and gamma_C (17 KiB), 1 KiB per DMA instruction.
+// Staged bytes per chunk: [-W] and K'^T fragments (32 KiB), each tile's U
+// (2 KiB), gamma_C (512 B, in a 1 KiB slot), 1 KiB per DMA instruction.
 constexpr int kStageW = kXAElems / 2 * 2;
 constexpr int kStageKT = kKTElems * 2;
 constexpr int kStageU = 4 * kWave * 4 * 2;
-constexpr int kStageBuf = kStageW + kStageKT + kStageU + 1024;
-constexpr int kDMA0 = (kStageW + kStageU) / 1024;
-constexpr int kDMA1 = kStageKT / 1024 + 1;
 
 // State wave operands of one chunk.
 template <class E>
