@@ -326,7 +326,7 @@ def long_configs(torch, d, steps, warmup):
                       None if p.h0 is None else d(p.h0), d(p.cu_seqlens, torch.int32))
         T, H, N = p.T, p.H, p.N
         del p
-        us = _time_calls(torch, pre.run, max(2, steps // 4), max(1, warmup // 2))
+        us = _time_calls(torch, pre.run, max(4, steps // 2), max(2, warmup // 2))
         alg = T * H * PREFILL_BYTES + 2 * N * H * STATE_BYTES
         out[name] = {
             "workload": f"{N} sequence(s), lengths {int(lens.min())}..{int(lens.max())}, "
