@@ -103,38 +103,22 @@ template <> struct Raw2<bf16> {
 };
 
 // State storage: four consecutive columns of one row. The state is touched
-// once per call: when the states of a call outgrow the memory-side cache
-// their accesses are nontemporal (streamed past the caches, kNT); smaller
-// ones stay cached for the next call.
-template <bool kNT, class V>
-__device__ __forceinline__ V ld_state(const V* p) {
-  if constexpr (kNT) return __builtin_nontemporal_load(p);
-  else return *p;
-}
-template <bool kNT, class V>
-__device__ __forceinline__ void st_state(V* p, V v) {
-  if constexpr (kNT) __builtin_nontemporal_store(v, p);
-  else *p = v;
-}
-template <bool kNT>
+// once per call, so its accesses are nontemporal (streamed past the caches).
 __device__ __forceinline__ float4 load_state4(const float* p) {
-  const floatx4 v = ld_state<kNT>(reinterpret_cast<const floatx4*>(p));
+  const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
   return float4{v[0], v[1], v[2], v[3]};
 }
-template <bool kNT>
 __device__ __forceinline__ float4 load_state4(const bf16* p) {
-  const bf16x4 v = ld_state<kNT>(reinterpret_cast<const bf16x4*>(p));
+  const bf16x4 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(p));
   return float4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
-template <bool kNT>
 __device__ __forceinline__ void store_state4(float* p, float4 x) {
-  st_state<kNT>(reinterpret_cast<floatx4*>(p), floatx4{x.x, x.y, x.z, x.w});
+  __builtin_nontemporal_store(floatx4{x.x, x.y, x.z, x.w}, reinterpret_cast<floatx4*>(p));
 }
-template <bool kNT>
 __device__ __forceinline__ void store_state4(bf16* p, float4 x) {
   bf16x4 v;
   v[0] = (bf16)x.x; v[1] = (bf16)x.y; v[2] = (bf16)x.z; v[3] = (bf16)x.w;
-  st_state<kNT>(reinterpret_cast<bf16x4*>(p), v);
+  __builtin_nontemporal_store(v, reinterpret_cast<bf16x4*>(p));
 }
 
 // Per-token inputs of one lane: channels 2 l, 2 l + 1 of q, k, log alpha;
@@ -167,7 +151,7 @@ __device__ __forceinline__ void fetch_token(TokenIn<IO>& x, const IO* q, const I
 // 32 (lane / 16) .. +31), so a lane's bf16 state row piece and the wave's
 // row of the slice fill whole 128-byte lines; 32-column slices otherwise
 // (lane: quad lane % 8, rows 16 (lane / 8) .. +15).
-template <class IO, class ST, bool kNorm, bool kSingle, bool kWide, bool kNT>
+template <class IO, class ST, bool kNorm, bool kSingle, bool kWide>
 __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const ST* h0,
@@ -215,7 +199,7 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
   const int64_t sbase = p * (int64_t)(kD * kD) + (int64_t)(kRows * rl) * kD + col0;
   if (h0 != nullptr) {
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) s[i] = load_state4<kNT>(h0 + sbase + i * kD);
+    for (int i = 0; i < kRows; ++i) s[i] = load_state4(h0 + sbase + i * kD);
   } else {
 #pragma unroll
     for (int i = 0; i < kRows; ++i) s[i] = float4{0.f, 0.f, 0.f, 0.f};
@@ -323,7 +307,7 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
 
   if (h_final != nullptr) {
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) store_state4<kNT>(h_final + sbase + i * kD, s[i]);
+    for (int i = 0; i < kRows; ++i) store_state4(h_final + sbase + i * kD, s[i]);
   }
 }
 
@@ -347,30 +331,17 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
   // L = 2 and 4 from 193 / 199 to 178 / 187 us (8 / 10 per CU). From about
   // 16 tokens on the token loop is VALU-bound and wants every wave it can
   // get, so no cap.
-  // States that fit the 256 MiB memory-side cache are read and written
-  // through the caches, uncapped, so a decode loop finds them there on the
-  // next step (fp32 states, H = 32, per step: 16 sequences 13.9 -> 8.7 us,
-  // 64 sequences 45.4 -> 41.9 us, 128 sequences 87.4 -> 81.4 us; at 256
-  // sequences, 512 MiB, the streamed form is faster: 171 against 195 us;
-  // bf16 states at 256 sequences, 256 MiB: 92 -> 87 us cached).
-  constexpr int64_t kCachedMax = (int64_t)256 << 20;
-  const int64_t state_bytes = pairs * kD * kD * (bf16_state ? 2 : 4);
-  const bool nt = state_bytes > kCachedMax;
   const int64_t n_seqs = pairs / H;
   const int64_t avg_len = n_seqs > 0 ? T / n_seqs : 0;
   int cap = 0;
-  if (!nt) cap = 0;   // cached states: every wave that fits
-  else if (single) cap = bf16_state ? 8 : 5;
+  if (single) cap = bf16_state ? 8 : 5;
   else if (avg_len <= 2) cap = 8;
   else if (avg_len <= 4) cap = 10;
   const size_t lds_pad = cap > 0 ? (size_t)(kLdsPerCu / cap - kStaticLds) : 0;
-#define KDA_REC_LAUNCH1(IO, ST, NORM, ONE, WIDE, NT)                                          \
-  recurrent_fwd_kernel<IO, ST, NORM, ONE, WIDE, NT><<<grid, block, lds_pad, stream>>>(       \
+#define KDA_REC_LAUNCH(IO, ST, NORM, ONE, WIDE)                                              \
+  recurrent_fwd_kernel<IO, ST, NORM, ONE, WIDE><<<grid, block, lds_pad, stream>>>(           \
       (const IO*)q, (const IO*)k, (const IO*)v, log_alpha, beta, (const ST*)h0, cu, seq_len, \
       T, H, pairs, (IO*)o, (ST*)h_final)
-#define KDA_REC_LAUNCH(IO, ST, NORM, ONE, WIDE)                 \
-  if (nt) KDA_REC_LAUNCH1(IO, ST, NORM, ONE, WIDE, true);       \
-  else KDA_REC_LAUNCH1(IO, ST, NORM, ONE, WIDE, false)
 #define KDA_REC_NORM(IO, ST, WIDE)                             \
   if (l2norm) {                                                \
     if (single) KDA_REC_LAUNCH(IO, ST, true, true, WIDE);      \
@@ -386,7 +357,6 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
   }
 #undef KDA_REC_NORM
 #undef KDA_REC_LAUNCH
-#undef KDA_REC_LAUNCH1
   return hipGetLastError();
 }
 
