@@ -347,8 +347,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}): the "
-              "KDA operator here runs on a single MI355X and this build has no multi-GPU "
-              "path. Run with --gpus 1.", file=sys.stderr)
+              "operator's kernels run on one MI355X (heads and sequences shard across GPUs "
+              "with no communication; that path is not implemented). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
