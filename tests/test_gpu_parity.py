@@ -372,6 +372,25 @@ def test_exact_recall(io):
     assert rel_max_err(host(o), p.v.astype(np.float64)) <= (1e-3 if io == "f32" else 3e-2)
 
 
+def test_binding_reports_rejected_arguments():
+    """The binding turns a rejected call into KDAError with the ABI status:
+    a q view starting 8 bytes into its allocation (misaligned), and an
+    output overlapping an input."""
+    p = workloads.make_prefill([100], H=2, seed=44, io="bf16", h0_std=0.05)
+    bf = torch.bfloat16
+    q_big = torch.zeros(p.q.size + 8, dtype=bf, device="cuda")
+    q_off = q_big[4:4 + p.q.size].view(p.q.shape)           # 8 bytes in
+    q_off.copy_(dev(p.q, bf))
+    args = (dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta))
+    with pytest.raises(kda.KDAError) as e:
+        kda.chunk_fwd(q_off, *args, dev(p.h0))
+    assert e.value.status == kda.KDA_ERR_ALIGN
+    q = dev(p.q, bf)
+    with pytest.raises(kda.KDAError) as e:
+        kda.chunk_fwd(q, *args, dev(p.h0), o=q)
+    assert e.value.status == kda.KDA_ERR_ALIAS
+
+
 def test_zero_tokens_keep_initial_state():
     H = 2
     h0 = workloads.make_decode_state(3, H, seed=37, std=0.05)
