@@ -9,7 +9,8 @@ Inputs are synthetic (seeded generators), resident in HBM before timing.
 
 Printed: ONE JSON line. ``value`` is prefill tokens/s (T / mean prefill call
 time from HIP events on the caller's stream); decode tokens/s is reported
-beside it. After the timed steps the prefill's kernels are also launched one
+beside it. ``timing`` gives the median, p10 and p90 of the timed calls and
+of prefill calls made with cold inputs (each after a 1 GiB scrub write). After the timed steps the prefill's kernels are also launched one
 at a time (phase entry point, all chunks per launch) to measure each
 kernel's own duration; ``kernels`` holds those and the decode kernel's, and
 ``roofline`` describes the one with the longest mean duration.
@@ -87,6 +88,11 @@ def _parse():
                          "the 16-sequence packed batch (about a minute of input generation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy first (counter scale factor)")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="turn one rocprofv3 --pmc run of the MFMA counters (MFMA_COUNTERS) of "
+                         "this script into a table; --durations adds rates")
+    ap.add_argument("--durations", metavar="KERNEL=US", nargs="*", default=None,
+                    help="traced mean duration per launch, e.g. intra=158.5 carry=131.5")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script with --copy-calibration into the traffic summary text")
@@ -143,6 +149,48 @@ def summarize_pmc(fetch_dir, write_dir):
         if k in f and k in w:
             lines.append(f"{k}_fetch_KiB = {f[k]:.1f}")
             lines.append(f"{k}_write_KiB = {w[k]:.1f}")
+    print("\n".join(lines))
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32", "GRBM_GUI_ACTIVE", "MfmaUtil")
+N_SIMDS, N_XCDS = 256 * 4, 8
+
+
+def summarize_mfma(run_dir, durations_us=None):
+    """Matrix-core use per launch of each kernel from one rocprofv3 --pmc run
+    of MFMA_COUNTERS. The profiler writes one value per dispatch and counter,
+    summed over the counter's instances: GRBM_GUI_ACTIVE (one per XCD) is
+    therefore divided by the XCD count to give the launch's active cycles.
+    MFMA busy is the profiler's own MfmaUtil (summed MFMA-busy cycles over
+    active cycles x SIMDs); flops count 512 per MOP. With durations (us per
+    launch of each kernel, from a kernel trace) the flops become rates
+    against the dense peaks (bf16 2.5 PFLOP/s, fp32 matrix 157.3 TFLOP/s)."""
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            k, c = _kernel_key(row["Kernel_Name"]), row["Counter_Name"]
+            if k is None or c not in MFMA_COUNTERS:
+                continue
+            dd = per.setdefault(k, {}).setdefault(row["Dispatch_Id"], {})
+            dd[c] = dd.get(c, 0.0) + float(row["Counter_Value"])
+    lines = ["| kernel | dispatches | active cycles per XCD | MfmaUtil (%) | bf16 MFMA flops "
+             "| fp32 MFMA flops | bf16 TFLOP/s (of 2500) | fp32 TFLOP/s (of 157.3) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for k in ("intra", "carry", "decode", "chunk_map"):
+        if k not in per:
+            continue
+        ds = [d for d in per[k].values() if all(c in d for c in MFMA_COUNTERS)]
+        mean = {c: float(np.mean([d[c] for d in ds])) for c in MFMA_COUNTERS}
+        bf = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        f32 = mean["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512
+        rb = rf = "-"
+        if durations_us and k in durations_us:
+            sec = durations_us[k] * 1e-6
+            rb = f"{bf / sec / 1e12:.1f} ({bf / sec / 1e12 / BF16_PEAK_TFLOPS:.3f})"
+            rf = f"{f32 / sec / 1e12:.1f} ({f32 / sec / 1e12 / 157.3:.3f})"
+        lines.append(f"| {k} | {len(ds)} | {mean['GRBM_GUI_ACTIVE'] / N_XCDS:.0f} | "
+                     f"{mean['MfmaUtil']:.2f} | {bf:.4g} | {f32:.4g} | {rb} | {rf} |")
     print("\n".join(lines))
 
 
@@ -222,6 +270,30 @@ def _time_calls(torch, fn, steps, warmup):
         ev[i + 1].record()
     torch.cuda.synchronize()
     return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])) * 1e3
+
+
+def _spread(ms):
+    """Median, p10 and p90 (us) of per-call durations in ms."""
+    us = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median_us": float(np.median(us)), "p10_us": float(np.percentile(us, 10)),
+            "p90_us": float(np.percentile(us, 90))}
+
+
+def cold_prefill(torch, pre, reps):
+    """Prefill calls each preceded by writing a 1 GiB scrub buffer, which
+    evicts the inputs from the 256 MiB memory-side cache (the 8K workload's
+    inputs are 337 MB, so a warm repeat finds part of them there). Returns
+    the per-call spread (us) of the prefill alone."""
+    scrub = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    ev = [_events(torch, 2) for _ in range(reps)]
+    for i in range(reps):
+        scrub.fill_(float(i))
+        ev[i][0].record()
+        pre.run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    del scrub
+    return _spread([e[0].elapsed_time(e[1]) for e in ev])
 
 
 def _hbm(alg_bytes, us):
@@ -343,6 +415,10 @@ def main():
     args = _parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_mfma:
+        durs = dict((k, float(v)) for k, v in (x.split("=", 1) for x in args.durations or []))
+        summarize_mfma(args.summarize_mfma, durs)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -468,6 +544,10 @@ def main():
         "attainable_frac": t_roof / t_pre,
     }
     decode_tps = cfg4.n_seqs / t_dec
+    # distribution of the timed calls (the means above give value and
+    # roofline), and the prefill with cold inputs
+    timing = {"prefill_warm": _spread(prefill_ms), "decode": _spread(decode_ms),
+              "prefill_cold": cold_prefill(torch, pre, max(5, args.steps // 2))}
 
     out = {
         "metric": METRIC,
@@ -490,6 +570,7 @@ def main():
         "prefill_phases_us": sum(mean[n] for n in names) * 1e3,
         "roofline": roofline,
         "prefill_path": prefill_path,
+        "timing": timing,
         "kernels": kernels,
     }
     if not args.no_extensions:
