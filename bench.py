@@ -23,6 +23,11 @@ and replayed from a HIP graph, the prefill with in-kernel q/k L2Norm, and
 the RMSNorm x sigmoid-gate epilogue over the prefill's 8192 x 32 output
 rows.
 
+``ceilings`` holds what plain kernels achieve on the same GPU (streaming
+read, copy, in-place update; bf16 MFMA and fp32 FMA loops); each roofline
+object adds ``achievable`` and ``frac_achievable`` against the ceiling of its
+kind (in-place update for the decode-shaped paths, copy otherwise).
+
 ``--long-configs`` adds the prefill on the long single sequence
 (T = 131072) and on the 16-sequence packed batch.
 
@@ -64,10 +69,11 @@ DECODE_BYTES = 2 * STATE_BYTES + TOKEN_BYTES               # 132612
 # Recurrent path, per token-head: S~^T k and S~^T q (2 d^2 each as FMAs),
 # the decay a*s (d^2) and the rank-1 correction (2 d^2).
 FLOPS_RECURRENT = 7 * D * D                                # 114688
-# fp32 VALU without packed-fp32 instructions: 256 CUs x 64 lanes x 2 flops
-# (one FMA per lane per cycle) x 2.4 GHz; the published 157.3 TFLOP/s
-# counts the packed forms, which this code is built without.
-FP32_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12             # 78.6
+# fp32 vector peak, as published for MI355X: 256 CUs x 256 flops per cycle x
+# 2.4 GHz. Plain (unpacked) FMAs reach it too on this chip: a loop of
+# independent v_fma_f32 measures about 124 TFLOP/s at the 2.2 GHz the
+# shader clock holds under load (the ceilings' probe reports it per run).
+FP32_VALU_TFLOPS = 256 * 256 * 2.4e9 / 1e12                 # 157.3
 # Epilogue, per row of 128 channels (bf16): o and gate read, y written.
 EPILOGUE_BYTES = 3 * 256
 
@@ -83,6 +89,8 @@ def _parse():
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--no-extensions", action="store_true",
                     help="skip the timings of the optional paths (shorter counter runs)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the plain-kernel probes of achievable bandwidth and FLOP rate")
     ap.add_argument("--long-configs", action="store_true",
                     help="also time the prefill on the long single sequence (T = 131072) and "
                          "the 16-sequence packed batch (about a minute of input generation)")
@@ -294,6 +302,72 @@ def cold_prefill(torch, pre, reps):
     torch.cuda.synchronize()
     del scrub
     return _spread([e[0].elapsed_time(e[1]) for e in ev])
+
+
+def ceilings(torch):
+    """Achievable rates of plain kernels on this GPU (the probes library built
+    beside the operator): streaming read, nontemporal copy and in-place
+    update of 1 GiB buffers, a bf16 MFMA loop and an fp32 FMA loop. Median of
+    five launches each, HIP events on the launch stream."""
+    import ctypes
+    from gated_delta_rule_50_amd.build import CEIL_LIB
+    if not CEIL_LIB.exists():
+        raise RuntimeError(f"{CEIL_LIB} is not built; run `python -m gated_delta_rule_50_amd.build`")
+    L = ctypes.CDLL(str(CEIL_LIB))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.kdab_read.argtypes = [vp, i64, vp, i32, vp]
+    L.kdab_copy.argtypes = [vp, vp, i64, i32, i32, vp]
+    L.kdab_rmw.argtypes = [vp, i64, i32, vp]
+    L.kdab_mfma.argtypes = [vp, i64, i32, vp]
+    L.kdab_valu.argtypes = [vp, i64, i32, vp]
+    nbytes = COPY_BYTES
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a).fill_(0.0)
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    pa, pb, ps = ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), \
+        ctypes.c_void_p(sink.data_ptr())
+
+    def med_us(launch, reps=5):
+        launch()
+        ev = [_events(torch, 2) for _ in range(reps)]
+        for e in ev:
+            e[0].record()
+            rc = launch()
+            e[1].record()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+
+    grids = (1024, 2048, 4096, 8192)   # best over launch sizes
+    out = {
+        "hbm_read_GBps": max(nbytes / med_us(lambda: L.kdab_read(pa, nbytes, ps, g, st))
+                             for g in grids) / 1e3,
+        "hbm_copy_GBps": max(2 * nbytes / med_us(lambda: L.kdab_copy(pa, pb, nbytes, 1, g, st))
+                             for g in grids) / 1e3,
+        "hbm_rmw_GBps": max(2 * nbytes / med_us(lambda: L.kdab_rmw(pa, nbytes, g, st))
+                            for g in grids) / 1e3,
+    }
+    # 2048 workgroups of four waves: eight waves per SIMD
+    iters, wg = 4000, 2048
+    flops = wg * 4 * 8 * iters * (2 * 16 * 16 * 32)
+    out["mfma_bf16_TFLOPs"] = flops / med_us(lambda: L.kdab_mfma(ps, iters, wg, st)) / 1e6
+    wg = 4096
+    flops = wg * 256 * 32 * iters * 2
+    out["valu_fp32_TFLOPs"] = flops / med_us(lambda: L.kdab_valu(ps, iters, wg, st)) / 1e6
+    del a, b, sink
+    out["note"] = ("measured ceilings of plain kernels on this GPU; roofline fractions use the "
+                   "published peaks, frac_achievable these")
+    return out
+
+
+def _with_ceiling(roof, ceil, key):
+    """Adds the measured ceiling of the same kind to a roofline object."""
+    if ceil and key in ceil:
+        roof["achievable"] = ceil[key]
+        roof["frac_achievable"] = roof["achieved"] / ceil[key]
+    return roof
 
 
 def _hbm(alg_bytes, us):
@@ -575,6 +649,16 @@ def main():
     }
     if not args.no_extensions:
         out["extensions"] = extensions(torch, d, pre_args, args.steps, args.warmup)
+    if not args.no_ceilings:
+        ceil = ceilings(torch)
+        out["ceilings"] = ceil
+        _with_ceiling(roofline, ceil, "hbm_rmw_GBps" if dom == "decode" else "hbm_copy_GBps")
+        kinds = {"recurrent_L4": "hbm_rmw_GBps", "recurrent_L64": "valu_fp32_TFLOPs",
+                 "decode_bf16_state": "hbm_rmw_GBps", "decode_batch1": "hbm_rmw_GBps",
+                 "epilogue": "hbm_copy_GBps"}
+        for name, key in kinds.items():
+            if name in out.get("extensions", {}):
+                _with_ceiling(out["extensions"][name]["roofline"], ceil, key)
     if args.long_configs:
         out["long_configs"] = long_configs(torch, d, args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -21,6 +21,9 @@ INCLUDE = ROOT / "include"
 LIB = PKG / "libkda.so"
 BUILD = ROOT / "_build"
 SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_recurrent.hip", "kda_epilogue.hip"]
+# achievable-rate probes used by bench.py's roofline figures (not the operator)
+CEIL_SRC = PKG / "ceilings" / "ceilings.hip"
+CEIL_LIB = PKG / "libkda_ceilings.so"
 
 
 def hipcc() -> str:
@@ -38,10 +41,11 @@ def _flags():
             *os.environ.get("KDA_EXTRA_FLAGS", "").split()]
 
 
-def _compile(src: str, verbose: bool) -> Path:
-    out = BUILD / (src + ".o")
-    cmd = [hipcc(), *_flags(), "-c", str(CSRC / src), "-o", str(out)]
-    if src.endswith(".hip"):
+def _compile(src, verbose: bool) -> Path:
+    path = Path(src) if os.path.isabs(str(src)) else CSRC / src
+    out = BUILD / (path.name + ".o")
+    cmd = [hipcc(), *_flags(), "-c", str(path), "-o", str(out)]
+    if path.suffix == ".hip":
         cmd[1:1] = ["-x", "hip"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
@@ -55,17 +59,23 @@ def _compile(src: str, verbose: bool) -> Path:
     return out
 
 
-def build(verbose: bool = False) -> Path:
-    BUILD.mkdir(exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB.with_suffix(".so.tmp")
+def _link(objs, lib: Path, verbose: bool) -> None:
+    tmp = lib.with_suffix(".so.tmp")
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", str(tmp),
            *map(str, objs)]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    tmp.replace(LIB)
+    tmp.replace(lib)
+
+
+def build(verbose: bool = False) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    srcs = [*SOURCES, str(CEIL_SRC)]
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], CEIL_LIB, verbose)
     return LIB
 
 

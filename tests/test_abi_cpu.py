@@ -302,3 +302,29 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 2, 128)
     with pytest.raises(ValueError):
         kda.decode_step(x, x, x, x, torch.zeros(4, 2), torch.zeros(4, 2, 128, 128))
+
+
+def test_probe_library_rejects_bad_arguments():
+    """The achievable-rate probes (bench.py's ceilings) load, export their
+    entry points and refuse bad arguments before any launch."""
+    path = ROOT / "gated_delta_rule_50_amd" / "libkda_ceilings.so"
+    if not path.exists():
+        pytest.skip("libkda_ceilings.so not built")
+    P = ctypes.CDLL(str(path))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    P.kdab_read.argtypes = [vp, i64, vp, i32, vp]
+    P.kdab_copy.argtypes = [vp, vp, i64, i32, i32, vp]
+    P.kdab_rmw.argtypes = [vp, i64, i32, vp]
+    P.kdab_mfma.argtypes = [vp, i64, i32, vp]
+    P.kdab_valu.argtypes = [vp, i64, i32, vp]
+    a, b, s = 0x10000, 0x20000000, 0x30000
+    assert P.kdab_read(None, 1024, s, 64, None) == -1            # null buffer
+    assert P.kdab_read(a + 4, 1024, s, 64, None) == -1           # misaligned
+    assert P.kdab_read(a, 1000, s, 64, None) == -1               # not a multiple of 16
+    assert P.kdab_read(a, 1024, None, 64, None) == -1            # no sink
+    assert P.kdab_read(a, 1024, s, 0, None) == -1                # empty grid
+    assert P.kdab_copy(a, a + 512, 1024, 1, 64, None) == -1      # overlapping
+    assert P.kdab_copy(a, b, -16, 1, 64, None) == -1
+    assert P.kdab_rmw(a, 0, 64, None) == -1
+    assert P.kdab_mfma(s, 0, 64, None) == -1                     # no iterations
+    assert P.kdab_valu(s, 10, (1 << 20) + 1, None) == -1         # grid too large
