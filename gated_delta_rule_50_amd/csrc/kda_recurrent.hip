@@ -8,6 +8,12 @@
 // over every token of a sequence with the state held in registers: the state
 // is read from HBM once before the first token and written once after the
 // last, so a call over L tokens moves the state's bytes once, not L times.
+// Over several tokens the decay is not applied to the state each token: with
+// S = Diag(G) S^ and G the channel-wise product of the alphas so far,
+//   e = S^^T (G alpha_t * k),  S^ <- S^ + (k / (G alpha_t)) (v - e)^T beta,
+// so a token costs three FMAs per state value instead of a multiply and
+// three FMAs. G is folded into S^ (S^ <- G alpha_t * S^, G <- 1) whenever a
+// channel's G alpha_t would fall below 2^-40, and once at the end.
 // This is the path the review's "FLOPs Accounting and Inference Strategy"
 // section gives short inputs (the recurrent kernel for generation); the
 // serving note of the "L2 Deep Distill" page routes q_len <= 64 to it. The
@@ -39,6 +45,10 @@ namespace kda {
 namespace {
 
 constexpr int kRowPitch = 20;                  // LDS floats per 16-row group (bank spread)
+// The token loop keeps S = Diag(G) S^ with G the decay accumulated since the
+// last fold; it folds G into S^ before G of any channel would drop below
+// this (so k / G stays far from overflow).
+constexpr float kFoldBelow = 0x1p-40f;
 constexpr int kStaticLds = 4 * 8 * kRowPitch * 4;   // the four token-vector rows, bytes
 constexpr int kLdsPerCu = 160 * 1024;               // gfx950 LDS per CU
 
@@ -211,6 +221,22 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
   };
 
   const int widx = (lane >> 3) * kRowPitch + 2 * (lane & 7);  // channels 2 l, 2 l + 1
+  // the token loop's running decay G of channels 2 l, 2 l + 1 (S = Diag(G) S^)
+  constexpr bool kScaled = !kSingle;
+  float G0 = 1.f, G1 = 1.f;
+  // multiplies this lane's state rows by the per-channel factors staged in s_a
+  auto scale_rows = [&]() {
+#pragma unroll
+    for (int m = 0; m < kRows / 4; ++m) {
+      const float4 f = *reinterpret_cast<const float4*>(s_a + row4(m));
+      const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float4& x = s[4 * m + r];
+        x.x *= fv[r]; x.y *= fv[r]; x.z *= fv[r]; x.w *= fv[r];
+      }
+    }
+  };
   TokenIn<IO> nxt;
   if (bos < eos) fetch_token(nxt, q, k, v, log_alpha, beta, bos * H + h, lane, col0 + cq);
 
@@ -242,11 +268,29 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
       qk *= rk * rq;
     }
     __syncthreads();  // the previous token's reads of the rows are done
-    *reinterpret_cast<float2*>(s_ka + widx) = float2{a0 * k0, a1 * k1};
-    *reinterpret_cast<float2*>(s_qa + widx) = float2{a0 * q0, a1 * q1};
-    *reinterpret_cast<float2*>(s_a + widx) = float2{a0, a1};
-    *reinterpret_cast<float2*>(s_k + widx) = float2{k0, k1};
+    bool fold = false;
+    if constexpr (kScaled) {
+      float g0 = G0 * a0, g1 = G1 * a1;
+      fold = __builtin_amdgcn_ballot_w64(!(g0 >= kFoldBelow && g1 >= kFoldBelow)) != 0;
+      if (fold) {
+        // S~ = Diag(G alpha) S^ in place; G restarts at 1
+        *reinterpret_cast<float2*>(s_a + widx) = float2{g0, g1};
+        g0 = g1 = 1.f;
+      }
+      G0 = g0;
+      G1 = g1;
+      *reinterpret_cast<float2*>(s_ka + widx) = float2{g0 * k0, g1 * k1};
+      *reinterpret_cast<float2*>(s_qa + widx) = float2{g0 * q0, g1 * q1};
+      *reinterpret_cast<float2*>(s_k + widx) =
+          float2{k0 * __builtin_amdgcn_rcpf(g0), k1 * __builtin_amdgcn_rcpf(g1)};
+    } else {
+      *reinterpret_cast<float2*>(s_ka + widx) = float2{a0 * k0, a1 * k1};
+      *reinterpret_cast<float2*>(s_qa + widx) = float2{a0 * q0, a1 * q1};
+      *reinterpret_cast<float2*>(s_a + widx) = float2{a0, a1};
+      *reinterpret_cast<float2*>(s_k + widx) = float2{k0, k1};
+    }
     __syncthreads();
+    if (kScaled && fold) scale_rows();
 
     // Partial column sums over this lane's rows: e = S~^T k, pr = S~^T q.
     float4 pe = {0.f, 0.f, 0.f, 0.f}, pr = {0.f, 0.f, 0.f, 0.f};
@@ -285,19 +329,36 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     gather16(dhi, d4[1], d4[3]);
     const float4 d = {d4[0], d4[1], d4[2], d4[3]};
 
+    if constexpr (kScaled) {
+      // S^ += (k / G) d^T
 #pragma unroll
-    for (int m = 0; m < kRows / 4; ++m) {
-      const float4 a = *reinterpret_cast<const float4*>(s_a + row4(m));
-      const float4 kv = *reinterpret_cast<const float4*>(s_k + row4(m));
-      const float av[4] = {a.x, a.y, a.z, a.w};
-      const float kvv[4] = {kv.x, kv.y, kv.z, kv.w};
+      for (int m = 0; m < kRows / 4; ++m) {
+        const float4 kv = *reinterpret_cast<const float4*>(s_k + row4(m));
+        const float kvv[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float4& x = s[4 * m + r];
-        x.x = av[r] * x.x + kvv[r] * d.x;
-        x.y = av[r] * x.y + kvv[r] * d.y;
-        x.z = av[r] * x.z + kvv[r] * d.z;
-        x.w = av[r] * x.w + kvv[r] * d.w;
+        for (int r = 0; r < 4; ++r) {
+          float4& x = s[4 * m + r];
+          x.x += kvv[r] * d.x;
+          x.y += kvv[r] * d.y;
+          x.z += kvv[r] * d.z;
+          x.w += kvv[r] * d.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < kRows / 4; ++m) {
+        const float4 a = *reinterpret_cast<const float4*>(s_a + row4(m));
+        const float4 kv = *reinterpret_cast<const float4*>(s_k + row4(m));
+        const float av[4] = {a.x, a.y, a.z, a.w};
+        const float kvv[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float4& x = s[4 * m + r];
+          x.x = av[r] * x.x + kvv[r] * d.x;
+          x.y = av[r] * x.y + kvv[r] * d.y;
+          x.z = av[r] * x.z + kvv[r] * d.z;
+          x.w = av[r] * x.w + kvv[r] * d.w;
+        }
       }
     }
 
@@ -306,6 +367,13 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
   }
 
   if (h_final != nullptr) {
+    if constexpr (kScaled) {
+      // S = Diag(G) S^
+      __syncthreads();
+      *reinterpret_cast<float2*>(s_a + widx) = float2{G0, G1};
+      __syncthreads();
+      scale_rows();
+    }
 #pragma unroll
     for (int i = 0; i < kRows; ++i) store_state4(h_final + sbase + i * kD, s[i]);
   }

@@ -82,6 +82,21 @@ def test_recurrent_long_sequence_strong_decay(io):
 
 
 @pytest.mark.parametrize("state", ["f32", "bf16"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_recurrent_decay_underflow(io, state):
+    """Decays the token loop must fold into the state before they leave the
+    safe range: channels 0-15 multiplied by e^-200 (zero in fp32) every fifth
+    token, channels 16-31 by e^-3 every token (a fold every ~9 tokens),
+    channels 32-47 by 1 (never folded), the rest as drawn."""
+    p = workloads.make_prefill([64, 7, 33, 1], H=2, seed=64, io=io, h0_std=0.05)
+    p.log_alpha[::5, :, :16] = -200.0
+    p.log_alpha[:, :, 16:32] = -3.0
+    p.log_alpha[:, :, 32:48] = 0.0
+    o, hf = _run(p, state)
+    _check(p, o, hf, state)
+
+
+@pytest.mark.parametrize("state", ["f32", "bf16"])
 def test_fixed_length_layout_equals_packed(state):
     """cu_seqlens = NULL with n_seqs sequences of T / n_seqs tokens is the
     same computation as the explicit cu_seqlens, bit for bit."""
