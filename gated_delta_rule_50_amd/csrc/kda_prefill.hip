@@ -1077,6 +1077,84 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   }
 }
 
+// ------------------------------------------------- carry for short sequences
+// One wave per (sequence, head, 16-column tile) and no staging: for batches
+// of short sequences, where the pipelined carry above pays its fixed cost
+// (state load, ring fill and drain in a workgroup that fills a CU) for one
+// or two chunks. Here every wave loads its operands straight from the
+// intermediate block (the eight tile waves of a block share an XCD, so the
+// block comes from HBM once) and several waves share each SIMD, so the
+// latency of one wave's loads hides behind the others. Same arithmetic per
+// chunk as the pipelined carry (O = Ut + Qt S from the state at the chunk
+// start, then the state update), so the results are bit-identical to it.
+template <class E>
+__global__ __launch_bounds__(kWave) void carry_short_kernel(
+    const uint8_t* __restrict__ inter, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
+    const float* __restrict__ h0, float* __restrict__ h_final, E* __restrict__ o,
+    int32_t n_seqs, int64_t T, int32_t H) {
+  // the eight tiles of a (sequence, head) get ids with the same id % 8 (one XCD)
+  const int id = blockIdx.x;
+  const int pair = (id & 7) + 8 * ((id >> 3) / 8);
+  const int jt = (id >> 3) % 8;
+  if (pair >= n_seqs * H || status[0] != 0) return;
+  const int n = pair / H, h = pair % H;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4;
+  const int j = 16 * jt + (lane & 15);
+  const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
+  const int b0 = chunk_offset[n], b1 = chunk_offset[n + 1];
+
+  floatx4 S[8];
+  Frag<E> fs[4];
+  const float* h0p = h0 ? h0 + (int64_t)pair * kD * kD : nullptr;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[mt][e] = h0p ? h0p[(16 * mt + 4 * g + e) * kD + j] : 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
+
+  for (int b = b0; b < b1; ++b) {
+    const E* blk = reinterpret_cast<const E*>(inter + ((int64_t)b * H + h) * Inter<E>::kBytes);
+    // O^T = Ut^T + S^T Qt^T from the state at the chunk start
+    OutOps<E, 1> po;
+    load_out_ops<E, 1>(po, blk, jt, lane);
+    floatx4 X[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) X[nt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) X[nt] = mma(X[nt], fs[kb], po.fq[nt][kb]);
+    Frag16<E> ob[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[nt][e] += po.ut[0][nt].get(e);
+      ob[nt] = frag16<E>(X[nt]);
+    }
+    StateOps<E> ps;
+    load_state_ops(ps, blk + Inter<E>::kXA, blk + Inter<E>::kKT,
+                   blk + Inter<E>::kUC + jt * 8 * kWave * 4,
+                   reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(blk) +
+                                                  Inter<E>::kGCByte),
+                   lane);
+    carry_state<E>(S, fs, ps);
+    const int64_t tok0 = seq_start + (int64_t)(b - b0) * kC;
+    store_out<E>(ob, o, tok0, (int)min((int64_t)kC, seq_end - tok0), H, h, lane, 16 * jt);
+  }
+  if (h_final) {
+    float* hf = h_final + (int64_t)pair * kD * kD;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
+  }
+}
+
 // ------------------------------------------------------------- launchers
 size_t inter_block_bytes(bool bf16_io) {
   return bf16_io ? Inter<bf16>::kBytes : Inter<float>::kBytes;
@@ -1124,7 +1202,17 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
   // 1.28 us per chunk on the 8K workload).
   const bool two = bf16_io && pairs * 8 > kCarryRound;
   const int64_t nblocks = ((pairs + 7) / 8) * 8 * (two ? 4 : 8);   // column-tile groups
-  if (two)
+#ifndef KDA_SHORT_AVG_TOKENS
+#define KDA_SHORT_AVG_TOKENS 128
+#endif
+  // batches of short sequences (mean length up to two chunks): one wave per
+  // tile, no pipeline (the single-sequence call always pipelines)
+  const bool short_seqs = bf16_io && !single && n_seqs > 0 &&
+                          T <= (int64_t)KDA_SHORT_AVG_TOKENS * n_seqs;
+  if (short_seqs)
+    carry_short_kernel<bf16><<<(unsigned)(((pairs + 7) / 8) * 64), kWave, 0, stream>>>(
+        inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H);
+  else if (two)
     carry_kernel<bf16, 2><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
         inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single);
   else if (bf16_io)

@@ -195,9 +195,50 @@ def test_phases_equal_full_call_and_deterministic():
 # the carry runs two column tiles per workgroup; these batches take that
 # path (more than 32 pairs), with ragged, one-token and empty sequences.
 def _many_pairs_batch(seed, io="bf16"):
+    """More (sequence, head) pairs than one round of one-tile carry
+    workgroups, sequences long enough on average (> 128 tokens) for the
+    pipelined carry."""
     rng = np.random.default_rng(seed)
-    lengths = [int(x) for x in rng.integers(1, 200, size=18)] + [0, 1, 64, 129]
-    return workloads.make_prefill(lengths, H=2, seed=seed, io=io, h0_std=0.05)
+    lengths = [int(x) for x in rng.integers(150, 400, size=18)] + [0, 1, 64, 129]
+    p = workloads.make_prefill(lengths, H=2, seed=seed, io=io, h0_std=0.05)
+    assert p.T > 128 * p.N
+    return p
+
+
+def _short_batch(seed, n=40, H=3):
+    """A batch of short sequences (mean at most 128 tokens: the short-sequence
+    carry) with the edge lengths 0, 1, 63, 64, 65, 128 and 129."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(0, 140, size=n)] + [0, 1, 63, 64, 65, 128, 129]
+    p = workloads.make_prefill(lengths, H=H, seed=seed, io="bf16", h0_std=0.05)
+    assert p.T <= 128 * p.N
+    return p
+
+
+def test_short_sequence_carry_matches_oracle():
+    p = _short_batch(65)
+    o, hf = _run_prefill(p)
+    _check_prefill(p, o, hf)
+    rh = recurrent.forward(p.q, p.k, p.v, p.log_alpha, p.beta, p.h0, p.cu_seqlens)[1]
+    for n in range(p.N):   # every sequence's final state, the empty ones included
+        assert rel_fro_err(hf[n], rh[n]) <= TOL[p.io][1], n
+
+
+def test_short_sequence_carry_equals_pipelined_bitwise():
+    """The short-sequence carry (the batch) and the pipelined carry (each
+    sequence alone) do the same arithmetic per tile and chunk."""
+    p = _short_batch(66, n=12, H=2)
+    o, hf = _run_prefill(p)
+    bf = torch.bfloat16
+    cu = p.cu_seqlens
+    for n in range(p.N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        if e == s:
+            continue
+        on, hn = kda.chunk_fwd(dev(p.q[s:e], bf), dev(p.k[s:e], bf), dev(p.v[s:e], bf),
+                               dev(p.log_alpha[s:e]), dev(p.beta[s:e]), dev(p.h0[n:n + 1]))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(on), o[s:e]) and np.array_equal(host(hn)[0], hf[n]), n
 
 
 def test_two_tile_carry_matches_oracle():

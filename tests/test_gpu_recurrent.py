@@ -300,14 +300,18 @@ def test_degenerate_cases(path, case):
         assert rel_fro_err(hf, want) <= 1e-2
 
 
-@pytest.mark.parametrize("lens", [[64, 3, 40], [65, 200, 1]])
+@pytest.mark.parametrize("lens", [[48, 3, 40], [49, 2, 17], [65, 200, 1]])
 def test_mode_switch_forward(lens):
-    """kda.forward picks the recurrent path for max length <= 64 and the
-    chunked one otherwise; both match the oracle."""
+    """kda.forward picks the recurrent path for max length <= 48 (the
+    measured crossover) and the chunked one otherwise; both match the
+    oracle."""
     p = workloads.make_prefill(lens, H=2, seed=63, io="bf16", h0_std=0.05)
     bf = torch.bfloat16
-    o, hf = kda.forward(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha),
-                        dev(p.beta), dev(p.h0), dev(p.cu_seqlens, torch.int32),
-                        max_seqlen=max(lens))
+    args = (dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta),
+            dev(p.h0), dev(p.cu_seqlens, torch.int32))
+    o, hf = kda.forward(*args, max_seqlen=max(lens))
+    want = kda.recurrent_fwd if max(lens) <= kda.RECURRENT_MAX_LEN else kda.chunk_fwd
+    o2, hf2 = want(*args)
     torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(hf, hf2)   # the path the switch names
     _check(p, host(o), host(hf))
