@@ -17,7 +17,8 @@ kernel's own duration; ``kernels`` holds those and the decode kernel's, and
 
 ``extensions`` times the operator's optional paths, each on its own
 workload with its own roofline: the fused multi-token recurrent call
-(256 sequences x 32 heads x L = 4 and 64 new tokens), the decode step with a
+(256 sequences x 32 heads x L = 4 and 64 new tokens; the L = 64 batch also
+through the chunked path, which is the faster one there), the decode step with a
 bf16 state, batch-1 decode (one sequence x 32 heads) launched step by step
 and replayed from a HIP graph, the prefill with in-kernel q/k L2Norm, and
 the RMSNorm x sigmoid-gate epilogue over the prefill's 8192 x 32 output
@@ -398,6 +399,16 @@ def extensions(torch, d, pre_args, steps, warmup):
                         f"~N(0,0.02) updated in place", "us": us,
             "tokens_per_s": N * L / (us * 1e-6), "alg_bytes": alg,
             "tflops": tf, "roofline": roof}
+        if L == 64:
+            # the same batch through the chunked path (its short-sequence
+            # carry): from 48 tokens per sequence on the faster of the two
+            pre = Prefill(*ins, d(p.h0), d(p.cu_seqlens, torch.int32))
+            us = _time_calls(torch, pre.run, steps, warmup)
+            out["chunked_L64"] = {
+                "workload": f"the L = 64 batch through kda_chunk_fwd (packed, {N} sequences)",
+                "us": us, "tokens_per_s": N * L / (us * 1e-6), "alg_bytes": alg,
+                "roofline": _hbm(alg, us)}
+            del pre
         del p, ins, S, rec
     cfg4 = workloads.config(4)
     ds = workloads.make_decode_step(cfg4.n_seqs, cfg4.H, cfg4.seed, 0, io=cfg4.io)
@@ -654,6 +665,7 @@ def main():
         out["ceilings"] = ceil
         _with_ceiling(roofline, ceil, "hbm_rmw_GBps" if dom == "decode" else "hbm_copy_GBps")
         kinds = {"recurrent_L4": "hbm_rmw_GBps", "recurrent_L64": "valu_fp32_TFLOPs",
+                 "chunked_L64": "hbm_copy_GBps",
                  "decode_bf16_state": "hbm_rmw_GBps", "decode_batch1": "hbm_rmw_GBps",
                  "epilogue": "hbm_copy_GBps"}
         for name, key in kinds.items():
