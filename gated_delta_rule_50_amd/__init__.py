@@ -3,6 +3,6 @@
 ``kda`` binds the C ABI of libkda.so (HIP kernels for gfx950);
 ``workloads`` draws the seeded synthetic inputs.
 """
-from .kda import (KDAError, Prefill, Recurrent, alloc_workspace, chunk_fwd,  # noqa: F401
-                  chunk_fwd_workspace_bytes, decode_step, forward, lib, recurrent_fwd,
-                  rmsnorm_gate)
+from .kda import (KDAError, Prefill, Recurrent, alloc_workspace, check_inputs,  # noqa: F401
+                  chunk_fwd, chunk_fwd_workspace_bytes, decode_step, forward, lib,
+                  recurrent_fwd, rmsnorm_gate)

@@ -20,7 +20,8 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libkda.so"
 BUILD = ROOT / "_build"
-SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_recurrent.hip", "kda_epilogue.hip"]
+SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_recurrent.hip", "kda_epilogue.hip",
+           "kda_check.hip"]
 # achievable-rate probes used by bench.py's roofline figures (not the operator)
 CEIL_SRC = PKG / "ceilings" / "ceilings.hip"
 CEIL_LIB = PKG / "libkda_ceilings.so"

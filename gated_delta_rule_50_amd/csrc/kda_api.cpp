@@ -23,6 +23,10 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
                                 void* o, void* h_final, hipStream_t stream);
 hipError_t launch_rmsnorm_gate(bool bf16_io, const void* o, const void* g, const float* w,
                                float eps, int64_t rows, void* y, hipStream_t stream);
+hipError_t launch_check_inputs(bool bf16_io, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const int32_t* cu,
+                               int32_t n_seqs, int64_t T, int32_t H, int32_t* flags,
+                               hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -269,6 +273,33 @@ kda_status kda_rmsnorm_gate(const void* o, const void* gate, const float* weight
   if (overlap(ry, rg) || overlap(ry, rw)) return KDA_ERR_ALIAS;
   const hipError_t err = kda::launch_rmsnorm_gate(io == KDA_IO_BF16, o, gate, weight, eps, rows,
                                                   y, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_check_inputs(const void* q, const void* k, const void* v, const float* log_alpha,
+                            const float* beta, const int32_t* cu_seqlens, int32_t n_seqs,
+                            int64_t total_tokens, int32_t heads, int32_t dk, int32_t dv,
+                            kda_io_dtype io_arg, int32_t* flags, void* stream) {
+  const int io = raw(io_arg);
+  const int64_t T = total_tokens;
+  if (T < 0 || heads < 1 || (cu_seqlens != nullptr && n_seqs < 1)) return KDA_ERR_SHAPE;
+  if (dk != kDim || dv != kDim || !valid_io(io) || heads > 65535) return KDA_ERR_UNSUPPORTED;
+  if (cu_seqlens != nullptr && T > INT32_MAX) return KDA_ERR_SHAPE;
+  if (T > ((int64_t)1 << 40) / heads) return KDA_ERR_SHAPE;
+  if (!flags) return KDA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !log_alpha || !beta)) return KDA_ERR_NULL;
+  if (!aligned16({q, k, v, log_alpha}) || !aligned4({beta, cu_seqlens, flags}))
+    return KDA_ERR_ALIGN;
+  const int64_t th = T * heads, eb = io_bytes(io);
+  const Range rf(flags, 4);
+  const Range rq(q, th * kDim * eb), rk(k, th * kDim * eb), rv(v, th * kDim * eb);
+  const Range rla(log_alpha, th * kDim * 4), rb(beta, th * 4);
+  const Range rcu(cu_seqlens, cu_seqlens ? 4 * ((int64_t)n_seqs + 1) : 0);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rcu})
+    if (overlap(rf, *in)) return KDA_ERR_ALIAS;
+  const hipError_t err = kda::launch_check_inputs(
+      io == KDA_IO_BF16, q, k, v, log_alpha, beta, cu_seqlens, cu_seqlens ? n_seqs : 0, T,
+      heads, flags, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

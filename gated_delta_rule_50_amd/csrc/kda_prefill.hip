@@ -1202,13 +1202,13 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
   // 1.28 us per chunk on the 8K workload).
   const bool two = bf16_io && pairs * 8 > kCarryRound;
   const int64_t nblocks = ((pairs + 7) / 8) * 8 * (two ? 4 : 8);   // column-tile groups
-#ifndef KDA_SHORT_AVG_TOKENS
-#define KDA_SHORT_AVG_TOKENS 128
-#endif
   // batches of short sequences (mean length up to two chunks): one wave per
-  // tile, no pipeline (the single-sequence call always pipelines)
+  // tile, no pipeline (the single-sequence call always pipelines). Measured
+  // crossover: the short carry wins up to 128 tokens per sequence, ties at
+  // 256 and loses at 512.
+  constexpr int64_t kShortMeanTokens = 2 * kC;
   const bool short_seqs = bf16_io && !single && n_seqs > 0 &&
-                          T <= (int64_t)KDA_SHORT_AVG_TOKENS * n_seqs;
+                          T <= kShortMeanTokens * n_seqs;
   if (short_seqs)
     carry_short_kernel<bf16><<<(unsigned)(((pairs + 7) / 8) * 64), kWave, 0, stream>>>(
         inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H);

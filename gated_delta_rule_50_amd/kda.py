@@ -18,12 +18,13 @@ KDA_ERR_WORKSPACE, KDA_ERR_ALIAS, KDA_ERR_HIP, KDA_ERR_ALIGN = 4, 5, 6, 7
 KDA_IO_F32, KDA_IO_BF16 = 0, 1
 KDA_STATE_F32, KDA_STATE_BF16 = 0, 1
 KDA_FLAG_QK_L2NORM = 1
+KDA_BAD_QKV, KDA_BAD_GATE, KDA_BAD_BETA, KDA_BAD_CU = 1, 2, 4, 8
 CHUNK = 64
 HEAD_DIM = 128
 
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_phase",
-           "kda_decode_step", "kda_recurrent_fwd", "kda_rmsnorm_gate", "kda_status_string",
-           "kda_version")
+           "kda_decode_step", "kda_recurrent_fwd", "kda_rmsnorm_gate", "kda_check_inputs",
+           "kda_status_string", "kda_version")
 
 _LIB = None
 
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.kda_rmsnorm_gate.argtypes = [vp, vp, vp, ctypes.c_float, i64, i32, ctypes.c_int, vp,
                                        vp]
         L.kda_rmsnorm_gate.restype = ctypes.c_int
+        L.kda_check_inputs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                       ctypes.c_int, vp, vp]
+        L.kda_check_inputs.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.restype = i32
@@ -288,6 +292,32 @@ def rmsnorm_gate(o, gate, weight=None, eps=1e-6, *, y=None, stream=None):
     if st != KDA_OK:
         raise KDAError(st, "kda_rmsnorm_gate")
     return y
+
+
+def check_inputs(q, k, v, log_alpha, beta, cu_seqlens=None, *, flags=None, stream=None):
+    """Debug check of the documented preconditions (finite q, k, v, beta;
+    log_alpha finite and <= 0; cu_seqlens rising from 0 to T) on the device.
+    Same tensors as chunk_fwd, or the decode step's ([N, H, 128] as T = N).
+    With flags (a device int32 tensor of one element) the check is enqueued
+    and flags receives the OR of the KDA_BAD_* bits; without, the bits are
+    returned as an int (which waits for the stream)."""
+    dev = k.device
+    _io(k.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, k.dtype, dev)
+    _check(log_alpha, "log_alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    out = torch.empty(1, dtype=torch.int32, device=dev) if flags is None else flags
+    _check(out, "flags", torch.int32, dev)
+    T, H = int(k.shape[0]), int(k.shape[1])
+    n = 0 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    st = lib().kda_check_inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                _ptr(cu_seqlens), n, T, H, int(k.shape[2]), int(v.shape[2]),
+                                _io(k.dtype), _ptr(out), _stream(stream, dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_check_inputs")
+    return out if flags is not None else int(out.item())
 
 
 # Longest sequence routed to the recurrent kernel. The pages' serving notes

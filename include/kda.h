@@ -47,6 +47,7 @@
  *    cu_seqlens[0] = 0 and cu_seqlens[N] = T. Violations give unspecified
  *    values but never out-of-bounds accesses: kernels clamp every index, and
  *    a malformed cu_seqlens sets the workspace status word (below).
+ *    kda_check_inputs() checks all of them on request.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -303,6 +304,43 @@ kda_status kda_recurrent_fwd(const void *q, const void *k, const void *v,
 kda_status kda_rmsnorm_gate(const void *o, const void *gate,
                             const float *weight, float eps, int64_t rows,
                             int32_t dv, kda_io_dtype io, void *y,
+                            void *stream);
+
+/*
+ * kda_check_inputs - debug check of the preconditions the compute entry
+ * points document but cannot verify on the device.
+ *
+ * The gate is the natural log of a per-channel decay alpha in (0, 1] (the
+ * "Kimi Linear" review, section "The KDA State Update Equation", gives a
+ * decay per key channel in [0, 1]; alpha = 0 has no finite log), so every
+ * log_alpha element must be finite and <= 0; q, k, v and beta must be
+ * finite; a packed batch needs 0 = cu_seqlens[0] <= ... <= cu_seqlens[N] = T.
+ * The call reads the inputs once (the same tensors and layout as
+ * kda_chunk_fwd, or the decode step's with T = N) and writes to *flags, on
+ * the device and asynchronously on `stream`, the OR of
+ *   KDA_BAD_QKV   a non-finite element of q, k or v
+ *   KDA_BAD_GATE  a log_alpha element that is NaN, +-inf or > 0
+ *   KDA_BAD_BETA  a non-finite beta
+ *   KDA_BAD_CU    cu_seqlens not rising from 0 to T (only if cu_seqlens is
+ *                 not NULL; n_seqs is ignored when it is NULL)
+ * so 0 means every documented precondition holds. flags is one int32 of
+ * device memory owned by the caller (4-byte aligned), written by a kernel
+ * (no memset: the call may be captured in a HIP graph).
+ * Errors: KDA_ERR_NULL (flags NULL, or a tensor NULL with T > 0),
+ * KDA_ERR_SHAPE (T < 0, heads < 1, n_seqs < 1 with cu_seqlens, T * heads
+ * above 2^40), KDA_ERR_UNSUPPORTED (dk or dv != 128, unknown dtype, heads
+ * > 65535), KDA_ERR_ALIGN, KDA_ERR_ALIAS (flags inside an input),
+ * KDA_ERR_HIP.
+ */
+#define KDA_BAD_QKV 1
+#define KDA_BAD_GATE 2
+#define KDA_BAD_BETA 4
+#define KDA_BAD_CU 8
+kda_status kda_check_inputs(const void *q, const void *k, const void *v,
+                            const float *log_alpha, const float *beta,
+                            const int32_t *cu_seqlens, int32_t n_seqs,
+                            int64_t total_tokens, int32_t heads, int32_t dk,
+                            int32_t dv, kda_io_dtype io, int32_t *flags,
                             void *stream);
 
 /* Static description of a status code (never NULL). */

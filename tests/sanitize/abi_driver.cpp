@@ -11,7 +11,7 @@
 #include "kda.h"
 
 namespace kda {
-int g_chunk = 0, g_rec = 0, g_epi = 0;
+int g_chunk = 0, g_rec = 0, g_epi = 0, g_chk = 0;
 hipError_t launch_chunk_fwd(int, bool, bool, const void*, const void*, const void*, const float*,
                             const float*, const float*, const int32_t*, int32_t, int64_t, int32_t,
                             int64_t, void*, float*, int32_t*, int32_t*, uint8_t*, hipStream_t) {
@@ -29,6 +29,12 @@ hipError_t launch_recurrent_fwd(bool, bool, bool, const void*, const void*, cons
 hipError_t launch_rmsnorm_gate(bool, const void*, const void*, const float*, float, int64_t, void*,
                                hipStream_t) {
   ++g_epi;
+  return hipSuccess;
+}
+hipError_t launch_check_inputs(bool, const void*, const void*, const void*, const float*,
+                               const float*, const int32_t*, int32_t, int64_t, int32_t, int32_t*,
+                               hipStream_t) {
+  ++g_chk;
   return hipSuccess;
 }
 }  // namespace kda
@@ -112,10 +118,26 @@ int main() {
                                KDA_IO_BF16, at(0), nullptr), KDA_OK, "epilogue in place");
   expect((int)kda_rmsnorm_gate(at(0), at(MB), (const float*)at(2 * MB), -1.f, 64, 128,
                                KDA_IO_BF16, at(3 * MB), nullptr), KDA_ERR_SHAPE, "epilogue eps");
+  // input check
+  int32_t* fl = (int32_t*)at(10 * 64 * MB);
+  const int32_t* cu = (const int32_t*)at(6 * 64 * MB);
+  expect((int)kda_check_inputs(at(0), at(MB), at(2 * MB), (const float*)at(3 * MB),
+                               (const float*)at(4 * MB), cu, 3, 8, 2, 128, 128, KDA_IO_BF16, fl,
+                               nullptr), KDA_OK, "check valid");
+  expect((int)kda_check_inputs(at(0), at(MB), at(2 * MB), (const float*)at(3 * MB),
+                               (const float*)at(4 * MB), nullptr, 0, 0, 2, 128, 128, KDA_IO_F32,
+                               fl, nullptr), KDA_OK, "check T=0");
+  expect((int)kda_check_inputs(at(0), at(MB), at(2 * MB), (const float*)at(3 * MB),
+                               (const float*)at(4 * MB), cu, 3, 8, 2, 128, 128, KDA_IO_BF16,
+                               (int32_t*)at(MB + 64), nullptr), KDA_ERR_ALIAS, "check alias");
+  expect((int)kda_check_inputs(at(0), at(MB), at(2 * MB), (const float*)at(3 * MB),
+                               (const float*)at(4 * MB), cu, 3, 8, 2, 128, 128, (kda_io_dtype)4,
+                               fl, nullptr), KDA_ERR_UNSUPPORTED, "check io 4");
   for (int st = -1; st < 9; ++st)
     if (kda_status_string((kda_status)st) == nullptr) ++fails;
-  if (kda::g_chunk != 5 || kda::g_rec != 2 || kda::g_epi != 1) {
-    fprintf(stderr, "launch counts %d %d %d\n", kda::g_chunk, kda::g_rec, kda::g_epi);
+  if (kda::g_chunk != 5 || kda::g_rec != 2 || kda::g_epi != 1 || kda::g_chk != 2) {
+    fprintf(stderr, "launch counts %d %d %d %d\n", kda::g_chunk, kda::g_rec, kda::g_epi,
+            kda::g_chk);
     ++fails;
   }
   if (!fails) printf("abi driver ok\n");

@@ -39,6 +39,9 @@ def lib():
     L.kda_recurrent_fwd.restype = ctypes.c_int
     L.kda_rmsnorm_gate.argtypes = [vp, vp, vp, ctypes.c_float, i64, i32, ctypes.c_int, vp, vp]
     L.kda_rmsnorm_gate.restype = ctypes.c_int
+    L.kda_check_inputs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                   ctypes.c_int, vp, vp]
+    L.kda_check_inputs.restype = ctypes.c_int
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_version.restype = i32
@@ -328,3 +331,24 @@ def test_probe_library_rejects_bad_arguments():
     assert P.kdab_rmw(a, 0, 64, None) == -1
     assert P.kdab_mfma(s, 0, 64, None) == -1                     # no iterations
     assert P.kdab_valu(s, 10, (1 << 20) + 1, None) == -1         # grid too large
+
+
+def test_check_inputs_rejects_bad_arguments(lib):
+    """kda_check_inputs validates its arguments before any launch (fake
+    addresses, never dereferenced)."""
+    T, H = 10, 2
+    q, k, v = 0x100000, 0x200000, 0x300000
+    la, b, cu, fl = 0x400000, 0x500000, 0x600000, 0x700000
+    call = lib.kda_check_inputs
+    assert call(q, k, v, la, b, cu, 3, T, H, 128, 128, BF16, None, None) == NULL
+    assert call(q, None, v, la, b, cu, 3, T, H, 128, 128, BF16, fl, None) == NULL
+    assert call(q, k, v, la, b, cu, 3, -1, H, 128, 128, BF16, fl, None) == SHAPE
+    assert call(q, k, v, la, b, cu, 0, T, H, 128, 128, BF16, fl, None) == SHAPE
+    assert call(q, k, v, la, b, cu, 3, T, 0, 128, 128, BF16, fl, None) == SHAPE
+    assert call(q, k, v, la, b, cu, 3, T, H, 64, 128, BF16, fl, None) == UNSUP
+    assert call(q, k, v, la, b, cu, 3, T, H, 128, 128, 5, fl, None) == UNSUP
+    assert call(q + 8, k, v, la, b, cu, 3, T, H, 128, 128, BF16, fl, None) == ALIGN
+    assert call(q, k, v, la, b, cu, 3, T, H, 128, 128, BF16, fl + 2, None) == ALIGN
+    assert call(q, k, v, la, b, cu, 3, T, H, 128, 128, BF16, q + 64, None) == ALIAS
+    assert call(q, k, v, la, b, cu, 3, T, H, 128, 128, BF16, cu + 4, None) == ALIAS
+    assert call(q, k, v, la, b, cu, 3, 1 << 40, H, 128, 128, BF16, fl, None) == SHAPE
