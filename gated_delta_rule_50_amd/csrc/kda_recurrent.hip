@@ -51,6 +51,12 @@ constexpr int kRowPitch = 20;                  // LDS floats per 16-row group (b
 constexpr float kFoldBelow = 0x1p-40f;
 constexpr int kStaticLds = 4 * 8 * kRowPitch * 4;   // the four token-vector rows, bytes
 constexpr int kLdsPerCu = 160 * 1024;               // gfx950 LDS per CU
+// fp32 decode steps with at most this many 32-column waves use 16-column
+// slices. Graph-replayed steps of 32 heads: 1 sequence 2.84 -> 2.56 us,
+// 2 sequences even, 4 and 8 sequences slower (3.97 -> 4.33, 7.32 -> 9.66 us:
+// every wave stages the whole token vectors, so narrower waves repeat more
+// of that work once there are enough of them to fill the CUs).
+constexpr int64_t kNarrowMaxWaves = 128;
 
 // Sum of x over lanes l and l ^ 8 (DPP rotate by 8 inside each 16-lane row).
 __device__ __forceinline__ float sum_xor8(float x) {
@@ -157,17 +163,21 @@ __device__ __forceinline__ void fetch_token(TokenIn<IO>& x, const IO* q, const I
 }  // namespace
 
 // kSingle: exactly one token per sequence (the decode step), no token loop.
-// kWide: 64-column slices (lane: column quad lane % 16, rows
-// 32 (lane / 16) .. +31), so a lane's bf16 state row piece and the wave's
-// row of the slice fill whole 128-byte lines; 32-column slices otherwise
-// (lane: quad lane % 8, rows 16 (lane / 8) .. +15).
-template <class IO, class ST, bool kNorm, bool kSingle, bool kWide>
+// kCols: value columns per wave. 32 by default (lane: column quad lane % 8,
+// rows 16 (lane / 8) .. +15); 64 for the bf16-state decode step (lane: quad
+// lane % 16, rows 32 (lane / 16) .. +31), so a lane's bf16 state row piece
+// and the wave's row of the slice fill whole 128-byte lines; 16 for decode
+// steps over a few (sequence, head) pairs (lane: quad lane % 4, rows
+// 8 (lane / 4) .. +7), twice the waves with half the state each, since such
+// a step is bound by one wave's load latency rather than by bandwidth.
+template <class IO, class ST, bool kNorm, bool kSingle, int kCols>
 __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const ST* h0,
     const int32_t* __restrict__ cu, int64_t seq_len, int64_t T, int32_t H, int64_t pairs,
     IO* __restrict__ o, ST* h_final) {
-  constexpr int kCols = kWide ? 64 : 32;          // value columns per wave
+  static_assert(kCols == 16 || kCols == 32 || kCols == 64, "16-, 32- or 64-column slices");
+  constexpr bool kWide = kCols == 64;
   constexpr int kSl = kD / kCols;                  // waves per (sequence, head)
   constexpr int kQuads = kCols / 4;                // column quads per slice
   constexpr int kRows = kD / (64 / kQuads);        // key rows per lane
@@ -314,9 +324,13 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     const float e01 = sum_pair32(pe.x, pe.y), e23 = sum_pair32(pe.z, pe.w);
     const float p01 = sum_pair32(pr.x, pr.y), p23 = sum_pair32(pr.z, pr.w);
     float ec = sum_pair16(e01, e23), pc = sum_pair16(p01, p23);
-    if constexpr (!kWide) {
+    if constexpr (kCols <= 32) {   // lane bit 3
       ec = sum_xor8(ec);
       pc = sum_xor8(pc);
+    }
+    if constexpr (kCols == 16) {   // lane bit 2 (bit 3 already summed)
+      ec = sum_ror4(ec);
+      pc = sum_ror4(pc);
     }
     ec *= rk;
     pc *= rq;
@@ -363,7 +377,9 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     }
 
     // narrow slices: lanes l and l ^ 8 hold the same column
-    if (kWide || (lane & 8) == 0) o[(t * H + h) * kD + col0 + cq] = from_f<IO>(pc + qk * dc);
+    // lanes that differ only in the summed bits below bit 4 hold the same column
+    constexpr int kDup = kCols == 64 ? 0 : (kCols == 32 ? 8 : 12);
+    if ((lane & kDup) == 0) o[(t * H + h) * kD + col0 + cq] = from_f<IO>(pc + qk * dc);
   }
 
   if (h_final != nullptr) {
@@ -386,9 +402,12 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
                                 void* o, void* h_final, hipStream_t stream) {
   if (pairs == 0) return hipSuccess;
   const bool single = cu == nullptr && seq_len == 1;
-  // bf16 states in a decode step: 64-column slices, whole-line state rows
+  // bf16 states in a decode step: 64-column slices, whole-line state rows;
+  // fp32 decode steps over a few pairs (up to 32, one sequence of 32
+  // heads): 16-column slices
   const bool wide = single && bf16_state;
-  const int64_t blocks = (pairs + 7) / 8 * 8 * (wide ? 2 : 4);
+  const bool narrow = single && !bf16_state && pairs * 4 <= kNarrowMaxWaves;
+  const int64_t blocks = (pairs + 7) / 8 * 8 * (wide ? 2 : (narrow ? 8 : 4));
   dim3 grid((unsigned)blocks), block(64);
   // Resident workgroups per CU. With one or a few tokens per sequence the
   // kernel streams the states, and HBM serves that stream best with few
@@ -406,22 +425,26 @@ hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, cons
   else if (avg_len <= 2) cap = 8;
   else if (avg_len <= 4) cap = 10;
   const size_t lds_pad = cap > 0 ? (size_t)(kLdsPerCu / cap - kStaticLds) : 0;
-#define KDA_REC_LAUNCH(IO, ST, NORM, ONE, WIDE)                                              \
-  recurrent_fwd_kernel<IO, ST, NORM, ONE, WIDE><<<grid, block, lds_pad, stream>>>(           \
+#define KDA_REC_LAUNCH(IO, ST, NORM, ONE, COLS)                                              \
+  recurrent_fwd_kernel<IO, ST, NORM, ONE, COLS><<<grid, block, lds_pad, stream>>>(           \
       (const IO*)q, (const IO*)k, (const IO*)v, log_alpha, beta, (const ST*)h0, cu, seq_len, \
       T, H, pairs, (IO*)o, (ST*)h_final)
-#define KDA_REC_NORM(IO, ST, WIDE)                             \
+#define KDA_REC_NORM(IO, ST, COLS)                             \
   if (l2norm) {                                                \
-    if (single) KDA_REC_LAUNCH(IO, ST, true, true, WIDE);      \
-    else KDA_REC_LAUNCH(IO, ST, true, false, false);           \
+    if (single) KDA_REC_LAUNCH(IO, ST, true, true, COLS);      \
+    else KDA_REC_LAUNCH(IO, ST, true, false, 32);              \
   } else {                                                     \
-    if (single) KDA_REC_LAUNCH(IO, ST, false, true, WIDE);     \
-    else KDA_REC_LAUNCH(IO, ST, false, false, false);          \
+    if (single) KDA_REC_LAUNCH(IO, ST, false, true, COLS);     \
+    else KDA_REC_LAUNCH(IO, ST, false, false, 32);             \
   }
   if (bf16_io) {
-    if (bf16_state) { KDA_REC_NORM(bf16, bf16, true); } else { KDA_REC_NORM(bf16, float, false); }
+    if (bf16_state) { KDA_REC_NORM(bf16, bf16, 64); }
+    else if (narrow) { KDA_REC_NORM(bf16, float, 16); }
+    else { KDA_REC_NORM(bf16, float, 32); }
   } else {
-    if (bf16_state) { KDA_REC_NORM(float, bf16, true); } else { KDA_REC_NORM(float, float, false); }
+    if (bf16_state) { KDA_REC_NORM(float, bf16, 64); }
+    else if (narrow) { KDA_REC_NORM(float, float, 16); }
+    else { KDA_REC_NORM(float, float, 32); }
   }
 #undef KDA_REC_NORM
 #undef KDA_REC_LAUNCH

@@ -169,6 +169,26 @@ def test_matches_chunked_prefill():
     _check(p, host(orr), host(hr))
 
 
+@pytest.mark.parametrize("N", [1, 2, 9])
+def test_decode_step_slice_widths(N):
+    """fp32-state decode steps over at most 32 (sequence, head) pairs run
+    16-column slices, larger ones 32-column slices (1 x 32 and 2 x 32 pairs
+    sit on either side); both against the oracle over several steps."""
+    H = 32
+    S0 = workloads.make_decode_state(N, H, seed=59, std=0.02)
+    S = dev(S0)
+    ref = S0.astype(np.float64)
+    for step in range(4):
+        d = workloads.make_decode_step(N, H, seed=59, step=step, io="bf16")
+        bf = torch.bfloat16
+        o = kda.decode_step(dev(d.q, bf), dev(d.k, bf), dev(d.v, bf), dev(d.log_alpha),
+                            dev(d.beta), S)
+        torch.cuda.synchronize()
+        ro, ref = recurrent.decode_step(d.q, d.k, d.v, d.log_alpha, d.beta, ref)
+        assert rel_max_err(host(o), ro) <= TOL["bf16"][0], step
+        assert rel_fro_err(host(S), ref) <= TOL["bf16"][1], step
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_one_token_equals_decode_step(io):
     """L = 1 over N sequences in place is the decode step, bit for bit (the
