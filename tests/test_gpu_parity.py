@@ -372,6 +372,39 @@ def test_packed_equals_separate_bitwise():
         assert torch.equal(on, o[s:e]) and torch.equal(hn[0], hf[n])
 
 
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_identity_padding(path):
+    """Tokens with k = 0, v = 0, beta = 0 and log alpha = 0 leave the state
+    unchanged: appending 28 of them (and 61 to a second sequence) changes
+    neither the final states nor the outputs of the real tokens, bit for
+    bit, on either forward path."""
+    lens, pads = [100, 3], [28, 61]
+    p = workloads.make_prefill(lens, H=2, seed=36, io="bf16", h0_std=0.05)
+    parts = {n: [] for n in ("q", "k", "v", "log_alpha", "beta")}
+    for n_, (L, P) in enumerate(zip(lens, pads)):
+        s0 = int(p.cu_seqlens[n_])
+        for name in parts:
+            x = getattr(p, name)[s0:s0 + L]
+            pad = np.zeros((P,) + x.shape[1:], x.dtype)
+            if name == "q":
+                pad = p.q[:P].copy()           # any query: its output is not compared
+            parts[name].append(np.concatenate([x, pad]))
+    padded = {name: np.concatenate(v) for name, v in parts.items()}
+    cu_pad = np.concatenate([[0], np.cumsum([L + P for L, P in zip(lens, pads)])]).astype(np.int32)
+    bf = torch.bfloat16
+    fwd = kda.chunk_fwd if path == "chunk" else kda.recurrent_fwd
+    o1, h1 = fwd(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta),
+                 dev(p.h0), dev(p.cu_seqlens, torch.int32))
+    o2, h2 = fwd(dev(padded["q"], bf), dev(padded["k"], bf), dev(padded["v"], bf),
+                 dev(padded["log_alpha"]), dev(padded["beta"]), dev(p.h0),
+                 dev(cu_pad, torch.int32))
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    for n_, L in enumerate(lens):
+        a, b = int(p.cu_seqlens[n_]), int(cu_pad[n_])
+        assert torch.equal(o1[a:a + L], o2[b:b + L]), n_
+
+
 def test_decode_steps_match_prefill():
     """64 single-token decode steps equal one prefill over the same tokens."""
     N, H, steps = 4, 2, 64
