@@ -103,3 +103,33 @@ def test_prefill_then_decode_graph():
         for a, b in zip(got, ref):
             assert torch.equal(a, b), rep
     assert np.isfinite(pre.o.float().cpu().numpy()).all()
+
+
+def test_input_check_in_a_graph():
+    """kda_check_inputs clears its flag word with a kernel, so a captured
+    check reports each replay's inputs: clean, then with a planted positive
+    gate, then clean again (the inputs edited eagerly between replays)."""
+    p = workloads.make_prefill([50, 14], H=2, seed=85, io="bf16")
+    bf = torch.bfloat16
+    args = [dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta),
+            dev(p.cu_seqlens, torch.int32)]
+    flags = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kda.check_inputs(*args, flags=flags)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kda.check_inputs(*args, flags=flags)
+    la = args[3]
+    for rep, (value, want) in enumerate(((None, 0), (0.25, kda.KDA_BAD_GATE), (None, 0))):
+        la.copy_(dev(p.log_alpha))
+        if value is not None:
+            la[63, 1, 127] = value
+        flags.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(flags.item()) == want, rep
