@@ -41,6 +41,17 @@ __device__ __forceinline__ bool finite8(const float* p) {
   return finite_f(a.x) && finite_f(a.y) && finite_f(a.z) && finite_f(a.w) && finite_f(b.x) &&
          finite_f(b.y) && finite_f(b.z) && finite_f(b.w);
 }
+// Eight gates, each finite and <= 0 (NaN fails the comparison; -inf, which
+// is alpha = 0, fails the finiteness test).
+__device__ __forceinline__ bool gates_ok8(const float* p) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  bool ok = true;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ok = ok && x[e] <= 0.f && finite_f(x[e]);
+  return ok;
+}
 
 __global__ void clear_flags_kernel(int32_t* flags) { flags[0] = 0; }
 
@@ -56,13 +67,7 @@ __global__ __launch_bounds__(kCheckThreads) void check_inputs_kernel(
   const int64_t stride = (int64_t)gridDim.x * kCheckThreads;
   for (int64_t i = (int64_t)blockIdx.x * kCheckThreads + threadIdx.x; i < n8; i += stride) {
     if (!(finite8(q + 8 * i) && finite8(k + 8 * i) && finite8(v + 8 * i))) bad |= kBadQKV;
-    const float4 a = reinterpret_cast<const float4*>(log_alpha + 8 * i)[0];
-    const float4 b = reinterpret_cast<const float4*>(log_alpha + 8 * i)[1];
-    // NaN fails every comparison, so !(x <= 0) also catches it; -inf is
-    // alpha = 0, outside (0, 1]
-    const bool ok = a.x <= 0.f && a.y <= 0.f && a.z <= 0.f && a.w <= 0.f && b.x <= 0.f &&
-                    b.y <= 0.f && b.z <= 0.f && b.w <= 0.f && finite8(log_alpha + 8 * i);
-    if (!ok) bad |= kBadGate;
+    if (!gates_ok8(log_alpha + 8 * i)) bad |= kBadGate;
   }
   for (int64_t i = (int64_t)blockIdx.x * kCheckThreads + threadIdx.x; i < nb; i += stride)
     if (!finite_f(beta[i])) bad |= kBadBeta;

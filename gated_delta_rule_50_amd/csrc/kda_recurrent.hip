@@ -177,7 +177,6 @@ __global__ __launch_bounds__(64) void recurrent_fwd_kernel(
     const int32_t* __restrict__ cu, int64_t seq_len, int64_t T, int32_t H, int64_t pairs,
     IO* __restrict__ o, ST* h_final) {
   static_assert(kCols == 16 || kCols == 32 || kCols == 64, "16-, 32- or 64-column slices");
-  constexpr bool kWide = kCols == 64;
   constexpr int kSl = kD / kCols;                  // waves per (sequence, head)
   constexpr int kQuads = kCols / 4;                // column quads per slice
   constexpr int kRows = kD / (64 / kQuads);        // key rows per lane
