@@ -33,6 +33,9 @@ kind (in-place update for the decode-shaped paths, copy otherwise).
 (T = 131072) and on the 16-sequence packed batch.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--long-configs]
+
+With KDA_ROCTX=1 each timed call is wrapped in a named roctx range
+(kda_chunk_fwd, kda_decode_step) for rocprofv3 --marker-trace.
 """
 from __future__ import annotations
 
@@ -541,14 +544,25 @@ def main():
     do = torch.empty_like(dv)
     pairs = cfg4.n_seqs * cfg4.H
 
+    # KDA_ROCTX=1: named ranges around the two calls of a step, for
+    # rocprofv3 --marker-trace (torch's range markers are roctx on ROCm)
+    marks = os.environ.get("KDA_ROCTX") == "1"
+
+    def ranged(name, fn):
+        if marks:
+            torch.cuda.nvtx.range_push(name)
+        fn()
+        if marks:
+            torch.cuda.nvtx.range_pop()
+
     def step(ev=None):
         # one prefill call (pipelined inside the library) + one decode step
         if ev is not None:
             ev[0].record()
-        pre.run()
+        ranged("kda_chunk_fwd", pre.run)
         if ev is not None:
             ev[1].record()
-        decode_step(dq, dk, dv, dla, db, S, o=do)
+        ranged("kda_decode_step", lambda: decode_step(dq, dk, dv, dla, db, S, o=do))
         if ev is not None:
             ev[2].record()
 
