@@ -81,9 +81,10 @@ def test_recurrent_long_sequence_strong_decay(io):
     _check(p, o, hf)
 
 
+@pytest.mark.parametrize("norm", [False, True])
 @pytest.mark.parametrize("state", ["f32", "bf16"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_recurrent_decay_underflow(io, state):
+def test_recurrent_decay_underflow(io, state, norm):
     """Decays the token loop must fold into the state before they leave the
     safe range: channels 0-15 multiplied by e^-200 (zero in fp32) every fifth
     token, channels 16-31 by e^-3 every token (a fold every ~9 tokens),
@@ -92,8 +93,13 @@ def test_recurrent_decay_underflow(io, state):
     p.log_alpha[::5, :, :16] = -200.0
     p.log_alpha[:, :, 16:32] = -3.0
     p.log_alpha[:, :, 32:48] = 0.0
-    o, hf = _run(p, state)
-    _check(p, o, hf, state)
+    if norm:   # un-normalised q, k for the in-kernel L2Norm (x0.5 is exact in bf16)
+        p.q *= 3.0
+        p.k *= 0.5
+        if io == "bf16":
+            p.q = workloads.round_bf16(p.q)   # the values the device receives
+    o, hf = _run(p, state, norm=norm)
+    _check(p, o, hf, state, norm=norm)
 
 
 @pytest.mark.parametrize("state", ["f32", "bf16"])
