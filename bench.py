@@ -5,35 +5,45 @@ One step is one pass of the whole hot path: a chunked prefill call on the
 8K workload (one sequence, T = 8192, H = 32, d_k = d_v = 128, bf16 q/k/v,
 fp32 gates and state, h0 = 0) followed by one decode step on the decode
 workload (256 sequences x 32 heads, fp32 states of 512 MiB updated in place).
-Inputs are synthetic (seeded generators), resident in HBM before timing.
+Inputs are synthetic (seeded generators), resident in HBM before timing;
+every input set is drawn before the first timed call.
 
 Printed: ONE JSON line. ``value`` is prefill tokens/s (T / mean prefill call
 time from HIP events on the caller's stream); decode tokens/s is reported
-beside it. ``timing`` gives the median, p10 and p90 of the timed calls and
-of prefill calls made with cold inputs (each after a 1 GiB scrub write). After the timed steps the prefill's kernels are also launched one
-at a time (phase entry point, all chunks per launch) to measure each
-kernel's own duration; ``kernels`` holds those and the decode kernel's, and
-``roofline`` describes the one with the longest mean duration.
+beside it. ``roofline`` is the prefill call's (the headline path: algorithmic
+bytes of the call over its mean duration, with the call's measured HBM
+traffic from the committed counter summary), ``decode_roofline`` the decode
+step's. ``timing`` gives the median, p10 and p90 of the timed calls and of
+prefill calls made with cold inputs (each after a 1 GiB scrub write). After
+the timed steps the prefill's kernels are also launched one at a time (phase
+entry point) to measure each kernel's own duration (``kernels``).
+
+``long_configs``: the prefill on the long single sequence (T = 131072, strong
+decay, nonzero h0) and on the 16-sequence packed batch, each with its own
+roofline and traffic. ``sweep_h16``: one sequence of 16 heads at T = 2K ..
+64K, the shape of the pages' kernel-speed figure (their times are quoted as
+context; the pages do not name the hardware).
 
 ``extensions`` times the operator's optional paths, each on its own
 workload with its own roofline: the fused multi-token recurrent call
 (256 sequences x 32 heads x L = 4 and 64 new tokens; the L = 64 batch also
 through the chunked path, which is the faster one there), the decode step with a
 bf16 state, batch-1 decode (one sequence x 32 heads) launched step by step
-and replayed from a HIP graph, the prefill with in-kernel q/k L2Norm, and
-the RMSNorm x sigmoid-gate epilogue over the prefill's 8192 x 32 output
-rows.
+and replayed from a HIP graph, the prefill with in-kernel q/k L2Norm, the 8K
+prefill with fp32 I/O, the 8K prefill with decays strong enough that every
+chunk takes the exact per-element diagonal blocks, and the RMSNorm x
+sigmoid-gate epilogue over the prefill's 8192 x 32 output rows.
 
-``ceilings`` holds what plain kernels achieve on the same GPU (streaming
-read, copy, in-place update; bf16 MFMA and fp32 FMA loops); each roofline
-object adds ``achievable`` and ``frac_achievable`` against the ceiling of its
-kind (in-place update for the decode-shaped paths, copy otherwise).
+``probes`` holds what plain kernels (probes/ceilings.hip) reach on the same
+GPU: streaming read, copy, in-place update, bf16 MFMA and fp32 FMA loops.
+They are reference rates, not ceilings: a roofline object carries
+``frac_achievable`` only where its probe is at least as fast as the kernel.
 
-``--long-configs`` adds the prefill on the long single sequence
-(T = 131072) and on the 16-sequence packed batch.
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-long-configs]
+                    [--no-sweep] [--only WORKLOAD]
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--long-configs]
-
+``--only`` times one workload's prefill calls and nothing else (for counter
+runs): bench_step, long_T131072, packed_16_sequences.
 With KDA_ROCTX=1 each timed call is wrapped in a named roctx range
 (kda_chunk_fwd, kda_decode_step) for rocprofv3 --marker-trace.
 """
@@ -47,13 +57,14 @@ import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 import numpy as np
 
 METRIC = "KDA prefill tokens/s (H=32,d=128,T=8K) + decode tokens/s; % MFMA/HBM peak"
 ROOT = Path(__file__).resolve().parent
-TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_bench_step.txt"
+PROFILES = ROOT / "profiles"
 COPY_BYTES = 1 << 30        # the calibration copy reads and writes 1 GiB
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
@@ -76,7 +87,7 @@ FLOPS_RECURRENT = 7 * D * D                                # 114688
 # fp32 vector peak, as published for MI355X: 256 CUs x 256 flops per cycle x
 # 2.4 GHz. Plain (unpacked) FMAs reach it too on this chip: a loop of
 # independent v_fma_f32 measures about 124 TFLOP/s at the 2.2 GHz the
-# shader clock holds under load (the ceilings' probe reports it per run).
+# shader clock holds under load (the FMA probe reports it per run).
 FP32_VALU_TFLOPS = 256 * 256 * 2.4e9 / 1e12                 # 157.3
 # Epilogue, per row of 128 channels (bf16): o and gate read, y written.
 EPILOGUE_BYTES = 3 * 256
@@ -93,11 +104,17 @@ def _parse():
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--no-extensions", action="store_true",
                     help="skip the timings of the optional paths (shorter counter runs)")
-    ap.add_argument("--no-ceilings", action="store_true",
+    ap.add_argument("--no-probes", action="store_true",
                     help="skip the plain-kernel probes of achievable bandwidth and FLOP rate")
-    ap.add_argument("--long-configs", action="store_true",
-                    help="also time the prefill on the long single sequence (T = 131072) and "
-                         "the 16-sequence packed batch (about a minute of input generation)")
+    ap.add_argument("--no-long-configs", action="store_true",
+                    help="skip the prefill on the long single sequence (T = 131072) and the "
+                         "16-sequence packed batch (their inputs take about a minute to draw)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 16-head length sweep")
+    ap.add_argument("--only", choices=("bench_step", "long_T131072", "packed_16_sequences"),
+                    help="time only this workload's prefill calls (counter runs)")
+    ap.add_argument("--workload", default="bench_step",
+                    help="workload name written by --summarize-pmc")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy first (counter scale factor)")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
@@ -151,11 +168,11 @@ def _pmc_means(run_dir, counter):
             for k, v in per.items()}
 
 
-def summarize_pmc(fetch_dir, write_dir):
+def summarize_pmc(fetch_dir, write_dir, workload):
     f, w = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
     fr = COPY_BYTES / (f["copy"] * 1024.0)
     wr = COPY_BYTES / (w["copy"] * 1024.0)
-    lines = [f"sources_sha256 = {sources_hash()}",
+    lines = [f"workload = {workload}", f"sources_sha256 = {sources_hash()}",
              f"copy_read_factor = {fr:.6f}", f"copy_write_factor = {wr:.6f}"]
     for k in ("chunk_map", "intra", "carry", "decode"):
         if k in f and k in w:
@@ -206,13 +223,15 @@ def summarize_mfma(run_dir, durations_us=None):
     print("\n".join(lines))
 
 
-def load_traffic():
-    """Scaled HBM bytes per launch for each kernel, or {} if the committed
-    counter readings were taken on other kernel sources."""
-    if not TRAFFIC_FILE.exists():
+def load_traffic(workload="bench_step"):
+    """Scaled HBM bytes per launch for each kernel of a workload, from the
+    committed counter summary profiles/hbm_traffic_<workload>.txt, or {} if
+    there is none or it was taken on other kernel sources."""
+    path = PROFILES / f"hbm_traffic_{workload}.txt"
+    if not path.exists():
         return {}
     kv = {}
-    for line in TRAFFIC_FILE.read_text().splitlines():
+    for line in path.read_text().splitlines():
         if "=" in line and not line.lstrip().startswith("#"):
             key, val = (x.strip() for x in line.split("=", 1))
             kv[key] = val
@@ -220,10 +239,17 @@ def load_traffic():
         return {}
     fr, wr = float(kv["copy_read_factor"]), float(kv["copy_write_factor"])
     out = {}
-    for k in ("intra", "carry", "decode"):
+    for k in ("chunk_map", "intra", "carry", "decode"):
         if f"{k}_fetch_KiB" in kv:
             out[k] = (float(kv[f"{k}_fetch_KiB"]) * fr + float(kv[f"{k}_write_KiB"]) * wr) * 1024
     return out
+
+
+def prefill_traffic(traffic):
+    """Bytes one prefill call moves (its kernels' counter readings), or None."""
+    if "intra" not in traffic or "carry" not in traffic:
+        return None
+    return sum(traffic.get(k, 0.0) for k in ("chunk_map", "intra", "carry"))
 
 
 def _events(torch, n):
@@ -308,16 +334,16 @@ def cold_prefill(torch, pre, reps):
     return _spread([e[0].elapsed_time(e[1]) for e in ev])
 
 
-def ceilings(torch):
-    """Achievable rates of plain kernels on this GPU (the probes library built
-    beside the operator): streaming read, nontemporal copy and in-place
-    update of 1 GiB buffers, a bf16 MFMA loop and an fp32 FMA loop. Median of
-    five launches each, HIP events on the launch stream."""
+def probes(torch):
+    """Rates plain kernels reach on this GPU (probes/ceilings.hip): streaming
+    read, nontemporal copy and in-place update of 1 GiB buffers, a bf16 MFMA
+    loop and an fp32 FMA loop. Median of five launches each, HIP events on
+    the launch stream."""
     import ctypes
-    from gated_delta_rule_50_amd.build import CEIL_LIB
-    if not CEIL_LIB.exists():
-        raise RuntimeError(f"{CEIL_LIB} is not built; run `python -m gated_delta_rule_50_amd.build`")
-    L = ctypes.CDLL(str(CEIL_LIB))
+    from probes.build import LIB as PROBE_LIB
+    if not PROBE_LIB.exists():
+        raise RuntimeError(f"{PROBE_LIB} is not built; run `python -m probes.build`")
+    L = ctypes.CDLL(str(PROBE_LIB))
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.kdab_read.argtypes = [vp, i64, vp, i32, vp]
     L.kdab_copy.argtypes = [vp, vp, i64, i32, i32, vp]
@@ -361,27 +387,45 @@ def ceilings(torch):
     flops = wg * 256 * 32 * iters * 2
     out["valu_fp32_TFLOPs"] = flops / med_us(lambda: L.kdab_valu(ps, iters, wg, st)) / 1e6
     del a, b, sink
-    out["note"] = ("measured ceilings of plain kernels on this GPU; roofline fractions use the "
-                   "published peaks, frac_achievable these")
+    out["note"] = ("rates of plain grid-stride kernels on this GPU, for reference: roofline "
+                   "fractions use the published peaks; a roofline carries frac_achievable "
+                   "against the probe of its kind only where the probe is at least as fast "
+                   "as the kernel (the decode step and the epilogue outrun these probes)")
     return out
 
 
-def _with_ceiling(roof, ceil, key):
-    """Adds the measured ceiling of the same kind to a roofline object."""
-    if ceil and key in ceil:
-        roof["achievable"] = ceil[key]
-        roof["frac_achievable"] = roof["achieved"] / ceil[key]
+def _with_probe(roof, probe, key):
+    """Adds the probe rate of the same kind to a roofline object, and the
+    fraction of it only when the probe bounds the kernel."""
+    if probe and key in probe:
+        roof["probe"] = probe[key]
+        if roof["achieved"] <= probe[key]:
+            roof["frac_achievable"] = roof["achieved"] / probe[key]
+        else:
+            roof["exceeds_probe"] = True
     return roof
 
 
-def _hbm(alg_bytes, us):
+def _hbm(alg_bytes, us, traffic=None):
     gbps = alg_bytes / (us * 1e-6) / 1e9
-    return {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": gbps / HBM_PEAK_GBPS}
+    roof = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic}
+    if traffic is not None:
+        roof["traffic_ratio"] = traffic / alg_bytes
+    return roof
 
 
-def extensions(torch, d, pre_args, steps, warmup):
-    """Timings of the optional paths (module docstring), inputs resident."""
+def prefill_alg_bytes(T, H, N, io_bytes=2, h0=False):
+    """Algorithmic bytes of one prefill call: per token-head q, k, v, o in
+    the I/O type, log_alpha fp32 and beta fp32; per (sequence, head) h_final
+    (and h0 when given)."""
+    per_th = 4 * D * io_bytes + D * 4 + 4
+    return T * H * per_th + (2 if h0 else 1) * N * H * STATE_BYTES
+
+
+def extensions(torch, d, pre_args, steps, warmup, extra=None, us_8k=None):
+    """Timings of the optional paths (module docstring), inputs resident.
+    extra: device inputs of the fp32 and exact-diagonal 8K prefills."""
     from gated_delta_rule_50_amd import Prefill, Recurrent, decode_step, rmsnorm_gate, workloads
     bf = torch.bfloat16
     out = {}
@@ -462,6 +506,24 @@ def extensions(torch, d, pre_args, steps, warmup):
         "workload": "the 8K prefill with KDA_FLAG_QK_L2NORM", "us": us,
         "tokens_per_s": pre_args[0].shape[0] / (us * 1e-6)}
     o = pre_n.o
+    for name, what in (("fp32_8k", "the 8K x 32-head prefill with fp32 q/k/v/o (fp32 "
+                                    "intermediates)"),
+                       ("exact_diag_8k", "the 8K x 32-head prefill, bf16, with half the "
+                                         "channels decaying by e^-3..e^-4 per token, so every "
+                                         "16-token diagonal block is evaluated per element")):
+        if not extra or name not in extra:
+            continue
+        x = extra[name]
+        pre_x = Prefill(x["q"], x["k"], x["v"], x["la"], x["beta"], None, None)
+        us = _time_calls(torch, pre_x.run, steps, warmup)
+        io_b = 4 if x["q"].dtype == torch.float32 else 2
+        alg = prefill_alg_bytes(x["T"], x["H"], 1, io_b)
+        out["prefill_" + name] = {"workload": what, "us": us,
+                                  "tokens_per_s": x["T"] / (us * 1e-6), "alg_bytes": alg,
+                                  "roofline": _hbm(alg, us)}
+        if us_8k:
+            out["prefill_" + name]["time_vs_bf16_8k"] = us / us_8k
+        del pre_x
     rows = o.shape[0] * o.shape[1]
     e = workloads.make_epilogue(rows, seed=76, io="bf16")
     gate, w = d(e.gate, bf).view(o.shape), d(e.weight)
@@ -473,36 +535,106 @@ def extensions(torch, d, pre_args, steps, warmup):
     return out
 
 
-def long_configs(torch, d, steps, warmup):
-    """Prefill throughput on the long-context and packed variable-length
-    workloads (parity cases of their own, timed here for their scaling)."""
-    from gated_delta_rule_50_amd import Prefill, workloads
-    bf = torch.bfloat16
-    out = {}
-    for cid, name in ((2, "long_T131072"), (3, "packed_16_sequences")):
-        p = workloads.config(cid).prefill()
-        lens = np.diff(p.cu_seqlens)
-        pre = Prefill(d(p.q, bf), d(p.k, bf), d(p.v, bf), d(p.log_alpha), d(p.beta),
-                      None if p.h0 is None else d(p.h0), d(p.cu_seqlens, torch.int32))
-        T, H, N = p.T, p.H, p.N
-        del p
-        us = _time_calls(torch, pre.run, max(4, steps // 2), max(2, warmup // 2))
-        alg = T * H * PREFILL_BYTES + 2 * N * H * STATE_BYTES
-        out[name] = {
-            "workload": f"{N} sequence(s), lengths {int(lens.min())}..{int(lens.max())}, "
+SWEEP_T = (2048, 4096, 8192, 16384, 32768, 65536)
+SWEEP_H = 16
+
+
+def draw_inputs(names):
+    """Host inputs of the extra prefill workloads, drawn concurrently before
+    any timing (the generators release the interpreter lock while drawing)."""
+    from gated_delta_rule_50_amd import workloads
+    makers = {
+        "long_T131072": lambda: workloads.config(2).prefill(),
+        "packed_16_sequences": lambda: workloads.config(3).prefill(),
+        "sweep_h16": lambda: workloads.make_prefill([SWEEP_T[-1]], SWEEP_H, seed=1600,
+                                                    io="bf16"),
+        "fp32_8k": lambda: workloads.make_prefill([8192], 32, seed=1101, io="f32"),
+        "exact_diag_8k": lambda: workloads.make_prefill([8192], 32, seed=1201, io="bf16",
+                                                        decay="extreme"),
+    }
+    if not names:
+        return {}
+    with ThreadPoolExecutor(max_workers=len(names)) as ex:
+        futs = {n: ex.submit(makers[n]) for n in names}
+        return {n: f.result() for n, f in futs.items()}
+
+
+def to_device(torch, d, p):
+    """Device copies of a host prefill batch (bf16 or fp32 q/k/v)."""
+    dt = torch.bfloat16 if p.io == "bf16" else torch.float32
+    return {"q": d(p.q, dt), "k": d(p.k, dt), "v": d(p.v, dt), "la": d(p.log_alpha),
+            "beta": d(p.beta), "h0": None if p.h0 is None else d(p.h0),
+            "cu": d(p.cu_seqlens, torch.int32), "T": p.T, "H": p.H, "N": p.N,
+            "lens": np.diff(p.cu_seqlens)}
+
+
+def long_config(torch, x, name, steps, warmup):
+    """Prefill throughput on the long-context or packed variable-length
+    workload (parity cases of their own, timed here for their scaling)."""
+    from gated_delta_rule_50_amd import Prefill
+    pre = Prefill(x["q"], x["k"], x["v"], x["la"], x["beta"], x["h0"], x["cu"])
+    us = _time_calls(torch, pre.run, max(4, steps // 2), max(2, warmup // 2))
+    T, H, N, lens = x["T"], x["H"], x["N"], x["lens"]
+    alg = prefill_alg_bytes(T, H, N, 2, h0=x["h0"] is not None)
+    del pre
+    torch.cuda.empty_cache()
+    return {"workload": f"{N} sequence(s), lengths {int(lens.min())}..{int(lens.max())}, "
                         f"T={T}, H={H}, bf16 q/k/v, h0 ~N(0,0.02)",
             "us": us, "tokens_per_s": T / (us * 1e-6), "alg_bytes": alg,
             "longest_chain_chunks": int((lens.max() + C - 1) // C),
-            "roofline": _hbm(alg, us)}
+            "roofline": _hbm(alg, us, prefill_traffic(load_traffic(name)))}
+
+
+def sweep_h16(torch, x, steps, warmup):
+    """One sequence of 16 heads at T = 2K .. 64K (prefixes of one seeded
+    64K-token batch): the operator shape of the pages' kernel-speed figure."""
+    from gated_delta_rule_50_amd import Prefill
+    rows = []
+    for T in SWEEP_T:
+        pre = Prefill(x["q"][:T], x["k"][:T], x["v"][:T], x["la"][:T], x["beta"][:T])
+        us = _time_calls(torch, pre.run, steps, warmup)
+        alg = prefill_alg_bytes(T, SWEEP_H, 1)
+        rows.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6),
+                     "frac_hbm": alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                     "chunks": (T + C - 1) // C})
         del pre
-        torch.cuda.empty_cache()
-    return out
+    torch.cuda.empty_cache()
+    return {"workload": f"1 sequence, H={SWEEP_H}, d=128, bf16 q/k/v, h0=0",
+            "rows": rows,
+            "pages_context": "the pages' kernel-speed figure gives about 2 ms at 2K and about "
+                             "32 ms at 64K tokens for this shape (batch 1, 16 heads, head "
+                             "dimension 128) without naming the hardware or whether the time "
+                             "covers more than the forward pass: context, not a target"}
+
+
+def only_workload(torch, d, name, steps, warmup):
+    """Times one workload's prefill calls and nothing else (counter runs);
+    for bench_step, the step's prefill call and decode step."""
+    from gated_delta_rule_50_amd import Prefill, decode_step, workloads
+    if name == "bench_step":
+        x = to_device(torch, d, workloads.config(1).prefill())
+        cfg4 = workloads.config(4)
+        S = d(workloads.make_decode_state(cfg4.n_seqs, cfg4.H, cfg4.seed))
+        ds = workloads.make_decode_step(cfg4.n_seqs, cfg4.H, cfg4.seed, 0, io=cfg4.io)
+        bf = torch.bfloat16
+        dargs = (d(ds.q, bf), d(ds.k, bf), d(ds.v, bf), d(ds.log_alpha), d(ds.beta), S)
+    else:
+        x = to_device(torch, d, draw_inputs([name])[name])
+        dargs = None
+    pre = Prefill(x["q"], x["k"], x["v"], x["la"], x["beta"], x["h0"], x["cu"])
+
+    def call():
+        pre.run()
+        if dargs is not None:
+            decode_step(*dargs)
+    us = _time_calls(torch, call, steps, warmup)
+    print(json.dumps({"only": name, "us_per_call": us, "calls": steps + warmup}))
 
 
 def main():
     args = _parse()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, args.workload)
         return
     if args.summarize_mfma:
         durs = dict((k, float(v)) for k, v in (x.split("=", 1) for x in args.durations or []))
@@ -525,14 +657,34 @@ def main():
 
     from gated_delta_rule_50_amd import Prefill, decode_step, lib, workloads
     lib()  # fail loudly if the HIP library is missing
-
-    cfg1 = workloads.config(1)
-    p = cfg1.prefill()
     bf = torch.bfloat16
 
     def d(x, dt=torch.float32):
         return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dt)
 
+    if args.only:
+        only_workload(torch, d, args.only, args.steps, args.warmup)
+        return
+
+    # every input set is drawn before the first timed call
+    t_gen = time.perf_counter()
+    names = []
+    if not args.no_long_configs:
+        names += ["long_T131072", "packed_16_sequences"]
+    if not args.no_sweep:
+        names.append("sweep_h16")
+    if not args.no_extensions:
+        names += ["fp32_8k", "exact_diag_8k"]
+    if names:
+        print(f"drawing inputs: {', '.join(names)}", file=sys.stderr, flush=True)
+    host = draw_inputs(names)
+    extra = {}
+    for n in list(host):
+        extra[n] = to_device(torch, d, host.pop(n))
+    gen_s = time.perf_counter() - t_gen
+
+    cfg1 = workloads.config(1)
+    p = cfg1.prefill()
     pre_args = (d(p.q, bf), d(p.k, bf), d(p.v, bf), d(p.log_alpha), d(p.beta), None,
                 d(p.cu_seqlens, torch.int32))
     pre = Prefill(*pre_args)
@@ -556,7 +708,7 @@ def main():
             torch.cuda.nvtx.range_pop()
 
     def step(ev=None):
-        # one prefill call (pipelined inside the library) + one decode step
+        # one prefill call + one decode step
         if ev is not None:
             ev[0].record()
         ranged("kda_chunk_fwd", pre.run)
@@ -572,30 +724,30 @@ def main():
     evs = [_events(torch, 3) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
+    for s_ in range(args.steps):
+        step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     prefill_ms = [ev[0].elapsed_time(ev[1]) for ev in evs]
     decode_ms = [ev[1].elapsed_time(ev[2]) for ev in evs]
 
-    # Per-kernel characterisation after the timed steps: the prefill's three
-    # kernels launched one at a time over all chunks (the phase entry point),
-    # so each kernel's own duration is measured on the launch stream.
+    # Per-kernel characterisation after the timed steps: the prefill's
+    # kernels launched one at a time over all chunks (the phase entry
+    # point), so each kernel's own duration is measured on the launch stream.
     for _ in range(args.warmup):
         for ph in range(3):
             pre.run_phase(ph)
     torch.cuda.synchronize()
     pevs = [_events(torch, 4) for _ in range(args.steps)]
-    for s in range(args.steps):
-        pevs[s][0].record()
+    for s_ in range(args.steps):
+        pevs[s_][0].record()
         for ph in range(3):
             pre.run_phase(ph)
-            pevs[s][1 + ph].record()
+            pevs[s_][1 + ph].record()
     torch.cuda.synchronize()
 
-    names = ["chunk_map", "intra", "carry"]
-    dur = {n: [ev[i].elapsed_time(ev[i + 1]) for ev in pevs] for i, n in enumerate(names)}
+    names_k = ["chunk_map", "intra", "carry"]
+    dur = {n: [ev[i].elapsed_time(ev[i + 1]) for ev in pevs] for i, n in enumerate(names_k)}
     dur["decode"] = decode_ms
     mean = {n: float(np.mean(v)) for n, v in dur.items()}
     t_pre = float(np.mean(prefill_ms)) * 1e-3
@@ -620,16 +772,23 @@ def main():
             gbps = kdesc["alg_bytes"] / (kdesc["mean_us"] * 1e-6) / 1e9
             kdesc["achieved_GBps"] = gbps
             kdesc["frac"] = gbps / HBM_PEAK_GBPS
-    traffic = load_traffic()
+    traffic = load_traffic("bench_step")
     for n, b in traffic.items():
-        kernels[n]["traffic_bytes"] = b
-    dom = max(("intra", "carry", "decode"), key=lambda n: kernels[n]["mean_us"])
-    kd = kernels[dom]
-    roofline = {"bound": "hbm", "achieved": kd["achieved_GBps"], "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": kd["frac"], "traffic": traffic.get(dom),
-                "kernel": dom}
+        if n in kernels:
+            kernels[n]["traffic_bytes"] = b
+            if "alg_bytes" in kernels[n]:
+                kernels[n]["traffic_ratio"] = b / kernels[n]["alg_bytes"]
 
+    # headline roofline: the prefill call (value is its tokens/s)
     pre_bytes = th * PREFILL_BYTES + nh * STATE_BYTES
+    roofline = _hbm(pre_bytes, t_pre * 1e6, prefill_traffic(traffic))
+    roofline["kernel"] = "kda_chunk_fwd call (intra_kernel + carry_kernel)"
+    roofline["unit_bytes"] = ("1540 B per token-head (q, k, v, o bf16; log_alpha, beta fp32) + "
+                              "65536 B per (sequence, head) h_final")
+    decode_roofline = _hbm(pairs * DECODE_BYTES, mean["decode"] * 1e3, traffic.get("decode"))
+    decode_roofline["kernel"] = "recurrent_fwd_kernel (decode step)"
+    decode_roofline["unit_bytes"] = "132612 B per (sequence, head)"
+
     t_roof = max(pre_bytes / (HBM_PEAK_GBPS * 1e9), th * FLOPS_EQ13 / (BF16_PEAK_TFLOPS * 1e12))
     prefill_path = {
         "time_us": t_pre * 1e6,
@@ -666,27 +825,39 @@ def main():
                                f"fp32 states", "T": p.T, "H": p.H, "d": D, "chunk": C,
                    "decode_batch": cfg4.n_seqs},
         "decode_tokens_per_s": decode_tps,
-        "prefill_phases_us": sum(mean[n] for n in names) * 1e3,
+        "prefill_phases_us": sum(mean[n] for n in names_k) * 1e3,
         "roofline": roofline,
+        "decode_roofline": decode_roofline,
         "prefill_path": prefill_path,
         "timing": timing,
         "kernels": kernels,
+        "input_draw_s": gen_s,
     }
+    print("8K prefill and decode timed", file=sys.stderr, flush=True)
+    if not args.no_long_configs:
+        out["long_configs"] = {n: long_config(torch, extra.pop(n), n, args.steps, args.warmup)
+                               for n in ("long_T131072", "packed_16_sequences")}
+        print("long configs timed", file=sys.stderr, flush=True)
+    if not args.no_sweep:
+        out["sweep_h16"] = sweep_h16(torch, extra.pop("sweep_h16"), args.steps, args.warmup)
+        print("16-head sweep timed", file=sys.stderr, flush=True)
     if not args.no_extensions:
-        out["extensions"] = extensions(torch, d, pre_args, args.steps, args.warmup)
-    if not args.no_ceilings:
-        ceil = ceilings(torch)
-        out["ceilings"] = ceil
-        _with_ceiling(roofline, ceil, "hbm_rmw_GBps" if dom == "decode" else "hbm_copy_GBps")
+        out["extensions"] = extensions(torch, d, pre_args, args.steps, args.warmup, extra,
+                                       t_pre * 1e6)
+        print("extensions timed", file=sys.stderr, flush=True)
+    extra.clear()
+    if not args.no_probes:
+        pr = probes(torch)
+        out["probes"] = pr
+        _with_probe(roofline, pr, "hbm_copy_GBps")
+        _with_probe(decode_roofline, pr, "hbm_rmw_GBps")
         kinds = {"recurrent_L4": "hbm_rmw_GBps", "recurrent_L64": "valu_fp32_TFLOPs",
                  "chunked_L64": "hbm_copy_GBps",
                  "decode_bf16_state": "hbm_rmw_GBps", "decode_batch1": "hbm_rmw_GBps",
                  "epilogue": "hbm_copy_GBps"}
         for name, key in kinds.items():
             if name in out.get("extensions", {}):
-                _with_ceiling(out["extensions"][name]["roofline"], ceil, key)
-    if args.long_configs:
-        out["long_configs"] = long_configs(torch, d, args.steps, args.warmup)
+                _with_probe(out["extensions"][name]["roofline"], pr, key)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out))

@@ -22,9 +22,6 @@ LIB = PKG / "libkda.so"
 BUILD = ROOT / "_build"
 SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_recurrent.hip", "kda_epilogue.hip",
            "kda_check.hip"]
-# achievable-rate probes used by bench.py's roofline figures (not the operator)
-CEIL_SRC = PKG / "ceilings" / "ceilings.hip"
-CEIL_LIB = PKG / "libkda_ceilings.so"
 
 
 def hipcc() -> str:
@@ -72,11 +69,9 @@ def _link(objs, lib: Path, verbose: bool) -> None:
 
 def build(verbose: bool = False) -> Path:
     BUILD.mkdir(exist_ok=True)
-    srcs = [*SOURCES, str(CEIL_SRC)]
-    with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    _link(objs[:len(SOURCES)], LIB, verbose)
-    _link(objs[len(SOURCES):], CEIL_LIB, verbose)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    _link(objs, LIB, verbose)
     return LIB
 
 

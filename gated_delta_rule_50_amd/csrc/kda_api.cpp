@@ -264,7 +264,7 @@ kda_status kda_rmsnorm_gate(const void* o, const void* gate, const float* weight
   if (rows < 0 || !(eps >= 0.f) || eps > 3.0e38f) return KDA_ERR_SHAPE;
   if (dv != kDim || !valid_io(io)) return KDA_ERR_UNSUPPORTED;
   if (rows == 0) return KDA_OK;
-  if (rows > (int64_t)UINT32_MAX * 16) return KDA_ERR_SHAPE;
+  if (rows > ((int64_t)1 << 36)) return KDA_ERR_SHAPE;
   if (!o || !gate || !y) return KDA_ERR_NULL;
   if (!aligned16({o, gate, weight, y})) return KDA_ERR_ALIGN;
   const int64_t bytes = rows * kDim * io_bytes(io);

@@ -775,8 +775,8 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     const uint8_t* inter,   // not restrict: prefetch loads stay ahead of the barriers
     const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
-    const float* __restrict__ h0, float* __restrict__ h_final, E* __restrict__ o,
-    int32_t n_seqs, int64_t T, int32_t H, int32_t single) {
+    const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
+    E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, int32_t single) {
   static_assert(kTiles == 1 || kTiles == 2, "one or two column tiles per workgroup");
   constexpr bool kStaged = sizeof(E) == 2;
   static_assert(kStaged || kTiles == 1, "fp32 intermediates: one tile per workgroup");
@@ -1091,8 +1091,8 @@ template <class E>
 __global__ __launch_bounds__(kWave) void carry_short_kernel(
     const uint8_t* __restrict__ inter, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
-    const float* __restrict__ h0, float* __restrict__ h_final, E* __restrict__ o,
-    int32_t n_seqs, int64_t T, int32_t H) {
+    const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
+    E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H) {
   // the eight tiles of a (sequence, head) get ids with the same id % 8 (one XCD)
   const int id = blockIdx.x;
   const int pair = (id & 7) + 8 * ((id >> 3) / 8);

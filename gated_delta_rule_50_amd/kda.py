@@ -108,6 +108,23 @@ def _check(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _shape(t, name, shape):
+    """Raises ValueError unless t (when given) has exactly `shape`. Checked
+    before anything else: the kernels index every buffer by T, H, N and the
+    head size, so a mis-shaped tensor would be read or written past its end."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _head_rows(k, name="k"):
+    """(rows, H) of a [rows, H, 128] tensor, or ValueError."""
+    if k.dim() != 3 or k.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} has shape {tuple(k.shape)}, expected [T, H, {HEAD_DIM}]")
+    return int(k.shape[0]), int(k.shape[1])
+
+
 def _stream(stream, device):
     s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -142,9 +159,17 @@ class Prefill:
     def __init__(self, q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
                  h_final=None, want_final=True, workspace=None, qk_l2norm=False):
         dev = k.device
-        self.io = _io(k.dtype)
-        self.T, self.H = int(k.shape[0]), int(k.shape[1])
+        self.T, self.H = _head_rows(k)
+        if cu_seqlens is not None and cu_seqlens.dim() != 1:
+            raise ValueError(f"cu_seqlens has shape {tuple(cu_seqlens.shape)}, expected [N + 1]")
         self.N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+        T, H, N, D = self.T, self.H, self.N, HEAD_DIM
+        for t, n in ((q, "q"), (v, "v"), (log_alpha, "log_alpha"), (o, "o")):
+            _shape(t, n, (T, H, D))
+        _shape(beta, "beta", (T, H))
+        _shape(h0, "h0", (N, H, D, D))
+        _shape(h_final, "h_final", (N, H, D, D))
+        self.io = _io(k.dtype)
         for t, n in ((q, "q"), (k, "k"), (v, "v")):
             _check(t, n, k.dtype, dev)
         _check(log_alpha, "log_alpha", torch.float32, dev)
@@ -196,8 +221,12 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     beta [N, H] fp32. Returns o [N, H, 128].
     """
     dev = k.device
+    N, H = _head_rows(k)
+    for t, n in ((q, "q"), (v, "v"), (log_alpha, "log_alpha"), (o, "o")):
+        _shape(t, n, (N, H, HEAD_DIM))
+    _shape(beta, "beta", (N, H))
+    _shape(S, "S", (N, H, HEAD_DIM, HEAD_DIM))
     io = _io(k.dtype)
-    N, H = int(k.shape[0]), int(k.shape[1])
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, k.dtype, dev)
     _check(log_alpha, "log_alpha", torch.float32, dev)
@@ -228,12 +257,21 @@ class Recurrent:
                  state_dtype=torch.float32, qk_l2norm=False, o=None, h_final=None,
                  want_final=True):
         dev = k.device
-        self.io = _io(k.dtype)
-        self.T, self.H = int(k.shape[0]), int(k.shape[1])
+        self.T, self.H = _head_rows(k)
         if cu_seqlens is not None:
+            if cu_seqlens.dim() != 1:
+                raise ValueError(f"cu_seqlens has shape {tuple(cu_seqlens.shape)}, "
+                                 "expected [N + 1]")
             self.N = int(cu_seqlens.shape[0]) - 1
         else:
             self.N = 1 if n_seqs is None else int(n_seqs)
+        T, H, N, D = self.T, self.H, self.N, HEAD_DIM
+        for t, n in ((q, "q"), (v, "v"), (log_alpha, "log_alpha"), (o, "o")):
+            _shape(t, n, (T, H, D))
+        _shape(beta, "beta", (T, H))
+        _shape(h0, "h0", (N, H, D, D))
+        _shape(h_final, "h_final", (N, H, D, D))
+        self.io = _io(k.dtype)
         for t, n in ((q, "q"), (k, "k"), (v, "v")):
             _check(t, n, k.dtype, dev)
         _check(log_alpha, "log_alpha", torch.float32, dev)
@@ -276,12 +314,15 @@ def rmsnorm_gate(o, gate, weight=None, eps=1e-6, *, y=None, stream=None):
     row of 128 channels. o, gate [..., 128] in one I/O dtype; weight [128]
     float32 or None; y may be o (in place). Returns y."""
     dev = o.device
+    if o.dim() < 1 or o.shape[-1] != HEAD_DIM:
+        raise ValueError(f"o has shape {tuple(o.shape)}, expected [..., {HEAD_DIM}]")
+    _shape(gate, "gate", o.shape)
+    _shape(weight, "weight", (HEAD_DIM,))
+    _shape(y, "y", o.shape)
     io = _io(o.dtype)
     _check(o, "o", None, dev)
     _check(gate, "gate", o.dtype, dev)
     _check(weight, "weight", torch.float32, dev)
-    if gate.shape != o.shape:
-        raise ValueError(f"gate shape {tuple(gate.shape)} != o shape {tuple(o.shape)}")
     if y is None:
         y = torch.empty_like(o)
     _check(y, "y", o.dtype, dev)
@@ -302,6 +343,13 @@ def check_inputs(q, k, v, log_alpha, beta, cu_seqlens=None, *, flags=None, strea
     and flags receives the OR of the KDA_BAD_* bits; without, the bits are
     returned as an int (which waits for the stream)."""
     dev = k.device
+    T, H = _head_rows(k)
+    for t, n in ((q, "q"), (v, "v"), (log_alpha, "log_alpha")):
+        _shape(t, n, (T, H, HEAD_DIM))
+    _shape(beta, "beta", (T, H))
+    if cu_seqlens is not None and cu_seqlens.dim() != 1:
+        raise ValueError(f"cu_seqlens has shape {tuple(cu_seqlens.shape)}, expected [N + 1]")
+    _shape(flags, "flags", (1,))
     _io(k.dtype)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, k.dtype, dev)
@@ -310,7 +358,6 @@ def check_inputs(q, k, v, log_alpha, beta, cu_seqlens=None, *, flags=None, strea
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
     out = torch.empty(1, dtype=torch.int32, device=dev) if flags is None else flags
     _check(out, "flags", torch.int32, dev)
-    T, H = int(k.shape[0]), int(k.shape[1])
     n = 0 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
     st = lib().kda_check_inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                 _ptr(cu_seqlens), n, T, H, int(k.shape[2]), int(v.shape[2]),

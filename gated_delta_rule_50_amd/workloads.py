@@ -10,7 +10,8 @@ Parameterization"): 128-dim heads, L2-normalised q and k, beta = sigmoid(.),
 alpha in (0, 1] per channel, supplied here as its natural log.
 
 Recipe (numpy PCG64, ``default_rng(seed)``), in draw order:
-  lengths (packed batches only) -> q -> k -> v -> beta -> log_alpha -> h0.
+  lengths (the seeded variable-length batch: integers uniform in [lo, hi],
+  both ends included) -> q -> k -> v -> beta -> log_alpha -> h0.
   q, k  ~ N(0,1) float32, L2-normalised per (token, head) in fp64, then
         rounded to the I/O dtype (bf16: round-to-nearest-even). With
         qk="raw" the normalisation is skipped (inputs for the operator's
@@ -20,11 +21,20 @@ Recipe (numpy PCG64, ``default_rng(seed)``), in draw order:
   log_alpha = log(sigmoid(z)) / 16 = -softplus(-z)/16, z ~ N(0,1), computed
         in fp64, stored float32. "split" decay: channels [0, dk/2) use that
         draw; channels [dk/2, dk) draw uniform [-1.0, -0.25] (strong decay).
+        "extreme" decay: as "split" with channels [dk/2, dk) uniform in
+        [-4.0, -3.0], so a 16-token block's decay on those channels
+        exceeds e^-44 (decays the chunk kernels evaluate per element).
   h0    ~ N(0, std^2) float32 when std is given, else zeros (None).
 Large draws go in fixed row blocks, so results depend only on the seed.
+The draws stay in one sequential stream per batch; the elementwise and
+per-row arithmetic after them (normalisation, rounding, the log-sigmoid)
+runs on row blocks in a thread pool, which gives the same values as one
+thread.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -52,27 +62,55 @@ def _to_io(x: np.ndarray, io: str) -> np.ndarray:
     return round_bf16(x) if io == "bf16" else x.astype(np.float32)
 
 
-def _normal_f32(rng, shape):
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _normal_f32(rng, shape, post=None):
+    """N(0,1) float32 draws in row blocks of the first axis. post(blk), if
+    given, transforms each drawn block in place on the thread pool while the
+    next blocks are drawn."""
     out = np.empty(shape, dtype=np.float32)
     flat = out.reshape(shape[0], -1)
-    for s in range(0, shape[0], _BLOCK):
-        e = min(s + _BLOCK, shape[0])
-        flat[s:e] = rng.standard_normal(flat[s:e].shape, dtype=np.float32)
+    if post is None:
+        for s in range(0, shape[0], _BLOCK):
+            e = min(s + _BLOCK, shape[0])
+            flat[s:e] = rng.standard_normal(flat[s:e].shape, dtype=np.float32)
+        return out
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        pending = []
+        for s in range(0, shape[0], _BLOCK):
+            e = min(s + _BLOCK, shape[0])
+            flat[s:e] = rng.standard_normal(flat[s:e].shape, dtype=np.float32)
+            pending.append(ex.submit(post, out[s:e]))
+            if len(pending) > 2 * _workers():
+                pending.pop(0).result()
+        for f in pending:
+            f.result()
     return out
+
+
+def _round_block(io):
+    def rnd(blk):
+        if io == "bf16":
+            blk[...] = round_bf16(blk)
+    return rnd
 
 
 def _unit_rows(rng, shape, io, normalise=True):
     """N(0,1) rows normalised along the last axis in fp64, rounded to io."""
-    x = _normal_f32(rng, shape)
     if not normalise:
-        return _to_io(x, io)
-    flat = x.reshape(-1, shape[-1])
-    for s in range(0, flat.shape[0], _BLOCK):
-        e = min(s + _BLOCK, flat.shape[0])
-        blk = flat[s:e].astype(np.float64)
-        blk /= np.linalg.norm(blk, axis=-1, keepdims=True)
-        flat[s:e] = _to_io(blk.astype(np.float32), io)
-    return x
+        return _normal_f32(rng, shape, _round_block(io))
+
+    def norm(blk):
+        x = blk.astype(np.float64)
+        x /= np.linalg.norm(x, axis=-1, keepdims=True)
+        blk[...] = _to_io(x.astype(np.float32), io)
+    return _normal_f32(rng, shape, norm)
 
 
 def _log_sigmoid_over_16(z64: np.ndarray) -> np.ndarray:
@@ -81,19 +119,31 @@ def _log_sigmoid_over_16(z64: np.ndarray) -> np.ndarray:
 
 
 def _log_alpha(rng, T, H, dk, decay):
+    strong = {"split": (-1.0, -0.25), "extreme": (-4.0, -3.0)}
+    if decay != "mild" and decay not in strong:
+        raise ValueError(f"unknown decay recipe {decay!r}")
     la = np.empty((T, H, dk), dtype=np.float32)
     half = dk // 2
-    for s in range(0, T, _BLOCK):
-        e = min(s + _BLOCK, T)
-        if decay == "mild":
-            z = rng.standard_normal((e - s, H, dk))
-            la[s:e] = _log_sigmoid_over_16(z).astype(np.float32)
-        elif decay == "split":
-            z = rng.standard_normal((e - s, H, half))
-            la[s:e, :, :half] = _log_sigmoid_over_16(z).astype(np.float32)
-            la[s:e, :, half:] = rng.uniform(-1.0, -0.25, (e - s, H, dk - half)).astype(np.float32)
-        else:
-            raise ValueError(f"unknown decay recipe {decay!r}")
+    nz = dk if decay == "mild" else half
+
+    def fill(s, e, z):
+        la[s:e, :, :nz] = _log_sigmoid_over_16(z).astype(np.float32)
+
+    # the draws stay in order on this thread; each block's log-sigmoid runs
+    # on the pool while the next block is drawn (a few blocks in flight)
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        pending = []
+        for s in range(0, T, _BLOCK):
+            e = min(s + _BLOCK, T)
+            z = rng.standard_normal((e - s, H, nz))
+            pending.append(ex.submit(fill, s, e, z))
+            if decay in strong:
+                lo, hi = strong[decay]
+                la[s:e, :, half:] = rng.uniform(lo, hi, (e - s, H, dk - half)).astype(np.float32)
+            if len(pending) > 2 * _workers():
+                pending.pop(0).result()
+        for f in pending:
+            f.result()
     return la
 
 
@@ -122,10 +172,20 @@ class Prefill:
         return len(self.cu_seqlens) - 1
 
 
+def _draw_lengths(rng, n, lo, hi):
+    return tuple(int(x) for x in rng.integers(lo, hi, size=n, endpoint=True))
+
+
 def make_prefill(lengths, H, seed, io="bf16", decay="mild", h0_std=None,
-                 dk=D, dv=D, qk="unit") -> Prefill:
-    """Draws one packed batch with sequences of the given lengths."""
+                 dk=D, dv=D, qk="unit", draw_lengths=None) -> Prefill:
+    """Draws one packed batch with sequences of the given lengths. With
+    draw_lengths = (n, lo, hi) the lengths are the stream's first draw
+    (and must equal `lengths`, which varlen_lengths computes the same way)."""
     rng = np.random.default_rng(seed)
+    if draw_lengths is not None:
+        drawn = _draw_lengths(rng, *draw_lengths)
+        if tuple(int(x) for x in lengths) != drawn:
+            raise ValueError("lengths differ from the batch's seeded length draw")
     lengths = np.asarray(lengths, dtype=np.int64)
     T = int(lengths.sum())
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
@@ -133,7 +193,7 @@ def make_prefill(lengths, H, seed, io="bf16", decay="mild", h0_std=None,
     unit = {"unit": True, "raw": False}[qk]
     q = _unit_rows(rng, (T, H, dk), io, unit)
     k = _unit_rows(rng, (T, H, dk), io, unit)
-    v = _to_io(_normal_f32(rng, (T, H, dv)), io)
+    v = _normal_f32(rng, (T, H, dv), _round_block(io))
     beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
     la = _log_alpha(rng, T, H, dk, decay)
     h0 = None
@@ -210,12 +270,14 @@ class Config:
     def prefill(self) -> Prefill:
         assert self.kind == "prefill"
         return make_prefill(self.lengths, self.H, self.seed, self.io,
-                            self.decay, self.h0_std)
+                            self.decay, self.h0_std,
+                            draw_lengths=self.extra.get("draw_lengths"))
 
 
-def _varlen_lengths(seed, n, lo, hi):
-    rng = np.random.default_rng(seed)
-    return tuple(int(x) for x in rng.integers(lo, hi, size=n, endpoint=True))
+def varlen_lengths(seed, n, lo, hi):
+    """The lengths a batch seeded `seed` draws first (make_prefill's
+    draw_lengths)."""
+    return _draw_lengths(np.random.default_rng(seed), n, lo, hi)
 
 
 def config(cid: int) -> Config:
@@ -233,11 +295,11 @@ def config(cid: int) -> Config:
                       H=32, io="bf16", seed=seed, lengths=(131072,),
                       decay="split", h0_std=0.02)
     if cid == 3:
-        # lengths are drawn from their own stream so the batch draw stays
-        # in the documented order (lengths first, then q, k, v, ...)
-        lengths = _varlen_lengths(seed + 100000, 16, 512, 16384)
+        # the lengths are the batch stream's first draw, then q, k, v, ...
+        spec = (16, 512, 16384)
         return Config(3, "varlen_16seq_H32_bf16", "prefill", H=32, io="bf16",
-                      seed=seed, lengths=lengths, h0_std=0.02, n_seqs=16)
+                      seed=seed, lengths=varlen_lengths(seed, *spec), h0_std=0.02,
+                      n_seqs=16, extra={"draw_lengths": spec})
     if cid == 4:
         return Config(4, "decode_N256_H32_bf16_64steps", "decode", H=32,
                       io="bf16", seed=seed, n_seqs=256, steps=64)

@@ -27,6 +27,15 @@ def rel_fro_err(got, ref):
     return float(np.linalg.norm((got - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30))
 
 
+def rel_fro_err_dev(got, ref):
+    """rel_fro_err of a device tensor against a host fp64 array, evaluated
+    in fp64 on the device (large states: the measure, not the operator)."""
+    r = torch.from_numpy(np.ascontiguousarray(ref, dtype=np.float64)).to(got.device)
+    num = torch.linalg.vector_norm(got.double() - r).item()
+    den = torch.linalg.vector_norm(r).item()
+    return float(num / max(den, 1e-30))
+
+
 # Tolerances: output max-abs error relative to max|o|; state relative
 # Frobenius error. fp32 I/O: 1e-4 on o and (unstated on the pages, chosen
 # here) 1e-4 on the state; bf16 I/O: 2e-2 on o, 1e-2 on the state.

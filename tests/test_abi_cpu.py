@@ -310,9 +310,9 @@ def test_binding_refuses_cpu_tensors():
 def test_probe_library_rejects_bad_arguments():
     """The achievable-rate probes (bench.py's ceilings) load, export their
     entry points and refuse bad arguments before any launch."""
-    path = ROOT / "gated_delta_rule_50_amd" / "libkda_ceilings.so"
+    path = ROOT / "probes" / "libkda_probes.so"
     if not path.exists():
-        pytest.skip("libkda_ceilings.so not built")
+        pytest.skip("libkda_probes.so not built")
     P = ctypes.CDLL(str(path))
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     P.kdab_read.argtypes = [vp, i64, vp, i32, vp]
@@ -352,3 +352,89 @@ def test_check_inputs_rejects_bad_arguments(lib):
     assert call(q, k, v, la, b, cu, 3, T, H, 128, 128, BF16, q + 64, None) == ALIAS
     assert call(q, k, v, la, b, cu, 3, T, H, 128, 128, BF16, cu + 4, None) == ALIAS
     assert call(q, k, v, la, b, cu, 3, 1 << 40, H, 128, 128, BF16, fl, None) == SHAPE
+
+
+def _host_prefill_args(T=130, H=3, N=2):
+    torch = pytest.importorskip("torch")
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, dtype=dt)  # noqa: E731
+    return dict(q=z(T, H, 128), k=z(T, H, 128), v=z(T, H, 128), log_alpha=z(T, H, 128),
+                beta=z(T, H), h0=z(N, H, 128, 128),
+                cu_seqlens=torch.tensor([0, 60, T], dtype=torch.int32),
+                o=z(T, H, 128), h_final=z(N, H, 128, 128))
+
+
+# one mis-shaped tensor per case: (argument, bad shape)
+PREFILL_BAD = [("q", (130, 3, 64)), ("v", (130, 2, 128)), ("log_alpha", (129, 3, 128)),
+               ("beta", (130,)), ("beta", (130, 3, 1)), ("h0", (3, 128, 128)),
+               ("h0", (1, 3, 128, 128)), ("h_final", (2, 3, 128, 64)), ("o", (130, 3, 127)),
+               ("cu_seqlens", (2, 2))]
+
+
+@pytest.mark.parametrize("name,shape", PREFILL_BAD)
+def test_binding_rejects_misshaped_prefill_tensor(name, shape):
+    """Every tensor the prefill kernels index by (T, H, N, 128) is checked for
+    its exact shape before anything reaches the library."""
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_50_amd import kda
+    a = _host_prefill_args()
+    a[name] = torch.zeros(*shape, dtype=a[name].dtype)
+    with pytest.raises(ValueError, match="shape"):
+        kda.Prefill(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["h0"],
+                    a["cu_seqlens"], o=a["o"], h_final=a["h_final"])
+    with pytest.raises(ValueError, match="shape"):
+        kda.Recurrent(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["h0"],
+                      a["cu_seqlens"], o=a["o"], h_final=a["h_final"])
+
+
+def test_binding_shape_check_passes_good_shapes():
+    """With every shape right, host tensors fail on the device check instead."""
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_50_amd import kda
+    a = _host_prefill_args()
+    for ctor in (kda.Prefill, kda.Recurrent):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            ctor(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["h0"],
+                 a["cu_seqlens"], o=a["o"], h_final=a["h_final"])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.check_inputs(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["cu_seqlens"])
+
+
+@pytest.mark.parametrize("name,shape", [("q", (4, 2, 64)), ("v", (4, 3, 128)),
+                                        ("log_alpha", (5, 2, 128)), ("beta", (4,)),
+                                        ("S", (4, 2, 128, 64)), ("S", (2, 128, 128)),
+                                        ("o", (4, 2, 100))])
+def test_binding_rejects_misshaped_decode_tensor(name, shape):
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_50_amd import kda
+    z = lambda *s: torch.zeros(*s)  # noqa: E731
+    a = dict(q=z(4, 2, 128), k=z(4, 2, 128), v=z(4, 2, 128), log_alpha=z(4, 2, 128),
+             beta=z(4, 2), S=z(4, 2, 128, 128), o=z(4, 2, 128))
+    a[name] = z(*shape)
+    with pytest.raises(ValueError, match="shape"):
+        kda.decode_step(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["S"], o=a["o"])
+
+
+@pytest.mark.parametrize("name,shape", [("gate", (10, 2, 128)), ("weight", (64,)),
+                                        ("weight", (1, 128)), ("y", (10, 128)),
+                                        ("o", (10, 3, 64))])
+def test_binding_rejects_misshaped_epilogue_tensor(name, shape):
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_50_amd import kda
+    a = dict(o=torch.zeros(10, 3, 128), gate=torch.zeros(10, 3, 128),
+             weight=torch.zeros(128), y=torch.zeros(10, 3, 128))
+    a[name] = torch.zeros(*shape)
+    with pytest.raises(ValueError, match="shape"):
+        kda.rmsnorm_gate(a["o"], a["gate"], a["weight"], y=a["y"])
+
+
+@pytest.mark.parametrize("name,shape", [("q", (6, 2, 128, 1)), ("beta", (6, 3)),
+                                        ("log_alpha", (6, 2, 64)), ("flags", (2,))])
+def test_binding_rejects_misshaped_check_inputs_tensor(name, shape):
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_50_amd import kda
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, dtype=dt)  # noqa: E731
+    a = dict(q=z(6, 2, 128), k=z(6, 2, 128), v=z(6, 2, 128), log_alpha=z(6, 2, 128),
+             beta=z(6, 2), flags=z(1, dt=torch.int32))
+    a[name] = z(*shape, dt=a[name].dtype)
+    with pytest.raises(ValueError, match="shape"):
+        kda.check_inputs(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], flags=a["flags"])

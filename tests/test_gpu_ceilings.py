@@ -8,7 +8,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from gated_delta_rule_50_amd.build import CEIL_LIB  # noqa: E402
+from probes.build import LIB as CEIL_LIB  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 

@@ -1,8 +1,9 @@
 """Parity at the full sizes of the benchmark workloads.
 
-The HIP path runs every head of the full workload; the fp64 oracle checks a
-sample of heads (heads are independent), and for decode a sample of
-sequences, carried over all 64 steps with the oracle's own fp64 state.
+The HIP path runs every head of the full workload and the fp64 oracle checks
+every head (in groups of eight heads, which bounds host memory; heads are
+independent, so the split changes nothing), and for decode every sequence,
+carried over all 64 steps with the oracle's own fp64 state.
 """
 import numpy as np
 import pytest
@@ -11,7 +12,8 @@ torch = pytest.importorskip("torch")
 
 from gated_delta_rule_50_amd import kda, workloads  # noqa: E402
 from oracle import recurrent  # noqa: E402
-from tests.kda_testutil import TOL, dev, host, io_dtype, rel_fro_err, rel_max_err  # noqa: E402
+from tests.kda_testutil import (TOL, dev, host, io_dtype, rel_fro_err,  # noqa: E402
+                                rel_fro_err_dev, rel_max_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,20 +27,38 @@ def _prefill(p):
     return o, hf
 
 
-def _check_heads(p, o, hf, heads, per_sequence=False):
-    o_h = o[:, heads].float().cpu().numpy().astype(np.float64)
-    hf_h = hf[:, heads].cpu().numpy().astype(np.float64)
+def _check_all_heads(p, o, hf, per_sequence=False, group=8):
+    """Every head against the oracle, `group` heads per oracle call. The
+    measures are those of the whole output: max |o - o_ref| over all heads
+    divided by max |o_ref| over all heads, and the relative Frobenius error
+    of all states (and of each sequence's states)."""
     assert torch.isfinite(o.float()).all() and torch.isfinite(hf).all()
-    ro, rh = recurrent.forward(p.q[:, heads], p.k[:, heads], p.v[:, heads],
-                               p.log_alpha[:, heads], p.beta[:, heads],
-                               None if p.h0 is None else p.h0[:, heads], p.cu_seqlens)
+    err_o = ref_o = 0.0
+    d2 = r2 = 0.0
+    d2_n, r2_n = np.zeros(p.N), np.zeros(p.N)
+    for h0_ in range(0, p.H, group):
+        heads = list(range(h0_, min(h0_ + group, p.H)))
+        ro, rh = recurrent.forward(p.q[:, heads], p.k[:, heads], p.v[:, heads],
+                                   p.log_alpha[:, heads], p.beta[:, heads],
+                                   None if p.h0 is None else p.h0[:, heads], p.cu_seqlens)
+        o_h = o[:, heads].float().cpu().numpy().astype(np.float64)
+        err_o = max(err_o, float(np.abs(o_h - ro).max()))
+        ref_o = max(ref_o, float(np.abs(ro).max()))
+        del o_h, ro
+        hf_h = hf[:, heads].cpu().numpy().astype(np.float64)
+        dd = ((hf_h - rh) ** 2).reshape(p.N, -1).sum(axis=1)
+        rr = (rh ** 2).reshape(p.N, -1).sum(axis=1)
+        d2_n += dd
+        r2_n += rr
+        d2 += dd.sum()
+        r2 += rr.sum()
     tol_o, tol_s = TOL[p.io]
-    eo, es = rel_max_err(o_h, ro), rel_fro_err(hf_h, rh)
-    print(f"heads {heads}: o err {eo:.3e}, state err {es:.3e}")
+    eo, es = err_o / max(ref_o, 1e-30), np.sqrt(d2 / max(r2, 1e-300))
+    print(f"all {p.H} heads: o err {eo:.3e}, state err {es:.3e}")
     assert eo <= tol_o and es <= tol_s
     if per_sequence:
         for n in range(p.N):
-            e_n = rel_fro_err(hf_h[n], rh[n])
+            e_n = np.sqrt(d2_n[n] / max(r2_n[n], 1e-300))
             assert e_n <= tol_s, (n, e_n)
 
 
@@ -47,23 +67,24 @@ def test_config2_long_context_strong_decay():
     e^-16..e^-64 per chunk, nonzero h0."""
     p = workloads.config(2).prefill()
     o, hf = _prefill(p)
-    _check_heads(p, o, hf, [0, 17, 31])
+    _check_all_heads(p, o, hf)
 
 
 def test_config3_packed_variable_length():
     p = workloads.config(3).prefill()
     assert p.N == 16 and 512 <= np.diff(p.cu_seqlens).min() and np.diff(p.cu_seqlens).max() <= 16384
     o, hf = _prefill(p)
-    _check_heads(p, o, hf, [0, 13, 31], per_sequence=True)
+    _check_all_heads(p, o, hf, per_sequence=True)
 
 
 def test_config4_decode_64_steps():
+    """All 256 sequences x 32 heads, every step against the oracle's own
+    fp64 trajectory."""
     cfg = workloads.config(4)
     N, H = cfg.n_seqs, cfg.H
     S0 = workloads.make_decode_state(N, H, cfg.seed)
     S = dev(S0)
-    sample = np.arange(0, N, 16)            # 16 of the 256 sequences, all heads
-    ref = S0[sample].astype(np.float64)
+    ref = S0.astype(np.float64)
     bf = torch.bfloat16
     worst_o = worst_s = 0.0
     for step in range(cfg.steps):
@@ -71,10 +92,9 @@ def test_config4_decode_64_steps():
         o = kda.decode_step(dev(d.q, bf), dev(d.k, bf), dev(d.v, bf), dev(d.log_alpha),
                             dev(d.beta), S)
         torch.cuda.synchronize()
-        ro, ref = recurrent.decode_step(d.q[sample], d.k[sample], d.v[sample],
-                                        d.log_alpha[sample], d.beta[sample], ref)
-        eo = rel_max_err(host(o[sample]), ro)
-        es = rel_fro_err(S[sample].cpu().numpy().astype(np.float64), ref)
+        ro, ref = recurrent.decode_step(d.q, d.k, d.v, d.log_alpha, d.beta, ref)
+        eo = rel_max_err(host(o), ro)
+        es = rel_fro_err_dev(S, ref)
         worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
         assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1], (step, eo, es)
         assert torch.isfinite(o.float()).all()
@@ -106,14 +126,14 @@ def test_recurrent_multi_token_full_size(L):
 
 def test_config4_decode_64_steps_bf16_state():
     """Config 4's 64 decode steps with the state stored in bf16 (rounded after
-    every step) through kda_recurrent_fwd, against the oracle's fp64 state:
-    the accumulated rounding must stay within the 1e-2 state tolerance."""
+    every step) through kda_recurrent_fwd, against the oracle's fp64 state
+    (all 256 sequences, every step): the accumulated rounding must stay
+    within the 1e-2 state tolerance."""
     cfg = workloads.config(4)
     N, H = cfg.n_seqs, cfg.H
     S0 = workloads.round_bf16(workloads.make_decode_state(N, H, cfg.seed))
     S = dev(S0, torch.bfloat16)
-    sample = np.arange(0, N, 16)
-    ref = S0[sample].astype(np.float64)
+    ref = S0.astype(np.float64)
     bf = torch.bfloat16
     worst_o = worst_s = 0.0
     for step in range(cfg.steps):
@@ -122,10 +142,9 @@ def test_config4_decode_64_steps_bf16_state():
                                  dev(d.beta), S, n_seqs=N, state_dtype=torch.bfloat16,
                                  h_final=S)
         torch.cuda.synchronize()
-        ro, ref = recurrent.decode_step(d.q[sample], d.k[sample], d.v[sample],
-                                        d.log_alpha[sample], d.beta[sample], ref)
-        eo = rel_max_err(host(o[sample]), ro)
-        es = rel_fro_err(S[sample].float().cpu().numpy().astype(np.float64), ref)
+        ro, ref = recurrent.decode_step(d.q, d.k, d.v, d.log_alpha, d.beta, ref)
+        eo = rel_max_err(host(o), ro)
+        es = rel_fro_err_dev(S, ref)
         worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
         assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1], (step, eo, es)
     print(f"bf16-state decode worst over 64 steps: o {worst_o:.3e}, state {worst_s:.3e}")

@@ -93,14 +93,16 @@ def test_operator_then_epilogue(path):
     assert rel_max_err(host(y), ref) <= TOL_Y["bf16"]
 
 
-def test_epilogue_full_size_8k_heads():
-    """Rows of the 8K x 32-head prefill (262144 rows), bf16, all checked."""
-    rows = 8192 * 32
+@pytest.mark.parametrize("rows", [8192 * 32, 131072 + 17])
+def test_epilogue_full_size_8k_heads(rows):
+    """Rows of the 8K x 32-head prefill (262144 rows), bf16, all checked; and
+    a count whose last 17 rows fall to the grid-stride loop's second pass
+    (the grid holds 8192 groups of 16 rows)."""
     e = workloads.make_epilogue(rows, seed=76, io="bf16")
     bf = torch.bfloat16
     y = kda.rmsnorm_gate(dev(e.o, bf), dev(e.gate, bf), dev(e.weight))
     torch.cuda.synchronize()
     ref = epilogue.rmsnorm_gate(e.o, e.gate, e.weight)
     err = rel_max_err(host(y), ref)
-    print(f"epilogue 262144 rows: err {err:.3e}")
+    print(f"epilogue {rows} rows: err {err:.3e}")
     assert err <= TOL_Y["bf16"]

@@ -65,3 +65,20 @@ def test_packed_lengths_recipe():
     assert all(512 <= L <= 16384 for L in cfg.lengths)
     assert cfg.lengths == workloads.config(3).lengths      # seeded
     assert workloads.config(1).lengths == (8192,) and workloads.config(4).kind == "decode"
+
+
+def test_packed_lengths_are_the_first_draw():
+    """The packed batch draws its lengths first from the batch's own stream,
+    then q (the recipe's draw order): a batch drawn with draw_lengths has the
+    q of a stream that skipped exactly those draws."""
+    import numpy as np
+    spec = (5, 16, 80)
+    lengths = workloads.varlen_lengths(77, *spec)
+    p = workloads.make_prefill(lengths, 2, seed=77, io="f32", draw_lengths=spec)
+    rng = np.random.default_rng(77)
+    rng.integers(16, 80, size=5, endpoint=True)
+    q0 = rng.standard_normal((sum(lengths), 2, 128), dtype=np.float32)
+    q0 = (q0 / np.linalg.norm(q0.astype(np.float64), axis=-1, keepdims=True)).astype(np.float32)
+    assert np.allclose(p.q, q0, rtol=0, atol=1e-7)
+    with pytest.raises(ValueError):
+        workloads.make_prefill((16,) * 5, 2, seed=77, io="f32", draw_lengths=spec)
