@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/kda.h: argument validation,
 // workspace sizing and launch sequencing. No compute happens here; every
 // step of the operator runs in the HIP kernels.
+#include <algorithm>
 #include <cstring>
 #include <initializer_list>
 #include <hip/hip_runtime.h>
@@ -12,9 +13,9 @@ namespace kda {
 hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q, const void* k,
                             const void* v, const float* log_alpha, const float* beta,
                             const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
-                            int32_t H, int64_t n_slots, void* o, float* h_final,
-                            int32_t* status, int32_t* chunk_offset, uint8_t* inter,
-                            hipStream_t stream);
+                            int32_t H, int64_t n_slots, int64_t win_slots, void* o,
+                            float* h_final, int32_t* status, int32_t* chunk_offset,
+                            float* state_area, uint8_t* inter, hipStream_t stream);
 size_t inter_block_bytes(bool bf16_io);
 hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, const void* q,
                                 const void* k, const void* v, const float* log_alpha,
@@ -82,15 +83,45 @@ int64_t chunk_slots(int64_t n_seqs, int64_t T) {
   return (T + kChunk - 1) / kChunk + n_seqs - 1;
 }
 
-int64_t inter_offset(int64_t n_seqs) { return 256 + round_up(4 * (n_seqs + 1), 256); }
+// Workspace layout: status word, chunk offsets, two [H, 128, 128] float32
+// states for sequences crossing a window boundary, then the intermediate
+// blocks of one window of chunk slots ([slot - W0][head]).
+int64_t state_offset(int64_t n_seqs) { return 256 + round_up(4 * (n_seqs + 1), 256); }
+int64_t inter_offset(int64_t n_seqs, int64_t heads) {
+  return state_offset(n_seqs) + 2 * heads * kDim * kDim * 4;
+}
+int64_t block_bytes(int io) { return (int64_t)kda::inter_block_bytes(io == KDA_IO_BF16); }
 
-// Returns 0 when the sizes are unusable.
+// Blocks of the window kda_chunk_fwd_workspace_bytes sizes for: the whole
+// call when its blocks take at most this much, else as many chunk slots as
+// fit (the 8K x 32-head bf16 call is one window). Windows run one after the
+// other over the chunk slots in sequence order, which costs one sequence
+// nothing but serialises the sequences of a packed batch (a window of 512
+// MiB holds one or two of the 16-sequence batch's): packed batches get a
+// larger window, so such batches stay one window.
+constexpr int64_t kWindowBytes = (int64_t)512 << 20;
+constexpr int64_t kPackedWindowBytes = (int64_t)8 << 30;
+
+bool valid_sizes(int64_t n_seqs, int64_t T, int64_t heads, int io) {
+  return n_seqs >= 1 && T >= 0 && heads >= 1 && heads <= 65535 && valid_io(io) &&
+         chunk_slots(n_seqs, T) <= INT32_MAX;
+}
+
+// Recommended size (0 when the sizes are unusable).
 size_t workspace_bytes(int64_t n_seqs, int64_t T, int64_t heads, int io) {
-  if (n_seqs < 1 || T < 0 || heads < 1 || heads > 65535 || !valid_io(io)) return 0;
+  if (!valid_sizes(n_seqs, T, heads, io)) return 0;
   const int64_t slots = chunk_slots(n_seqs, T);
-  if (slots > INT32_MAX) return 0;
-  const int64_t block = (int64_t)kda::inter_block_bytes(io == KDA_IO_BF16);
-  return (size_t)(inter_offset(n_seqs) + slots * heads * block);
+  const int64_t per_slot = heads * block_bytes(io);
+  const int64_t cap = n_seqs > 1 ? kPackedWindowBytes : kWindowBytes;
+  const int64_t win = std::min(slots, std::max<int64_t>(1, cap / per_slot));
+  return (size_t)(inter_offset(n_seqs, heads) + win * per_slot);
+}
+
+// Smallest usable size: a window of one chunk slot (0 when unusable).
+size_t workspace_min_bytes(int64_t n_seqs, int64_t T, int64_t heads, int io) {
+  if (!valid_sizes(n_seqs, T, heads, io)) return 0;
+  const int64_t slots = chunk_slots(n_seqs, T);
+  return (size_t)(inter_offset(n_seqs, heads) + (slots > 0 ? heads * block_bytes(io) : 0));
 }
 
 }  // namespace
@@ -102,6 +133,13 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32
   const int io = raw(io_arg);
   if (dk != kDim || dv != kDim) return 0;
   return workspace_bytes(n_seqs, total_tokens, heads, io);
+}
+
+size_t kda_chunk_fwd_workspace_min_bytes(int32_t n_seqs, int64_t total_tokens, int32_t heads,
+                                         int32_t dk, int32_t dv, kda_io_dtype io_arg) {
+  const int io = raw(io_arg);
+  if (dk != kDim || dv != kDim) return 0;
+  return workspace_min_bytes(n_seqs, total_tokens, heads, io);
 }
 
 }  // extern "C"
@@ -127,10 +165,19 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
   if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
   if (!aligned16({q, k, v, log_alpha, h0, o, h_final}) || !aligned4({beta, cu_seqlens}))
     return KDA_ERR_ALIGN;
-  const size_t need = workspace_bytes(n_seqs, T, heads, io);
+  const size_t need = workspace_min_bytes(n_seqs, T, heads, io);
   if (need == 0) return KDA_ERR_SHAPE;
   if (!workspace || workspace_bytes_given < need || ((uintptr_t)workspace & 255u))
     return KDA_ERR_WORKSPACE;
+  // window of chunk slots: as many as the given workspace holds blocks for
+  const int64_t slots = chunk_slots(n_seqs, T);
+  const int64_t per_slot = (int64_t)heads * block_bytes(io);
+  const int64_t fit = ((int64_t)std::min<size_t>(workspace_bytes_given, (size_t)INT64_MAX) -
+                       inter_offset(n_seqs, heads)) / per_slot;
+  const int64_t win = std::min(slots, fit);
+  // a single phase launch covers every chunk only when one window does
+  if (phases != 7 && win < slots) return KDA_ERR_WORKSPACE;
+  const int64_t used = inter_offset(n_seqs, heads) + win * per_slot;
 
   const int64_t th = T * heads;
   const int64_t eb = io_bytes(io);
@@ -140,7 +187,7 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
   const int64_t state_bytes = (int64_t)n_seqs * heads * kDim * kDim * 4;
   const Range rh0(h0, state_bytes), rhf(h_final, state_bytes);
   const Range rcu(cu_seqlens, 4 * ((int64_t)n_seqs + 1));
-  const Range rws(workspace, (int64_t)need);
+  const Range rws(workspace, used);
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rh0, &rcu, &rws})
     if (overlap(ro, *in)) return KDA_ERR_ALIAS;
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro, &rcu, &rws})
@@ -152,12 +199,12 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* status = reinterpret_cast<int32_t*>(ws);
   int32_t* chunk_offset = reinterpret_cast<int32_t*>(ws + 256);
-  uint8_t* inter = ws + inter_offset(n_seqs);
+  float* state_area = reinterpret_cast<float*>(ws + state_offset(n_seqs));
+  uint8_t* inter = ws + inter_offset(n_seqs, heads);
   const hipError_t err = kda::launch_chunk_fwd(
       phases, io == KDA_IO_BF16, (flags & KDA_FLAG_QK_L2NORM) != 0, q, k, v, log_alpha, beta,
-      h0, cu_seqlens, n_seqs, T, heads,
-      chunk_slots(n_seqs, T), o, h_final, status, chunk_offset, inter,
-      static_cast<hipStream_t>(stream));
+      h0, cu_seqlens, n_seqs, T, heads, slots, std::max<int64_t>(win, 1), o, h_final, status,
+      chunk_offset, state_area, inter, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

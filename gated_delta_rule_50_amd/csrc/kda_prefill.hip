@@ -138,12 +138,103 @@ __device__ __forceinline__ void lds_frag(const bf16* p, Frag<bf16>& f) {
 }
 __device__ __forceinline__ void lds_frag(const float* p, Frag<float>& f) { load8(p, f.v); }
 
+// Exact diagonal 16 x 16 blocks of A_kk and A_qk, for blocks whose decay is
+// too strong for the factored form:
+//   A_kk[i][j] = sum_c k_i[c] k_j[c] P_ij[c],  A_qk[i][j] = sum_c q_i[c] k_j[c] P_ij[c],
+//   P_ij[c] = prod_{t=j+1..i} alpha_t[c] (j <= i; 1 on the diagonal),
+// i.e. exp(g_i - g_j) formed as a product of decays <= 1, so nothing
+// overflows whatever the gate. Lane (r, g) of the wave handles token i = r
+// and reads its k, q and raw log alpha rows again (channels 16 ct + 4 g + e),
+// so the caller keeps nothing extra live. Per 16-channel tile the wave
+// stages alpha and k of its 16 tokens in LDS (`stage`, wave-private, 1 KiB
+// of alpha + 16 x 16 E); every lane then walks the columns j = 15 .. 0 with
+// a running product of its four channels. The sums over the lane's 32 channels are reduced over the
+// four lanes of the row. Returns kk_t[e] = A_kk[i][4 g + e],
+// qk_t[e] = A_qk[i][4 g + e] and kk_d[e] = A_kk[4 g + e][i], zero above the
+// diagonal; tokens past the sequence end are identity tokens (k = q = 0,
+// alpha = 1). With kNorm, rk and rq are the L2Norm scales of row i.
+template <class E, bool kNorm>
+__device__ __forceinline__ void exact_diag_block(const E* __restrict__ k_row,
+                                                 const E* __restrict__ q_row,
+                                                 const float* __restrict__ la_row, bool valid,
+                                                 float rk, float rq, int r, int g, uint8_t* stage,
+                                                 float (&kk_t)[4], float (&qk_t)[4],
+                                                 float (&kk_d)[4]) {
+  float* const sa = reinterpret_cast<float*>(stage);        // [16 tokens][16 channels]
+  E* const sk = reinterpret_cast<E*>(stage + 16 * 16 * 4);   // [16 tokens][16 channels]
+  float pkk[16], pqk[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) pkk[j] = pqk[j] = 0.f;
+  const Frag16<E> zero = frag16<E>(zero4());
+#pragma unroll 1
+  for (int ct = 0; ct < 8; ++ct) {
+    const int c0 = 16 * ct + 4 * g;
+    const Frag16<E> ki = valid ? ld16(k_row + c0) : zero;
+    const Frag16<E> qi = valid ? ld16(q_row + c0) : zero;
+    const float4 l = *reinterpret_cast<const float4*>(la_row + c0);
+    const float4 a = valid ? float4{exp_f(l.x), exp_f(l.y), exp_f(l.z), exp_f(l.w)}
+                           : float4{1.f, 1.f, 1.f, 1.f};
+    // the previous tile's reads are done before this tile's writes (LDS
+    // operations of one wave complete in order; the clobbers keep the
+    // compiler from moving accesses across)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    *reinterpret_cast<float4*>(sa + r * 16 + 4 * g) = a;
+    st16(sk + r * 16 + 4 * g, ki);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    float P[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      if (j < 15) {
+        const float4 an = *reinterpret_cast<const float4*>(sa + (j + 1) * 16 + 4 * g);
+        const float av[4] = {an.x, an.y, an.z, an.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) P[e] = j < r ? P[e] * av[e] : P[e];
+      }
+      const Frag16<E> kj = ld16(sk + j * 16 + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = kj.get(e) * P[e];
+        pkk[j] += ki.get(e) * t;
+        pqk[j] += qi.get(e) * t;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) kk_t[e] = qk_t[e] = kk_d[e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float skk = sum_xor32(sum_xor16(pkk[j]));
+    float sqk = sum_xor32(sum_xor16(pqk[j]));
+    if constexpr (kNorm) {
+      // L2Norm scales: row i's (rk, rq) and column j's rk (lane j + 16 g)
+      const float rkj = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (j + 16 * g),
+                                                                     __float_as_int(rk)));
+      skk *= rk * rkj;
+      sqk *= rq * rkj;
+    }
+    if (j > r) skk = sqk = 0.f;
+    if (g == (j >> 2)) {
+      kk_t[j & 3] = skk;
+      qk_t[j & 3] = sqk;
+    }
+    // lane (j, g) takes A_kk[4 g + e][j] from lane (4 g + e, g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = __int_as_float(
+          __builtin_amdgcn_ds_bpermute(4 * ((4 * g + e) + 16 * g), __float_as_int(skk)));
+      if (r == j) kk_d[e] = x;
+    }
+  }
+}
+
 template <class E, bool kNorm>
 __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int32_t* chunk_offset, int32_t* status, int32_t n_seqs,
-    int64_t T, int32_t H, uint8_t* __restrict__ inter, int32_t single) {
+    int64_t T, int32_t H, uint8_t* __restrict__ inter, int32_t single, int32_t W0) {
   // LDS, one region reused across phases:
   //   rows phase   sKf  Kf fragments of the four blocks [J][kb][lane][8]
   //                sF   per-block channel factors (five rows per block)
@@ -157,6 +248,10 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   constexpr int kTile = kWave * 4;                        // elements per tile
   constexpr int kRowsBytes = 4 * 4 * kWave * 8 * (int)sizeof(E) + (5 + 3) * 4 * kD * 4;
   constexpr int kTilesBytes = (4 * 16 + 12 + 4) * kTile * (int)sizeof(E);
+  // exact diagonal path: per wave, 16 x 16 alpha (fp32) and k (E) values,
+  // placed after the rows-phase data
+  constexpr int kStageBytes = 16 * 16 * (4 + (int)sizeof(E));
+  static_assert(kRowsBytes + 4 * kStageBytes <= kTilesBytes, "staging fits the shared region");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRowsBytes > kTilesBytes ? kRowsBytes : kTilesBytes];
   __shared__ __attribute__((aligned(16))) float sB[kC];
   __shared__ float sRk[kNorm ? kC : 1], sRq[kNorm ? kC : 1];   // L2Norm row scales
@@ -174,8 +269,11 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   // the blocks it needs first are the ones written last, still held in the
   // memory-side cache when it starts (1.19 -> 1.07 us per chunk of the carry
   // on the 8K workload with 32 heads).
+  // The grid covers the window of chunk slots [W0, W0 + gridDim.x); blocks
+  // are written to the window's part of the workspace.
   const int64_t lin = blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
-  const int b = (int)(gridDim.x - 1 - lin / H), h = (int)(lin % H);
+  const int bw = (int)(gridDim.x - 1 - lin / H), h = (int)(lin % H);
+  const int b = W0 + bw;
   int total, first;
   int64_t seq_start, seq_end;
   if (single) {
@@ -216,7 +314,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   const bool valid = i < len;
   auto row = [&](int x) -> int64_t { return ((tok0 + x) * H + h) * (int64_t)kD; };
 
-  E* blk = reinterpret_cast<E*>(inter + ((int64_t)b * H + h) * Inter<E>::kBytes);
+  E* blk = reinterpret_cast<E*>(inter + ((int64_t)bw * H + h) * Inter<E>::kBytes);
   E* XA = blk + Inter<E>::kXA;
   E* KT = blk + Inter<E>::kKT;
   E* UC = blk + Inter<E>::kUC;
@@ -285,13 +383,24 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   }
   if (g == 0) sB[i] = bt;
   asm volatile("" ::: "memory");
+  bool wide = false;   // a channel decays by more than e^-44 over this block
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int c = lane + 64 * u;
     const float s = sTot[I * kD + c];
     sE[I * kD + c] = exp_f(s);
     sEi[I * kD + c] = exp_f(fminf(-s, 88.f));
+    wide |= s < -44.f;
   }
+  // Diagonal blocks whose factor exp(-block sum) could exceed e^44 are
+  // computed per element instead (they replace the matrix-core tiles below);
+  // done here, where little else is live. Staging area: the part of the
+  // shared region the rows phase does not use.
+  const bool exact = __builtin_amdgcn_ballot_w64(wide) != 0;
+  float ex_kk[4], ex_qk[4], ex_kd[4];
+  if (exact)
+    exact_diag_block<E, kNorm>(k + ro, q + ro, log_alpha + ro, valid, rk, rq, r, g,
+                               smem + kRowsBytes + I * kStageBytes, ex_kk, ex_qk, ex_kd);
   Frag16<E> Kr[8], Qr[8];
   Frag<E> kfI[4];
 #pragma unroll
@@ -374,7 +483,6 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   // accumulates akT[J][e] = A_kk[16I + r][16J + 4g + e],
   // aqT[J][e] = A_qk[16I + r][16J + 4g + e] and akD[e] = A_kk[16I + 4g + e][16I + r].
   floatx4 akT[4], aqT[4], akD = zero4();
-  bool wide = false;
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
     akT[J] = zero4();
@@ -399,8 +507,6 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
         akT[J] = mma(akT[J], fa, fk);
         aqT[J] = mma(aqT[J], fa, fq);
       } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wide |= d0[e] > 1.2851e19f || d1[e] > 1.2851e19f;  // e^44
         akT[J] = mma(akT[J], kfI[kb], fk);
         aqT[J] = mma(aqT[J], kfI[kb], fq);
         akD = mma(akD, fk, kfI[kb]);
@@ -408,36 +514,16 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     }
   }
 
-  // exact diagonal block when its factors could overflow: g differences
-  // summed from the raw log alphas
-  if (__builtin_amdgcn_ballot_w64(wide)) {
-    auto exact = [&](int a, int c0, float& skk, float& sqk) {   // rows a >= c0
-      skk = sqk = 0.f;
-      if (a >= len || c0 > a) return;
-      for (int c = 0; c < kD; ++c) {
-        float dg = 0.f;
-        for (int x = c0 + 1; x <= a; ++x) dg += log_alpha[row(x) + c];
-        const float d = exp_f(dg);
-        const float kc = to_f(k[row(c0) + c]);
-        skk += to_f(k[row(a) + c]) * kc * d;
-        sqk += to_f(q[row(a) + c]) * kc * d;
-      }
-      if constexpr (kNorm) {
-        skk *= sRk[a] * sRk[c0];
-        sqk *= sRq[a] * sRk[c0];
-      }
-    };
+  // exact diagonal block (computed in step 1) in place of the factored one
+  if (exact) {
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       if (J != I) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float skk, sqk, tkk, tqk;
-        exact(16 * I + r, 16 * I + 4 * g + e, skk, sqk);
-        exact(16 * I + 4 * g + e, 16 * I + r, tkk, tqk);
-        akT[J][e] = skk;
-        aqT[J][e] = sqk;
-        akD[e] = tkk;
+        akT[J][e] = ex_kk[e];
+        aqT[J][e] = ex_qk[e];
+        akD[e] = ex_kd[e];
       }
     }
   }
@@ -588,6 +674,49 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     }
   }
 }
+
+// ------------------------------------------------------------- windows
+// The prefill runs over windows of chunk slots [W0, W1) (as many as the
+// workspace holds blocks for), the intra-chunk kernel then the carry per
+// window. A sequence whose chunks cross a window boundary leaves its state
+// in the workspace's state area at the end of one window and picks it up
+// at the start of the next: at most one sequence crosses each boundary, so
+// the area holds one state per head, in two slots that alternate between
+// windows (a window reads the slot the previous one wrote and writes the
+// other).
+struct WindowArgs {
+  int32_t W0, W1;          // this window's chunk slots
+  int32_t last;            // 1 for the last window of the call
+  const float* resume;     // [H, 128, 128] state left by the previous window
+  float* suspend;          // [H, 128, 128] state for the next window
+
+  // The sequence's chunks [sb0, sb1) inside the window: [b0, b1). Returns
+  // false when this window has nothing to do for the sequence. An empty
+  // sequence (sb0 == sb1) is handled once, by the window holding slot sb0
+  // (by the last window when sb0 is past every slot), which copies its
+  // initial state to h_final.
+  __device__ bool part(int sb0, int sb1, int& b0, int& b1) const {
+    if (sb0 == sb1) {
+      b0 = b1 = sb0;
+      return (sb0 >= W0 && sb0 < W1) || (last && sb0 >= W1);
+    }
+    b0 = max(sb0, W0);
+    b1 = min(sb1, W1);
+    return b0 < b1;
+  }
+  // State at chunk b0: h0 (or NULL for zeros) at the sequence's first
+  // chunk, else the state the previous window left.
+  __device__ const float* state_in(int sb0, int b0, const float* h0, int pair, int h) const {
+    if (b0 > sb0) return resume + (int64_t)h * kD * kD;
+    return h0 ? h0 + (int64_t)pair * kD * kD : nullptr;
+  }
+  // Where the state after chunk b1 - 1 goes: h_final (or nowhere) after the
+  // sequence's last chunk, else the next window's state slot.
+  __device__ float* state_out(int sb1, int b1, float* h_final, int pair, int h) const {
+    if (b1 < sb1) return suspend + (int64_t)h * kD * kD;
+    return h_final ? h_final + (int64_t)pair * kD * kD : nullptr;
+  }
+};
 
 // ------------------------------------------------------- sequential carry
 // One workgroup per (sequence, head, 16-column tile of the state), four
@@ -776,7 +905,8 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
     const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
-    E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, int32_t single) {
+    E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, int32_t single,
+    WindowArgs win) {
   static_assert(kTiles == 1 || kTiles == 2, "one or two column tiles per workgroup");
   constexpr bool kStaged = sizeof(E) == 2;
   static_assert(kStaged || kTiles == 1, "fp32 intermediates: one tile per workgroup");
@@ -804,9 +934,14 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
-  const int b0 = single ? 0 : chunk_offset[n];
-  const int b1 = single ? (int)((T + kC - 1) / kC) : chunk_offset[n + 1];
-  auto block_of = [&](int b) { return inter + ((int64_t)b * H + h) * Inter<E>::kBytes; };
+  // the sequence's chunks [sb0, sb1), of which [b0, b1) fall in this window
+  const int sb0 = single ? 0 : chunk_offset[n];
+  const int sb1 = single ? (int)((T + kC - 1) / kC) : chunk_offset[n + 1];
+  int b0, b1;
+  if (!win.part(sb0, sb1, b0, b1)) return;   // whole workgroup: no barrier reached
+  auto block_of = [&](int b) {
+    return inter + ((int64_t)(b - win.W0) * H + h) * Inter<E>::kBytes;
+  };
   auto slot = [&](int b) { return lds + ((b - b0) % kRing) * kBuf; };
 
   // loader roles: kTiles = 1 splits a chunk's transfers over waves 2 and 3
@@ -917,7 +1052,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     };
     floatx4 S[8];
     Frag<E> fs[4];
-    const float* h0p = h0 ? h0 + (int64_t)pair * kD * kD : nullptr;
+    const float* h0p = win.state_in(sb0, b0, h0, pair, h);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -945,7 +1080,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       for (int nt = 0; nt < 4; ++nt) x[nt] = ld16(src + (nt * kWave + lane) * 4);
     };
     auto out_of = [&](const Frag16<E> (&x)[4], int b) {
-      const int64_t tok0 = seq_start + (int64_t)(b - b0) * kC;
+      const int64_t tok0 = seq_start + (int64_t)(b - sb0) * kC;
       const int len = (int)min((int64_t)kC, seq_end - tok0);
       store_out<E>(x, o, tok0, len, H, h, lane, 16 * jt);
     };
@@ -985,8 +1120,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       read_out(ob, b1 - 1);
       out_of(ob, b1 - 1);
     }
-    if (h_final) {
-      float* hf = h_final + (int64_t)pair * kD * kD;
+    if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -1092,7 +1226,7 @@ __global__ __launch_bounds__(kWave) void carry_short_kernel(
     const uint8_t* __restrict__ inter, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
     const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
-    E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H) {
+    E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, WindowArgs win) {
   // the eight tiles of a (sequence, head) get ids with the same id % 8 (one XCD)
   const int id = blockIdx.x;
   const int pair = (id & 7) + 8 * ((id >> 3) / 8);
@@ -1103,11 +1237,13 @@ __global__ __launch_bounds__(kWave) void carry_short_kernel(
   const int g = lane >> 4;
   const int j = 16 * jt + (lane & 15);
   const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
-  const int b0 = chunk_offset[n], b1 = chunk_offset[n + 1];
+  const int sb0 = chunk_offset[n], sb1 = chunk_offset[n + 1];
+  int b0, b1;
+  if (!win.part(sb0, sb1, b0, b1)) return;
 
   floatx4 S[8];
   Frag<E> fs[4];
-  const float* h0p = h0 ? h0 + (int64_t)pair * kD * kD : nullptr;
+  const float* h0p = win.state_in(sb0, b0, h0, pair, h);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -1118,7 +1254,8 @@ __global__ __launch_bounds__(kWave) void carry_short_kernel(
     for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
 
   for (int b = b0; b < b1; ++b) {
-    const E* blk = reinterpret_cast<const E*>(inter + ((int64_t)b * H + h) * Inter<E>::kBytes);
+    const E* blk =
+        reinterpret_cast<const E*>(inter + ((int64_t)(b - win.W0) * H + h) * Inter<E>::kBytes);
     // O^T = Ut^T + S^T Qt^T from the state at the chunk start
     OutOps<E, 1> po;
     load_out_ops<E, 1>(po, blk, jt, lane);
@@ -1143,11 +1280,10 @@ __global__ __launch_bounds__(kWave) void carry_short_kernel(
                                                   Inter<E>::kGCByte),
                    lane);
     carry_state<E>(S, fs, ps);
-    const int64_t tok0 = seq_start + (int64_t)(b - b0) * kC;
+    const int64_t tok0 = seq_start + (int64_t)(b - sb0) * kC;
     store_out<E>(ob, o, tok0, (int)min((int64_t)kC, seq_end - tok0), H, h, lane, 16 * jt);
   }
-  if (h_final) {
-    float* hf = h_final + (int64_t)pair * kD * kD;
+  if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -1162,13 +1298,16 @@ size_t inter_block_bytes(bool bf16_io) {
 
 
 // phases: bit 0 chunk map, bit 1 intra-chunk, bit 2 carry (all three, in
-// order on one stream, make one prefill call).
+// order on one stream, make one prefill call). The chunk slots [0, n_slots)
+// run in windows of win_slots: per window the intra-chunk kernel, then the
+// carry. state_area holds two [H, 128, 128] float32 states for sequences
+// crossing a window boundary.
 hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q, const void* k,
                             const void* v, const float* log_alpha, const float* beta,
                             const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
-                            int32_t H, int64_t n_slots, void* o, float* h_final,
-                            int32_t* status, int32_t* chunk_offset, uint8_t* inter,
-                            hipStream_t stream) {
+                            int32_t H, int64_t n_slots, int64_t win_slots, void* o,
+                            float* h_final, int32_t* status, int32_t* chunk_offset,
+                            float* state_area, uint8_t* inter, hipStream_t stream) {
   hipError_t err = hipSuccess;
   // A full call on one sequence needs no chunk map: the two kernels derive
   // the chunk range from T and check cu_seqlens themselves.
@@ -1178,22 +1317,6 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if ((phases & 2) && T > 0 && n_slots > 0) {
-    dim3 grid((unsigned)n_slots, (unsigned)H);
-#define KDA_INTRA(E, NORM)                                                                  \
-  intra_kernel<E, NORM><<<grid, kIntraThreads, 0, stream>>>(                                \
-      (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, cu, chunk_offset, status, \
-      n_seqs, T, H, inter, single)
-    if (bf16_io) {
-      if (l2norm) KDA_INTRA(bf16, true); else KDA_INTRA(bf16, false);
-    } else {
-      if (l2norm) KDA_INTRA(float, true); else KDA_INTRA(float, false);
-    }
-#undef KDA_INTRA
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  if (!(phases & 4)) return hipSuccess;
   const int64_t pairs = (int64_t)n_seqs * H;
   // Two column tiles per workgroup once one-tile workgroups (eight per pair)
   // would not all be resident at once (one per CU on the 256-CU MI355X): on
@@ -1209,19 +1332,48 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
   constexpr int64_t kShortMeanTokens = 2 * kC;
   const bool short_seqs = bf16_io && !single && n_seqs > 0 &&
                           T <= kShortMeanTokens * n_seqs;
-  if (short_seqs)
-    carry_short_kernel<bf16><<<(unsigned)(((pairs + 7) / 8) * 64), kWave, 0, stream>>>(
-        inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H);
-  else if (two)
-    carry_kernel<bf16, 2><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
-        inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single);
-  else if (bf16_io)
-    carry_kernel<bf16, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
-        inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single);
-  else
-    carry_kernel<float, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
-        inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H, single);
-  return hipGetLastError();
+  const int64_t n_windows = n_slots > 0 ? (n_slots + win_slots - 1) / win_slots : 1;
+  const int64_t state_floats = (int64_t)H * kD * kD;
+  for (int64_t w = 0; w < n_windows; ++w) {
+    const int64_t W0 = w * win_slots, W1 = std::min(W0 + win_slots, n_slots);
+    if ((phases & 2) && T > 0 && W1 > W0) {
+      dim3 grid((unsigned)(W1 - W0), (unsigned)H);
+#define KDA_INTRA(E, NORM)                                                                  \
+  intra_kernel<E, NORM><<<grid, kIntraThreads, 0, stream>>>(                                \
+      (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, cu, chunk_offset, status, \
+      n_seqs, T, H, inter, single, (int32_t)W0)
+      if (bf16_io) {
+        if (l2norm) KDA_INTRA(bf16, true); else KDA_INTRA(bf16, false);
+      } else {
+        if (l2norm) KDA_INTRA(float, true); else KDA_INTRA(float, false);
+      }
+#undef KDA_INTRA
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    if (!(phases & 4)) continue;
+    WindowArgs win;
+    win.W0 = (int32_t)W0;
+    win.W1 = (int32_t)W1;
+    win.last = w == n_windows - 1;
+    win.resume = state_area + ((w + 1) & 1) * state_floats;
+    win.suspend = state_area + (w & 1) * state_floats;
+    if (short_seqs)
+      carry_short_kernel<bf16><<<(unsigned)(((pairs + 7) / 8) * 64), kWave, 0, stream>>>(
+          inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, win);
+    else if (two)
+      carry_kernel<bf16, 2><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+          inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single, win);
+    else if (bf16_io)
+      carry_kernel<bf16, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+          inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single, win);
+    else
+      carry_kernel<float, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+          inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H, single, win);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kda

@@ -22,9 +22,9 @@ KDA_BAD_QKV, KDA_BAD_GATE, KDA_BAD_BETA, KDA_BAD_CU = 1, 2, 4, 8
 CHUNK = 64
 HEAD_DIM = 128
 
-EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_phase",
-           "kda_decode_step", "kda_recurrent_fwd", "kda_rmsnorm_gate", "kda_check_inputs",
-           "kda_status_string", "kda_version")
+EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_workspace_min_bytes",
+           "kda_chunk_fwd", "kda_chunk_fwd_phase", "kda_decode_step", "kda_recurrent_fwd", "kda_rmsnorm_gate",
+           "kda_check_inputs", "kda_status_string", "kda_version")
 
 _LIB = None
 
@@ -46,6 +46,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
         L.kda_chunk_fwd_workspace_bytes.restype = sz
+        L.kda_chunk_fwd_workspace_min_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+        L.kda_chunk_fwd_workspace_min_bytes.restype = sz
         L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                     ctypes.c_int, ctypes.c_uint32, vp, vp, vp, sz, vp]
         L.kda_chunk_fwd.restype = ctypes.c_int
@@ -136,9 +138,18 @@ def chunk_fwd_workspace_bytes(n_seqs: int, total_tokens: int, heads: int,
                                                    HEAD_DIM, HEAD_DIM, _io(io_dtype)))
 
 
-def alloc_workspace(n_seqs, total_tokens, heads, io_dtype, device) -> torch.Tensor:
-    """A 256-byte aligned uint8 device buffer of the required size."""
-    nbytes = chunk_fwd_workspace_bytes(n_seqs, total_tokens, heads, io_dtype)
+def chunk_fwd_workspace_min_bytes(n_seqs: int, total_tokens: int, heads: int,
+                                  io_dtype: torch.dtype) -> int:
+    return int(lib().kda_chunk_fwd_workspace_min_bytes(n_seqs, total_tokens, heads,
+                                                       HEAD_DIM, HEAD_DIM, _io(io_dtype)))
+
+
+def alloc_workspace(n_seqs, total_tokens, heads, io_dtype, device, nbytes=None) -> torch.Tensor:
+    """A 256-byte aligned uint8 device buffer of the recommended size (or
+    nbytes: any size from chunk_fwd_workspace_min_bytes up works; a smaller
+    workspace runs the prefill in more windows of chunk slots)."""
+    if nbytes is None:
+        nbytes = chunk_fwd_workspace_bytes(n_seqs, total_tokens, heads, io_dtype)
     if nbytes == 0:
         raise ValueError("invalid sizes for the prefill workspace")
     raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)

@@ -75,7 +75,7 @@ def _normal_f32(rng, shape, post=None):
     given, transforms each drawn block in place on the thread pool while the
     next blocks are drawn."""
     out = np.empty(shape, dtype=np.float32)
-    flat = out.reshape(shape[0], -1)
+    flat = out.reshape(shape[0], int(np.prod(shape[1:], dtype=np.int64)))
     if post is None:
         for s in range(0, shape[0], _BLOCK):
             e = min(s + _BLOCK, shape[0])

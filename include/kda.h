@@ -87,15 +87,29 @@ typedef enum {
 #define KDA_FLAG_QK_L2NORM 1u
 
 /*
- * kda_chunk_fwd_workspace_bytes
- *   Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if an
- *   argument is invalid). The workspace must be 256-byte aligned.
+ * kda_chunk_fwd_workspace_bytes, kda_chunk_fwd_workspace_min_bytes
+ *   Recommended and smallest sizes of the device workspace of kda_chunk_fwd
+ *   for these sizes (0 if an argument is invalid). The workspace must be
+ *   256-byte aligned.
  *   n_seqs: sequences N in the packed batch (N = 1 when cu_seqlens is NULL).
  *   total_tokens: T, tokens over all sequences.
+ *   The prefill runs over windows of chunk slots, as many slots per window
+ *   as the given workspace holds (below), so any size from the smallest up
+ *   works and the results do not depend on it. For one sequence the
+ *   recommended size holds every chunk of calls up to about 512 MiB of
+ *   intermediates (8192 tokens x 32 heads in bf16 is one window) and that
+ *   much otherwise: it does not grow with T beyond that. Windows follow the
+ *   chunk slots in sequence order, so a window holds few sequences of a
+ *   packed batch and windows run one after the other: for N > 1 the
+ *   recommended size holds up to 8 GiB of intermediates. The smallest size
+ *   holds one chunk slot (slowest).
  */
 size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
                                      int32_t heads, int32_t dk, int32_t dv,
                                      kda_io_dtype io);
+size_t kda_chunk_fwd_workspace_min_bytes(int32_t n_seqs, int64_t total_tokens,
+                                         int32_t heads, int32_t dk, int32_t dv,
+                                         kda_io_dtype io);
 
 /*
  * kda_chunk_fwd - chunked prefill over a packed batch of sequences.
@@ -117,8 +131,10 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
  *                   same pointer as h0 (in-place continuation) but must not
  *                   partially overlap it
  *   workspace       device scratch of at least
- *                   kda_chunk_fwd_workspace_bytes(...) bytes, 256-byte
- *                   aligned; its contents on return are described below
+ *                   kda_chunk_fwd_workspace_min_bytes(...) bytes (the
+ *                   recommended size is kda_chunk_fwd_workspace_bytes(...)),
+ *                   256-byte aligned; its contents on return are described
+ *                   below
  *   A sequence of length 0 copies h0 (or zeros) to h_final. T = 0 writes
  *   nothing but h_final.
  *   Errors: KDA_ERR_NULL (q, k, v, log_alpha, beta or o NULL when T > 0;
@@ -127,19 +143,29 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t total_tokens,
  *   (sequence, head) pairs),
  *   KDA_ERR_UNSUPPORTED (d_k, d_v != 128, unknown dtype or flag bit,
  *   heads > 65535),
- *   KDA_ERR_WORKSPACE (NULL, smaller than required, not 256-byte aligned),
+ *   KDA_ERR_WORKSPACE (NULL, smaller than the minimum, not 256-byte
+ *   aligned),
  *   KDA_ERR_ALIAS (o overlapping an input; h_final overlapping q, k, v,
  *   log_alpha, beta or o; h_final partially overlapping h0), KDA_ERR_HIP.
  *
  * Workspace contents after the call (for inspection and tests; the format
  * is internal and may change). E is the element type: bf16 for
- * KDA_IO_BF16, float32 for KDA_IO_F32.
+ * KDA_IO_BF16, float32 for KDA_IO_F32. The chunk slots 0 .. S - 1, with
+ * S = ceil(T / 64) + N - 1 (at least the chunk count), run in windows of
+ * W slots, W = min(S, (bytes - inter_offset) / (H * block)): per window
+ * the intra-chunk kernel fills the window's blocks, then the carry
+ * consumes them.
  *   [0, 4)          int32 status: 0 ok, 1 malformed cu_seqlens
  *   [256, ...)      int32 chunk_offset[N + 1]: first global chunk index of
  *                   each sequence (exclusive prefix sum of ceil(L_n / 64))
- *   [inter_offset)  per (global chunk b, head h), a block of
- *                   40960 E + 128 float32, blocks ordered [b][h], where
- *                   inter_offset = 256 + round_up(4 (N + 1), 256):
+ *   [state_offset)  two float32 [H, 128, 128] states, state_offset =
+ *                   256 + round_up(4 (N + 1), 256): the state of the
+ *                   sequence crossing a window boundary, left by one window
+ *                   for the next (the two slots alternate)
+ *   [inter_offset)  per (chunk b of the last window, head h), a block of
+ *                   block = 40960 E + 128 float32 bytes, ordered
+ *                   [b - W0][h] (W0 = the window's first slot), where
+ *                   inter_offset = state_offset + 2 * H * 65536:
  *       XA  16384 E  [-W ; Qt]  as A-fragments, 8 row tiles x 4 k-blocks
  *       KT   8192 E  K'^T       as A-fragments, 8 row tiles x 2 k-blocks
  *       UC  16384 E  U and Ut^T as C-fragments, 8 column tiles x 8 row
@@ -183,8 +209,10 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
  *   phase 2: carry kernel (state propagation and chunk outputs; writes o and
  *            h_final)
  * Arguments, validation and errors are those of kda_chunk_fwd (an invalid
- * phase returns KDA_ERR_SHAPE). Phases 0, 1, 2 enqueued in order on one
- * stream with the same arguments compute exactly what kda_chunk_fwd does.
+ * phase returns KDA_ERR_SHAPE), except that the workspace must hold every
+ * chunk slot in one window (else KDA_ERR_WORKSPACE). Phases 0, 1, 2
+ * enqueued in order on one stream with the same arguments compute exactly
+ * what kda_chunk_fwd does.
  */
 kda_status kda_chunk_fwd_phase(int32_t phase, const void *q, const void *k,
                                const void *v, const float *log_alpha,

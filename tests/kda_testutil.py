@@ -56,10 +56,11 @@ def _lane_maps():
 
 
 def decode_block(ws_bytes, b, h, H, N, io):
-    """Returns dict(W, Qt, Kp, U, Ut, gC) (float64) of chunk b, head h."""
+    """Returns dict(W, Qt, Kp, U, Ut, gC) (float64) of chunk b, head h (the
+    workspace of a call whose window held every chunk)."""
     esz = 2 if io == "bf16" else 4
     block = 40960 * esz + 128 * 4
-    inter = 256 + (4 * (N + 1) + 255) // 256 * 256
+    inter = 256 + (4 * (N + 1) + 255) // 256 * 256 + 2 * H * 128 * 128 * 4
     base = inter + (b * H + h) * block
     raw = np.frombuffer(ws_bytes, dtype=np.uint8, count=block, offset=base)
     if io == "bf16":

@@ -12,10 +12,13 @@
 
 namespace kda {
 int g_chunk = 0, g_rec = 0, g_epi = 0, g_chk = 0;
+int64_t g_win = -1;   // window size of the last chunk launch
 hipError_t launch_chunk_fwd(int, bool, bool, const void*, const void*, const void*, const float*,
                             const float*, const float*, const int32_t*, int32_t, int64_t, int32_t,
-                            int64_t, void*, float*, int32_t*, int32_t*, uint8_t*, hipStream_t) {
+                            int64_t, int64_t win_slots, void*, float*, int32_t*, int32_t*, float*,
+                            uint8_t*, hipStream_t) {
   ++g_chunk;
+  g_win = win_slots;
   return hipSuccess;
 }
 // per chunk-head block: [-W ; Qt], K'^T, [U ; Ut] in the I/O type, gamma_C fp32
@@ -52,6 +55,7 @@ int main() {
   const uintptr_t MB = 1 << 20;
   const int T = 100, H = 2;
   const size_t ws = kda_chunk_fwd_workspace_bytes(1, T, H, 128, 128, KDA_IO_BF16);
+  const size_t ws_min = kda_chunk_fwd_workspace_min_bytes(1, T, H, 128, 128, KDA_IO_BF16);
   auto prefill = [&](const void* q, const void* o, const float* h0, float* hf, const void* wsp,
                      size_t wsb, int32_t n, const int32_t* cu, int64_t t, uint32_t flags) {
     return (int)kda_chunk_fwd(q, at(1 * 64 * MB), at(2 * 64 * MB), (const float*)at(3 * 64 * MB),
@@ -67,7 +71,17 @@ int main() {
   expect(prefill(at(0), o, nullptr, nullptr, w, ws, 1, nullptr, 0, 0), KDA_OK, "prefill T=0");
   expect(prefill(nullptr, o, h0, hf, w, ws, 1, nullptr, T, 0), KDA_ERR_NULL, "prefill q NULL");
   expect(prefill(at(8), o, h0, hf, w, ws, 1, nullptr, T, 0), KDA_ERR_ALIGN, "prefill misaligned");
-  expect(prefill(at(0), o, h0, hf, w, ws - 1, 1, nullptr, T, 0), KDA_ERR_WORKSPACE, "workspace");
+  expect(prefill(at(0), o, h0, hf, w, ws_min - 1, 1, nullptr, T, 0), KDA_ERR_WORKSPACE,
+         "workspace");
+  expect(prefill(at(0), o, h0, hf, w, ws_min, 1, nullptr, T, 0), KDA_OK, "one-slot window");
+  if (kda::g_win != 1) ++fails;
+  expect(prefill(at(0), o, h0, hf, w, ws, 1, nullptr, T, 0), KDA_OK, "one window");
+  if (kda::g_win != 2) ++fails;
+  expect((int)kda_chunk_fwd_phase(1, at(0), at(64 * MB), at(128 * MB),
+                                  (const float*)at(192 * MB), (const float*)at(256 * MB), h0,
+                                  nullptr, 1, T, H, 128, 128, KDA_IO_BF16, 0,
+                                  const_cast<void*>(o), hf, const_cast<void*>(w), ws_min, nullptr),
+         KDA_ERR_WORKSPACE, "phase with a partial window");
   expect(prefill(at(0), at(4096), h0, hf, w, ws, 1, nullptr, T, 0), KDA_ERR_ALIAS, "o over q");
   expect(prefill(at(0), o, h0, hf, w, ws, 1, nullptr, T, 2), KDA_ERR_UNSUPPORTED, "flag");
   expect(prefill(at(0), o, h0, hf, w, ws, 1, nullptr, -1, 0), KDA_ERR_SHAPE, "T < 0");
@@ -135,7 +149,7 @@ int main() {
                                fl, nullptr), KDA_ERR_UNSUPPORTED, "check io 4");
   for (int st = -1; st < 9; ++st)
     if (kda_status_string((kda_status)st) == nullptr) ++fails;
-  if (kda::g_chunk != 5 || kda::g_rec != 2 || kda::g_epi != 1 || kda::g_chk != 2) {
+  if (kda::g_chunk != 7 || kda::g_rec != 2 || kda::g_epi != 1 || kda::g_chk != 2) {
     fprintf(stderr, "launch counts %d %d %d %d\n", kda::g_chunk, kda::g_rec, kda::g_epi,
             kda::g_chk);
     ++fails;

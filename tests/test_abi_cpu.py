@@ -26,6 +26,8 @@ def lib():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
     L.kda_chunk_fwd_workspace_bytes.restype = sz
+    L.kda_chunk_fwd_workspace_min_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+    L.kda_chunk_fwd_workspace_min_bytes.restype = sz
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                 ctypes.c_int, ctypes.c_uint32, vp, vp, vp, sz, vp]
     L.kda_chunk_fwd.restype = ctypes.c_int
@@ -86,14 +88,36 @@ def _block_bytes(io):
 
 @pytest.mark.parametrize("io", [F32, BF16])
 @pytest.mark.parametrize("N,T,H", [(1, 0, 1), (1, 1, 1), (1, 8192, 32), (16, 135000, 32),
-                                   (3, 64, 2), (300, 100000, 4)])
+                                   (3, 64, 2), (300, 100000, 4), (1, 1 << 20, 32),
+                                   (1, 1 << 24, 64), (16, 1 << 22, 32)])
 def test_workspace_formula(lib, io, N, T, H):
+    """Recommended size: the whole call's blocks up to 512 MiB of them (8 GiB
+    for a packed batch), else that much (it stops growing with T); smallest:
+    one chunk slot."""
     slots = (T + 63) // 64 + N - 1
-    inter = 256 + (4 * (N + 1) + 255) // 256 * 256
-    assert lib.kda_chunk_fwd_workspace_bytes(N, T, H, 128, 128, io) == inter + slots * H * _block_bytes(io)
+    inter = 256 + (4 * (N + 1) + 255) // 256 * 256 + 2 * H * 128 * 128 * 4
+    per_slot = H * _block_bytes(io)
+    cap = (512 << 20) if N == 1 else (8 << 30)
+    win = min(slots, max(1, cap // per_slot))
+    assert lib.kda_chunk_fwd_workspace_bytes(N, T, H, 128, 128, io) == inter + win * per_slot
+    assert lib.kda_chunk_fwd_workspace_min_bytes(N, T, H, 128, 128, io) == \
+        inter + (per_slot if slots > 0 else 0)
+    assert lib.kda_chunk_fwd_workspace_bytes(N, T, H, 128, 128, io) <= inter + cap + per_slot
+
+
+def test_workspace_for_a_long_call_is_bounded(lib):
+    """A million-token call needs no more workspace than a 16K-token one."""
+    big = lib.kda_chunk_fwd_workspace_bytes(1, 1 << 20, 32, 128, 128, BF16)
+    mid = lib.kda_chunk_fwd_workspace_bytes(1, 1 << 14, 32, 128, 128, BF16)
+    assert big == mid < (600 << 20)
 
 
 def test_workspace_invalid(lib):
+    for f in (lib.kda_chunk_fwd_workspace_bytes, lib.kda_chunk_fwd_workspace_min_bytes):
+        assert f(0, 10, 1, 128, 128, BF16) == 0
+        assert f(1, -1, 1, 128, 128, BF16) == 0
+        assert f(1, 10, 70000, 128, 128, BF16) == 0
+        assert f(1, 10, 1, 128, 64, BF16) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(0, 10, 1, 128, 128, BF16) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(1, -1, 1, 128, 128, BF16) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(1, 10, 0, 128, 128, BF16) == 0
@@ -438,3 +462,13 @@ def test_binding_rejects_misshaped_check_inputs_tensor(name, shape):
     a[name] = z(*shape, dt=a[name].dtype)
     with pytest.raises(ValueError, match="shape"):
         kda.check_inputs(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], flags=a["flags"])
+
+
+def test_workspace_below_minimum_and_phase_windows(lib):
+    """Below the smallest size the call is refused; a phase launch needs
+    every chunk slot in one window."""
+    a = prefill_args(lib, T=1000, H=2)
+    mn = lib.kda_chunk_fwd_workspace_min_bytes(1, 1000, 2, 128, 128, BF16)
+    assert call_prefill(lib, dict(a, ws_bytes=mn - 1)) == WS
+    for ph in (1, 2):
+        assert call_prefill(lib, dict(a, ws_bytes=mn), phase=ph) == WS

@@ -90,6 +90,17 @@ def test_prefill_extreme_decay_exact_fallback(io):
     _check_prefill(p, o, hf)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_prefill_extreme_recipe_packed(io):
+    """The "extreme" gate recipe (half the channels at log alpha in [-4, -3],
+    so every 16-token diagonal block takes the exact path) on a packed batch
+    with ragged tails and nonzero initial states."""
+    p = workloads.make_prefill([300, 17, 64, 0, 129], H=4, seed=11, io=io, decay="extreme",
+                               h0_std=0.05)
+    o, hf = _run_prefill(p)
+    _check_prefill(p, o, hf)
+
+
 def _check_prefill_l2norm(p, o, hf):
     ro, rh = recurrent.forward(recurrent.l2norm(p.q), recurrent.l2norm(p.k), p.v,
                                p.log_alpha, p.beta, p.h0, p.cu_seqlens)

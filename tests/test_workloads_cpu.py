@@ -82,3 +82,9 @@ def test_packed_lengths_are_the_first_draw():
     assert np.allclose(p.q, q0, rtol=0, atol=1e-7)
     with pytest.raises(ValueError):
         workloads.make_prefill((16,) * 5, 2, seed=77, io="f32", draw_lengths=spec)
+
+
+def test_empty_batch_draws():
+    """A batch of empty sequences draws only its initial states."""
+    p = workloads.make_prefill([0, 0, 0], 2, seed=608, io="bf16", h0_std=0.05)
+    assert p.T == 0 and p.q.shape == (0, 2, 128) and p.h0.shape == (3, 2, 128, 128)
