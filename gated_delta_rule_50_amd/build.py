@@ -21,7 +21,7 @@ INCLUDE = ROOT / "include"
 LIB = PKG / "libkda.so"
 BUILD = ROOT / "_build"
 SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_recurrent.hip", "kda_epilogue.hip",
-           "kda_check.hip"]
+           "kda_check.hip", "kda_noalloc.hip"]
 
 
 def hipcc() -> str:

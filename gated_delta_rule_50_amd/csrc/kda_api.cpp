@@ -360,6 +360,8 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_ALIAS: return "an output overlaps an input it must not";
     case KDA_ERR_HIP: return "the HIP runtime reported a launch error";
     case KDA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned (beta, cu_seqlens: 4)";
+    case KDA_ERR_SCRATCH:
+      return "the call needs more workspace than the allocation-free entry point holds";
   }
   return "unknown status";
 }

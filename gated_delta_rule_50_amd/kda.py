@@ -14,7 +14,7 @@ import torch
 LIB_PATH = Path(__file__).resolve().parent / "libkda.so"
 
 KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_UNSUPPORTED = 0, 1, 2, 3
-KDA_ERR_WORKSPACE, KDA_ERR_ALIAS, KDA_ERR_HIP, KDA_ERR_ALIGN = 4, 5, 6, 7
+KDA_ERR_WORKSPACE, KDA_ERR_ALIAS, KDA_ERR_HIP, KDA_ERR_ALIGN, KDA_ERR_SCRATCH = 4, 5, 6, 7, 8
 KDA_IO_F32, KDA_IO_BF16 = 0, 1
 KDA_STATE_F32, KDA_STATE_BF16 = 0, 1
 KDA_FLAG_QK_L2NORM = 1
@@ -23,8 +23,10 @@ CHUNK = 64
 HEAD_DIM = 128
 
 EXPORTS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_workspace_min_bytes",
-           "kda_chunk_fwd", "kda_chunk_fwd_phase", "kda_decode_step", "kda_recurrent_fwd", "kda_rmsnorm_gate",
+           "kda_chunk_fwd", "kda_chunk_fwd_phase", "kda_chunk_fwd_noalloc", "kda_decode_step", "kda_recurrent_fwd", "kda_rmsnorm_gate",
            "kda_check_inputs", "kda_status_string", "kda_version")
+# bytes of the fixed device array kda_chunk_fwd_noalloc uses as its workspace
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _LIB = None
 
@@ -53,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd.restype = ctypes.c_int
         L.kda_chunk_fwd_phase.argtypes = [i32] + L.kda_chunk_fwd.argtypes
         L.kda_chunk_fwd_phase.restype = ctypes.c_int
+        L.kda_chunk_fwd_noalloc.argtypes = L.kda_chunk_fwd.argtypes[:16] + [vp]
+        L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                       ctypes.c_int, vp, vp]
         L.kda_decode_step.restype = ctypes.c_int
@@ -168,7 +172,8 @@ class Prefill:
     """
 
     def __init__(self, q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
-                 h_final=None, want_final=True, workspace=None, qk_l2norm=False):
+                 h_final=None, want_final=True, workspace=None, qk_l2norm=False,
+                 noalloc=False):
         dev = k.device
         self.T, self.H = _head_rows(k)
         if cu_seqlens is not None and cu_seqlens.dim() != 1:
@@ -194,24 +199,36 @@ class Prefill:
             h_final = torch.empty((self.N, self.H, k.shape[2], v.shape[2]),
                                   dtype=torch.float32, device=dev)
         _check(h_final, "h_final", torch.float32, dev)
-        if workspace is None:
+        if noalloc and workspace is not None:
+            raise ValueError("noalloc calls take no workspace")
+        if workspace is None and not noalloc:
             workspace = alloc_workspace(self.N, self.T, self.H, k.dtype, dev)
         _check(workspace, "workspace", torch.uint8, dev)
         self.device = dev
+        self.noalloc = noalloc
         self.o, self.h_final, self.workspace = o, h_final, workspace
         self._keep = (q, k, v, log_alpha, beta, h0, cu_seqlens)
         self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
                       _ptr(cu_seqlens), self.N, self.T, self.H, int(k.shape[2]),
                       int(v.shape[2]), self.io, KDA_FLAG_QK_L2NORM if qk_l2norm else 0,
-                      _ptr(o), _ptr(h_final), _ptr(workspace), workspace.numel())
+                      _ptr(o), _ptr(h_final))
+        if not noalloc:
+            self._args += (_ptr(workspace), workspace.numel())
 
     def run(self, stream=None):
-        st = lib().kda_chunk_fwd(*self._args, _stream(stream, self.device))
-        if st != KDA_OK:
-            raise KDAError(st, "kda_chunk_fwd")
+        if self.noalloc:
+            st = lib().kda_chunk_fwd_noalloc(*self._args, _stream(stream, self.device))
+            if st != KDA_OK:
+                raise KDAError(st, "kda_chunk_fwd_noalloc")
+        else:
+            st = lib().kda_chunk_fwd(*self._args, _stream(stream, self.device))
+            if st != KDA_OK:
+                raise KDAError(st, "kda_chunk_fwd")
         return self.o, self.h_final
 
     def run_phase(self, phase: int, stream=None):
+        if self.noalloc:
+            raise ValueError("the phase entry point takes a caller workspace")
         st = lib().kda_chunk_fwd_phase(int(phase), *self._args, _stream(stream, self.device))
         if st != KDA_OK:
             raise KDAError(st, f"kda_chunk_fwd_phase({phase})")
@@ -223,6 +240,16 @@ def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
     return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
                    want_final=want_final, workspace=workspace,
                    qk_l2norm=qk_l2norm).run(stream)
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
+                      h_final=None, want_final=True, qk_l2norm=False, stream=None):
+    """chunk_fwd through kda_chunk_fwd_noalloc: the workspace is the
+    library's fixed per-GPU array, so the call itself allocates nothing
+    (pass o, and h_final or want_final=False, to allocate nothing here
+    either). Calls overlapping on one GPU race on that array."""
+    return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
+                   want_final=want_final, qk_l2norm=qk_l2norm, noalloc=True).run(stream)
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):

@@ -18,7 +18,8 @@
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library
  *    never allocates device memory; scratch space is a caller-supplied
- *    workspace sized by kda_chunk_fwd_workspace_bytes().
+ *    workspace sized by kda_chunk_fwd_workspace_bytes() (or, for
+ *    kda_chunk_fwd_noalloc, a fixed array inside the library).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    null stream). Nothing synchronises the host.
  *  - Arguments that the host can see (pointers, sizes, dtypes, aliasing) are
@@ -70,7 +71,9 @@ typedef enum {
   KDA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned   */
   KDA_ERR_ALIAS = 5,       /* an output overlaps an input it must not      */
   KDA_ERR_HIP = 6,         /* the HIP runtime reported a launch error      */
-  KDA_ERR_ALIGN = 7        /* a tensor pointer is misaligned (see above)   */
+  KDA_ERR_ALIGN = 7,       /* a tensor pointer is misaligned (see above)   */
+  KDA_ERR_SCRATCH = 8      /* the call needs more workspace than
+                              kda_chunk_fwd_noalloc's fixed array holds    */
 } kda_status;
 
 typedef enum {
@@ -222,6 +225,36 @@ kda_status kda_chunk_fwd_phase(int32_t phase, const void *q, const void *k,
                                int32_t dv, kda_io_dtype io, uint32_t flags,
                                void *o, float *h_final, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * kda_chunk_fwd_noalloc - kda_chunk_fwd without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The workspace is a fixed array of KDA_NOALLOC_SCRATCH_BYTES bytes of
+ * device memory inside the library, one per GPU, held from the first call
+ * on that GPU until the process ends; the call uses the copy of the calling
+ * thread's current device (the stream must belong to it). The call
+ * allocates nothing (no hipMalloc, no library allocation); the caller still
+ * supplies every input and output. Arguments, results and errors are those
+ * of kda_chunk_fwd, plus KDA_ERR_SCRATCH when
+ * kda_chunk_fwd_workspace_min_bytes(...) for these sizes exceeds the array
+ * (returned before any HIP call) and KDA_ERR_HIP when the array's device
+ * address cannot be obtained. The prefill's windows are sized to the array
+ * (about 50 chunk slots at 32 bf16 heads), so T is not limited by it. Every call on one GPU uses the same array and
+ * leaves its contents behind (the workspace contents kda_chunk_fwd
+ * describes): calls that overlap on one GPU, on different streams or from
+ * different threads, race and give undefined results; calls ordered on one
+ * stream do not.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20) /* 128 MiB per GPU */
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 const float *log_alpha, const float *beta,
+                                 const float *h0, const int32_t *cu_seqlens,
+                                 int32_t n_seqs, int64_t total_tokens,
+                                 int32_t heads, int32_t dk, int32_t dv,
+                                 kda_io_dtype io, uint32_t flags, void *o,
+                                 float *h_final, void *stream);
 
 /*
  * kda_decode_step - one recurrent step for a batch of sequences.

@@ -14,7 +14,7 @@ ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "kda.h"
 LIB = ROOT / "gated_delta_rule_50_amd" / "libkda.so"
 
-OK, NULL, SHAPE, UNSUP, WS, ALIAS, HIPERR, ALIGN = range(8)
+OK, NULL, SHAPE, UNSUP, WS, ALIAS, HIPERR, ALIGN, SCRATCH = range(9)
 F32, BF16 = 0, 1
 
 
@@ -33,6 +33,8 @@ def lib():
     L.kda_chunk_fwd.restype = ctypes.c_int
     L.kda_chunk_fwd_phase.argtypes = [i32] + L.kda_chunk_fwd.argtypes
     L.kda_chunk_fwd_phase.restype = ctypes.c_int
+    L.kda_chunk_fwd_noalloc.argtypes = L.kda_chunk_fwd.argtypes[:16] + [vp]
+    L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                   vp, vp]
     L.kda_decode_step.restype = ctypes.c_int
@@ -462,6 +464,21 @@ def test_binding_rejects_misshaped_check_inputs_tensor(name, shape):
     a[name] = z(*shape, dt=a[name].dtype)
     with pytest.raises(ValueError, match="shape"):
         kda.check_inputs(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], flags=a["flags"])
+
+
+def test_noalloc_refuses_calls_beyond_its_array(lib):
+    """kda_chunk_fwd_noalloc refuses, before any HIP call, a call whose
+    smallest workspace (one chunk slot) exceeds its fixed array (fake
+    addresses, never touched)."""
+    cap = 128 << 20
+    T, H = 64, 1024
+    assert lib.kda_chunk_fwd_workspace_min_bytes(1, T, H, 128, 128, BF16) > cap
+    assert lib.kda_chunk_fwd_workspace_min_bytes(1, 1 << 24, 32, 128, 128, BF16) <= cap
+    p = [0x100000 * (i + 1) for i in range(9)]
+    st = lib.kda_chunk_fwd_noalloc(p[0], p[1], p[2], p[3], p[4], None, None, 1, T, H, 128,
+                                   128, BF16, 0, p[5], p[6], None)
+    assert st == SCRATCH
+    assert lib.kda_status_string(SCRATCH).decode().startswith("the call needs more workspace")
 
 
 def test_workspace_below_minimum_and_phase_windows(lib):
