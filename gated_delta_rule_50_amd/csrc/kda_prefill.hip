@@ -744,8 +744,7 @@ struct WindowArgs {
 // wave reads chunk b+1's fragments into a second register set while it
 // computes chunk b, so chunk b's slot is free for chunk b+3 during chunk b;
 // the output wave loads its Qt fragments and Ut^T from global memory two
-// chunks ahead. fp32 intermediates (fp32 I/O only) are read from global
-// memory by the compute waves without prefetch.
+// chunks ahead. (fp32 intermediates have their own carry, carry_f32_kernel.)
 constexpr int kRing = 3;
 constexpr int kCarryThreads = 256;
 constexpr int64_t kCarryRound = 256;   // carry workgroups resident at once (one per CU)
@@ -908,15 +907,14 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, int32_t single,
     WindowArgs win) {
   static_assert(kTiles == 1 || kTiles == 2, "one or two column tiles per workgroup");
-  constexpr bool kStaged = sizeof(E) == 2;
-  static_assert(kStaged || kTiles == 1, "fp32 intermediates: one tile per workgroup");
+  static_assert(sizeof(E) == 2, "bf16 intermediates (fp32 ones: carry_f32_kernel)");
   constexpr int kGroups = 8 / kTiles;                 // workgroups per (sequence, head)
   constexpr int kUOff = kStageW + kStageKT;           // slot offset of the U tiles
   constexpr int kGOff = kUOff + kTiles * kStageU;     // slot offset of gamma_C
   constexpr int kBuf = kGOff + 1024;
   constexpr int kSBuf = 4 * kWave * 8;                // one published state
   constexpr int kOBuf = 4 * kWave * 4;                // one O tile
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStaged ? kRing * kBuf : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBuf];
   __shared__ __attribute__((aligned(16))) E sS[kTiles * 2 * kSBuf];   // published states
   __shared__ __attribute__((aligned(16))) int32_t sTouch[kWave];       // L2 touch sink
   __shared__ __attribute__((aligned(16))) E sO[kTiles * 2 * kOBuf];   // output tiles
@@ -1033,23 +1031,13 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) store8(dst + (kb * kWave + lane) * 8, fs[kb]);
     };
-    // operand sources of chunk b: the LDS ring (bf16) or the block (fp32)
-    auto w_src = [&](int b) -> const E* {
-      if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b));
-      else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kXA;
+    // operand sources of chunk b in the LDS ring
+    auto w_src = [&](int b) { return reinterpret_cast<const E*>(slot(b)); };
+    auto kt_src = [&](int b) { return reinterpret_cast<const E*>(slot(b) + kStageW); };
+    auto u_src = [&](int b) {
+      return reinterpret_cast<const E*>(slot(b) + kUOff + w * kStageU);
     };
-    auto kt_src = [&](int b) -> const E* {
-      if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b) + kStageW);
-      else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kKT;
-    };
-    auto u_src = [&](int b) -> const E* {
-      if constexpr (kStaged) return reinterpret_cast<const E*>(slot(b) + kUOff + w * kStageU);
-      else return reinterpret_cast<const E*>(block_of(b)) + Inter<E>::kUC + jt * 8 * kWave * 4;
-    };
-    auto gc_src = [&](int b) -> const float* {
-      if constexpr (kStaged) return reinterpret_cast<const float*>(slot(b) + kGOff);
-      else return reinterpret_cast<const float*>(block_of(b) + Inter<E>::kGCByte);
-    };
+    auto gc_src = [&](int b) { return reinterpret_cast<const float*>(slot(b) + kGOff); };
     floatx4 S[8];
     Frag<E> fs[4];
     const float* h0p = win.state_in(sb0, b0, h0, pair, h);
@@ -1069,7 +1057,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     auto fetch = [&](StateOps<E>& p, int b) {
       load_state_ops(p, w_src(b), kt_src(b), u_src(b), gc_src(b), lane);
     };
-    if (kStaged && b0 < b1) fetch(sa, b0);
+    if (b0 < b1) fetch(sa, b0);
     // chunk b0's slot is read before the loaders reuse it for chunk b0 + 3
     __builtin_amdgcn_s_waitcnt(0xC07F);
     ring_barrier();
@@ -1087,20 +1075,14 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     auto step = [&](int b, StateOps<E>& cur, StateOps<E>& nxt) {
       Frag16<E> ob[4];
       read_out(ob, b - 1);   // first, so its wait does not cover the prefetch
-      if constexpr (kStaged) {
-        fetch(nxt, min(b + 1, b1 - 1));
-      } else {
-        fetch(cur, b);
-      }
+      fetch(nxt, min(b + 1, b1 - 1));
       carry_state<E>(S, fs, cur);
-      if constexpr (kStaged) {
-        // one prefetch read per product: a wave stalls once 16 LDS reads
-        // are outstanding, which would hold the products back
+      // one prefetch read per product: a wave stalls once 16 LDS reads are
+      // outstanding, which would hold the products back
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        }
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       }
       if (b > b0) out_of(ob, b - 1);
       publish(fs, b + 1);
@@ -1165,23 +1147,19 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     }
   } else if (kTiles == 1) {
     // two loaders
-    if (kStaged) {
-      for (int b = b0; b < b0 + 3 && b < b1; ++b) issue(b);
-      loader_wait(b0 + 2 < b1, false, false);   // chunks b0, b0 + 1 landed
-      if (w == 3)
-        for (int b = b0 + 3; b < b0 + kTouchAhead && b < b1; ++b) touch(b);
-    }
+    for (int b = b0; b < b0 + 3 && b < b1; ++b) issue(b);
+    loader_wait(b0 + 2 < b1, false, false);   // chunks b0, b0 + 1 landed
+    if (w == 3)
+      for (int b = b0 + 3; b < b0 + kTouchAhead && b < b1; ++b) touch(b);
     ring_barrier();
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
-      if (kStaged) {
-        const bool dma = b + 3 < b1;
-        const bool tch = w == 3 && b + kTouchAhead < b1;
-        const bool prev = w == 3 && b + kTouchAhead - 1 < b1;
-        if (dma) issue(b + 3);
-        if (tch) touch(b + kTouchAhead);
-        loader_wait(dma, tch, prev);
-      }
+      const bool dma = b + 3 < b1;
+      const bool tch = w == 3 && b + kTouchAhead < b1;
+      const bool prev = w == 3 && b + kTouchAhead - 1 < b1;
+      if (dma) issue(b + 3);
+      if (tch) touch(b + kTouchAhead);
+      loader_wait(dma, tch, prev);
       ring_barrier();
     }
   } else {
@@ -1206,6 +1184,222 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (b + 3 < b1) issue(b + 3);
       if (b + kTouchAhead < b1) touch(b + kTouchAhead);
+      ring_barrier();
+    }
+  }
+}
+
+// ------------------------------------------------------- carry, fp32 I/O
+// The carry for fp32 intermediates (fp32 I/O). A chunk's state operands
+// take 69 KiB in fp32, so the ring has two slots and the loaders stay one
+// chunk ahead; fp32 products run at a sixteenth of the bf16 rate (eight
+// 16x16x4 products per fragment), so a chunk's 256 state products take
+// long enough to hide that lead. One workgroup per (sequence, head,
+// 16-column tile), four waves:
+//   wave 0  state wave: reads each operand fragment from the ring just
+//           before its products (the next one in flight), state in
+//           registers, publishes the state each chunk
+//   wave 1  output wave: O^T = Ut^T + S^T Qt^T with Qt and Ut held in
+//           registers one chunk ahead; it stores O itself, issuing the
+//           next chunk's loads first so that its load waits never include
+//           its stores
+//   waves 2, 3  loaders: [-W] and U; K'^T, gamma_C and the L2 touches
+constexpr int kF32UOff = 2 * 32768;            // slot offsets (bytes)
+constexpr int kF32GOff = kF32UOff + 4096;
+constexpr int kF32Buf = kF32GOff + 1024;       // 69 KiB
+
+__global__ __launch_bounds__(kCarryThreads) void carry_f32_kernel(
+    const uint8_t* inter, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
+    const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
+    float* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, int32_t single,
+    WindowArgs win) {
+  typedef float E;
+  constexpr int kSBuf = 4 * kWave * 8;   // one published state (fp32 fragments)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kF32Buf];
+  __shared__ __attribute__((aligned(16))) float sS[2 * kSBuf];
+  __shared__ __attribute__((aligned(16))) int32_t sTouch[kWave];
+
+  const int id = blockIdx.x;
+  const int pair = (id & 7) + 8 * ((id >> 3) / 8);
+  const int jt = (id >> 3) % 8;
+  if (pair >= n_seqs * H) return;
+  if (single ? (cu != nullptr && (cu[0] != 0 || (int64_t)cu[1] != T)) : status[0] != 0) return;
+  const int n = pair / H, h = pair % H;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
+  const int sb0 = single ? 0 : chunk_offset[n];
+  const int sb1 = single ? (int)((T + kC - 1) / kC) : chunk_offset[n + 1];
+  int b0, b1;
+  if (!win.part(sb0, sb1, b0, b1)) return;   // whole workgroup: no barrier reached
+  auto block_of = [&](int b) {
+    return inter + ((int64_t)(b - win.W0) * H + h) * Inter<E>::kBytes;
+  };
+  auto slot = [&](int b) { return lds + ((b - b0) & 1) * kF32Buf; };
+
+  if (w == 0) {
+    const int j = 16 * jt + (lane & 15);
+    floatx4 S[8];
+    Frag<E> fs[4];
+    const float* h0p = win.state_in(sb0, b0, h0, pair, h);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[mt][e] = h0p ? h0p[(16 * mt + 4 * g + e) * kD + j] : 0.f;
+    auto publish = [&](int b) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
+      float* dst = sS + ((b - b0) & 1) * kSBuf;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) store8(dst + (kb * kWave + lane) * 8, fs[kb]);
+    };
+    publish(b0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    ring_barrier();
+    for (int b = b0; b < b1; ++b) {
+      const uint8_t* sl = slot(b);
+      const float* XW = reinterpret_cast<const float*>(sl);
+      const float* KT = reinterpret_cast<const float*>(sl + 32768);
+      const float* UA = reinterpret_cast<const float*>(sl + kF32UOff);
+      const float* GC = reinterpret_cast<const float*>(sl + kF32GOff);
+      // the same products in the same order as the bf16 carry's carry_state
+      floatx4 X[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) X[mt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          Frag<E> a;
+          lds_frag(XW + ((mt * 4 + kb) * kWave + lane) * 8, a);
+          X[mt] = mma(X[mt], a, fs[kb]);
+        }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int mt = 2; mt < 4; ++mt) {
+          Frag<E> a;
+          lds_frag(XW + ((mt * 4 + kb) * kWave + lane) * 8, a);
+          X[mt] = mma(X[mt], a, fs[kb]);
+        }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const Frag16<E> u = ld16(UA + (mt * kWave + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[mt][e] += u.get(e);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) S[mt] *= *reinterpret_cast<const floatx4*>(GC + 16 * mt + 4 * g);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<E> fv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { fv.set(e, X[2 * kb][e]); fv.set(4 + e, X[2 * kb + 1][e]); }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          Frag<E> a;
+          lds_frag(KT + ((mt * 2 + kb) * kWave + lane) * 8, a);
+          S[mt] = mma(S[mt], a, fv);
+        }
+      }
+      publish(b + 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      ring_barrier();
+    }
+    if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
+    }
+  } else if (w == 1) {
+    // output wave
+    OutOps<E, 1> out;
+    if (b0 < b1) load_out_ops(out, reinterpret_cast<const E*>(block_of(b0)), jt, lane);
+    ring_barrier();
+    for (int b = b0; b < b1; ++b) {
+      Frag<E> fsb[4];
+      const float* src = sS + ((b - b0) & 1) * kSBuf;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) lds_frag(src + (kb * kWave + lane) * 8, fsb[kb]);
+      floatx4 X[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) X[nt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) X[nt] = mma(X[nt], fsb[kb], out.fq[nt][kb]);
+      Frag16<E> ob[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[nt][e] += out.ut[0][nt].get(e);
+        ob[nt] = frag16<E>(X[nt]);
+      }
+      // next chunk's operands first, then this chunk's stores
+      load_out_ops(out, reinterpret_cast<const E*>(block_of(min(b + 1, b1 - 1))), jt, lane);
+      const int64_t tok0 = seq_start + (int64_t)(b - sb0) * kC;
+      store_out<E>(ob, o, tok0, (int)min((int64_t)kC, seq_end - tok0), H, h, lane, 16 * jt);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      ring_barrier();
+    }
+  } else {
+    // loaders: chunk b + 1 into the other slot while chunk b is computed
+    constexpr int kLines = (int)((Inter<E>::kBytes + 127) / 128);
+    constexpr int kShare = (kLines + 7) / 8;
+    constexpr int kTouchOps = (kShare + kWave - 1) / kWave;
+    auto issue = [&](int b) {
+      const uint8_t* src = block_of(b);
+      uint8_t* dst = slot(b);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)src, 0, (int)Inter<E>::kBytes, 0x00020000);
+      if (w == 2) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)   // [-W]: the first half of [-W ; Qt]
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, lane * 16,
+              i * 1024, 0, 0);
+        const int uc = (int)(Inter<E>::kUC * sizeof(E)) + jt * 8 * kWave * 4 * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)    // U of this tile
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(dst + kF32UOff + i * 1024), 16,
+              lane * 16, uc + i * 1024, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(dst + 32768 + i * 1024), 16,
+              lane * 16, (int)(Inter<E>::kKT * sizeof(E)) + i * 1024, 0, 0);
+        // gamma_C: 512 bytes; lanes >= 32 read past the block and get zeros
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + kF32GOff), 16, lane * 16,
+            (int)Inter<E>::kGCByte, 0, 0);
+      }
+    };
+    auto touch = [&](int b) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)block_of(b), 0, (int)Inter<E>::kBytes, 0x00020000);
+#pragma unroll
+      for (int u = 0; u < kTouchOps; ++u) {
+        const int line = min(jt * kShare + u * kWave + lane, kLines - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)sTouch, 4, line * 128, 0, 0, 0);
+      }
+    };
+    if (b0 < b1) issue(b0);
+    if (w == 3 && b0 + 1 < b1) touch(b0 + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    ring_barrier();
+    for (int b = b0; b < b1; ++b) {
+      if (b + 1 < b1) issue(b + 1);
+      if (w == 3 && b + 2 < b1) touch(b + 2);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk b + 1 landed
       ring_barrier();
     }
   }
@@ -1368,7 +1562,7 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
       carry_kernel<bf16, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
           inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single, win);
     else
-      carry_kernel<float, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+      carry_f32_kernel<<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
           inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H, single, win);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
