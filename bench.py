@@ -115,6 +115,8 @@ def _parse():
                     help="time only this workload's prefill calls (counter runs)")
     ap.add_argument("--workload", default="bench_step",
                     help="workload name written by --summarize-pmc")
+    ap.add_argument("--calls", type=int, default=3,
+                    help="calls the summarised counter runs made (steps + warmup)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy first (counter scale factor)")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
@@ -138,10 +140,10 @@ def sources_hash() -> str:
 
 
 def _kernel_key(name):
-    """Bench-step kernel a counter row belongs to. The counter passes run with
-    --no-extensions, so the only recurrent-kernel dispatches are the decode
-    step's (profilers print these template names mangled or demangled, and
-    not always faithfully, so only the base name is matched)."""
+    """Kernel a counter row belongs to. The counter passes run with --only,
+    so the only recurrent-kernel dispatches are the decode step's
+    (profilers print these template names mangled or demangled, and not
+    always faithfully, so only the base name is matched)."""
     if "recurrent_fwd_kernel" in name:
         return "decode"
     for k in ("intra", "carry", "chunk_map"):
@@ -151,9 +153,11 @@ def _kernel_key(name):
     return "copy" if "copy" in name.lower() else None
 
 
-def _pmc_means(run_dir, counter):
-    """Mean counter value (KiB) per dispatch of each kernel in one pmc run;
-    for 'copy', the largest dispatch (the 1 GiB calibration copy)."""
+def _pmc_per_call(run_dir, counter, calls):
+    """Counter value (KiB) per call of each kernel in one pmc run: the sum
+    over the kernel's dispatches divided by the calls the run made (a
+    windowed prefill launches its kernels once per window); for 'copy', the
+    largest dispatch (the 1 GiB calibration copy)."""
     per = {}
     for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         for row in csv.DictReader(open(f)):
@@ -164,18 +168,23 @@ def _pmc_means(run_dir, counter):
                 continue
             per.setdefault(k, {}).setdefault(row["Dispatch_Id"], 0.0)
             per[k][row["Dispatch_Id"]] += float(row["Counter_Value"])
-    return {k: (max(v.values()) if k == "copy" else sum(v.values()) / len(v))
-            for k, v in per.items()}
+    out = {k: (max(v.values()) if k == "copy" else sum(v.values()) / calls)
+           for k, v in per.items()}
+    out["_dispatches"] = {k: len(v) for k, v in per.items()}
+    return out
 
 
-def summarize_pmc(fetch_dir, write_dir, workload):
-    f, w = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
+def summarize_pmc(fetch_dir, write_dir, workload, calls):
+    f = _pmc_per_call(fetch_dir, "FETCH_SIZE", calls)
+    w = _pmc_per_call(write_dir, "WRITE_SIZE", calls)
     fr = COPY_BYTES / (f["copy"] * 1024.0)
     wr = COPY_BYTES / (w["copy"] * 1024.0)
     lines = [f"workload = {workload}", f"sources_sha256 = {sources_hash()}",
-             f"copy_read_factor = {fr:.6f}", f"copy_write_factor = {wr:.6f}"]
+             f"calls = {calls}", f"copy_read_factor = {fr:.6f}",
+             f"copy_write_factor = {wr:.6f}"]
     for k in ("chunk_map", "intra", "carry", "decode"):
         if k in f and k in w:
+            lines.append(f"{k}_dispatches = {f['_dispatches'][k]}")
             lines.append(f"{k}_fetch_KiB = {f[k]:.1f}")
             lines.append(f"{k}_write_KiB = {w[k]:.1f}")
     print("\n".join(lines))
@@ -224,7 +233,7 @@ def summarize_mfma(run_dir, durations_us=None):
 
 
 def load_traffic(workload="bench_step"):
-    """Scaled HBM bytes per launch for each kernel of a workload, from the
+    """Scaled HBM bytes per call for each kernel of a workload, from the
     committed counter summary profiles/hbm_traffic_<workload>.txt, or {} if
     there is none or it was taken on other kernel sources."""
     path = PROFILES / f"hbm_traffic_{workload}.txt"
@@ -634,7 +643,7 @@ def only_workload(torch, d, name, steps, warmup):
 def main():
     args = _parse()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.workload)
+        summarize_pmc(*args.summarize_pmc, args.workload, args.calls)
         return
     if args.summarize_mfma:
         durs = dict((k, float(v)) for k, v in (x.split("=", 1) for x in args.durations or []))
