@@ -875,10 +875,11 @@ __device__ __forceinline__ void carry_out(const OutOps<E, kTiles>& p, int t,
   for (int nt = 0; nt < 4; ++nt) st16(sOb + (nt * kWave + lane) * 4, frag16<E>(X[nt]));
 }
 
-// Stores one chunk's O tile (16 columns) from LDS for the valid tokens.
-// Only the state waves issue global stores: they never wait on global loads,
-// so the stores' completion never stalls a load wait (on this architecture
-// one counter tracks both).
+// Stores one chunk's O tile (16 columns) for the valid tokens. A loader wave
+// issues these stores after its wait for the ring, so they have a whole
+// chunk to complete before its next wait (one counter tracks loads and
+// stores here); in the state wave, whose step sets the chunk's pace, the
+// four stores cost about a fifth of the step.
 template <class E>
 __device__ __forceinline__ void store_out(const Frag16<E> (&x)[4], E* __restrict__ o,
                                           int64_t tok0, int len, int H, int h, int lane, int j0) {
@@ -892,9 +893,10 @@ __device__ __forceinline__ void store_out(const Frag16<E> (&x)[4], E* __restrict
 
 // One workgroup per (sequence, head, group of kTiles column tiles).
 //   kTiles = 1: waves 0 state, 1 output, 2 and 3 loaders (2 moves [-W] and
-//               U, 3 moves K'^T and gamma_C and touches L2);
+//               U and stores O, 3 moves K'^T and gamma_C and touches L2);
 //   kTiles = 2: waves 0 and 1 state (one tile each, sharing the staged
-//               [-W] and K'^T), 2 output (both tiles), 3 the only loader.
+//               [-W] and K'^T), 2 output (both tiles), 3 the only loader
+//               (and stores O).
 // Two tiles per workgroup halve the L2 traffic per column tile at the cost
 // of a longer chain per chunk; they pay when there are more (sequence,
 // head) pairs than one round of one-tile workgroups fills.
@@ -1018,6 +1020,25 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     }
   };
 
+  // O of chunk b (all tiles of the group), written to LDS by the output wave
+  // in step b and visible after that step's barrier; stored by a loader
+  // after its ring wait in the next step (or after the last step).
+  auto store_o = [&](int b) {
+    const int64_t tok0 = seq_start + (int64_t)(b - sb0) * kC;
+    const int len = (int)min((int64_t)kC, seq_end - tok0);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const E* src = sO + (t * 2 + ((b - b0) & 1)) * kOBuf;
+      Frag16<E> x[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) x[nt] = ld16(src + (nt * kWave + lane) * 4);
+      store_out<E>(x, o, tok0, len, H, h, lane, 16 * (jg * kTiles + t));
+    }
+    // the reads are done before the barrier after which the output wave
+    // rewrites this buffer, also where no lane stores
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+  };
+
   // Each role runs its own loop; all execute two barriers before the first
   // chunk and one per chunk.
   if (w < kTiles) {
@@ -1025,7 +1046,6 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     const int jt = jg * kTiles + w;
     const int j = 16 * jt + (lane & 15);
     E* const sSw = sS + w * 2 * kSBuf;
-    const E* const sOw = sO + w * 2 * kOBuf;
     auto publish = [&](const Frag<E> (&fs)[4], int b) {
       E* dst = sSw + ((b - b0) & 1) * kSBuf;
 #pragma unroll
@@ -1061,20 +1081,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     // chunk b0's slot is read before the loaders reuse it for chunk b0 + 3
     __builtin_amdgcn_s_waitcnt(0xC07F);
     ring_barrier();
-    // O of chunk b, written to LDS by the output wave
-    auto read_out = [&](Frag16<E> (&x)[4], int b) {
-      const E* src = sOw + ((b - b0) & 1) * kOBuf;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) x[nt] = ld16(src + (nt * kWave + lane) * 4);
-    };
-    auto out_of = [&](const Frag16<E> (&x)[4], int b) {
-      const int64_t tok0 = seq_start + (int64_t)(b - sb0) * kC;
-      const int len = (int)min((int64_t)kC, seq_end - tok0);
-      store_out<E>(x, o, tok0, len, H, h, lane, 16 * jt);
-    };
     auto step = [&](int b, StateOps<E>& cur, StateOps<E>& nxt) {
-      Frag16<E> ob[4];
-      read_out(ob, b - 1);   // first, so its wait does not cover the prefetch
       fetch(nxt, min(b + 1, b1 - 1));
       carry_state<E>(S, fs, cur);
       // one prefetch read per product: a wave stalls once 16 LDS reads are
@@ -1084,7 +1091,6 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       }
-      if (b > b0) out_of(ob, b - 1);
       publish(fs, b + 1);
       __builtin_amdgcn_s_waitcnt(0xC07F);
       ring_barrier();
@@ -1097,11 +1103,6 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       step(b + 1, sb, sa);
     }
     if (b < b1) step(b, sa, sb);
-    if (b0 < b1) {
-      Frag16<E> ob[4];
-      read_out(ob, b1 - 1);
-      out_of(ob, b1 - 1);
-    }
     if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
@@ -1153,6 +1154,11 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       for (int b = b0 + 3; b < b0 + kTouchAhead && b < b1; ++b) touch(b);
     ring_barrier();
     ring_barrier();
+    // Wave 2 issues chunk b-1's O stores after its wait, so at its next wait
+    // they sit between two chunks' DMA. That wait allows only the newer
+    // chunk's DMA to stay outstanding, which holds whether or not stores
+    // retire in order with loads: loads retire in order among themselves,
+    // and the allowance leaves no room for a store.
     for (int b = b0; b < b1; ++b) {
       const bool dma = b + 3 < b1;
       const bool tch = w == 3 && b + kTouchAhead < b1;
@@ -1160,8 +1166,10 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       if (dma) issue(b + 3);
       if (tch) touch(b + kTouchAhead);
       loader_wait(dma, tch, prev);
+      if (w == 2 && b > b0) store_o(b - 1);
       ring_barrier();
     }
+    if (w == 2 && b0 < b1) store_o(b1 - 1);
   } else {
     // one loader, kDMAw = 37 transfers per chunk: at most one chunk's
     // transfers are in flight (the counter holds 63), so iteration b first
@@ -1184,8 +1192,12 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (b + 3 < b1) issue(b + 3);
       if (b + kTouchAhead < b1) touch(b + kTouchAhead);
+      // after the issues: the next wait allows only the touch, so these
+      // stores never let a DMA transfer count as landed
+      if (b > b0) store_o(b - 1);
       ring_barrier();
     }
+    if (b0 < b1) store_o(b1 - 1);
   }
 }
 
