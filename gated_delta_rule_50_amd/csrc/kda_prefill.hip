@@ -1204,23 +1204,30 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
 // ------------------------------------------------------- carry, fp32 I/O
 // The carry for fp32 intermediates (fp32 I/O). A chunk's state operands
 // take 69 KiB in fp32, so the ring has two slots and the loaders stay one
-// chunk ahead; fp32 products run at a sixteenth of the bf16 rate (eight
-// 16x16x4 products per fragment), so a chunk's 256 state products take
-// long enough to hide that lead. One workgroup per (sequence, head,
-// 16-column tile), four waves:
-//   wave 0  state wave: reads each operand fragment from the ring just
-//           before its products (the next one in flight), state in
-//           registers, publishes the state each chunk
-//   wave 1  output wave: O^T = Ut^T + S^T Qt^T with Qt and Ut held in
-//           registers one chunk ahead; it stores O itself, issuing the
-//           next chunk's loads first so that its load waits never include
-//           its stores
-//   waves 2, 3  loaders: [-W] and U; K'^T, gamma_C and the L2 touches
+// chunk ahead. fp32 products run at a sixteenth of the bf16 rate (eight
+// 16x16x4 products per fragment), so the chain is bound by the state
+// products: 256 per chunk and column tile, about 8 k cycles on one SIMD.
+// Two state waves on two SIMDs share them, with the same products in the
+// same order as one wave would issue (so the results do not depend on the
+// split). One workgroup per (sequence, head, 16-column tile), six waves:
+//   waves 0, 1  state: wave s computes the pseudo-value rows 32 s .. 32 s + 31
+//           (over all 128 state rows) and, after the two halves are swapped
+//           through LDS, updates the state rows 64 s .. 64 s + 63; each
+//           publishes its half of the new state, and both read the full
+//           state back for the next chunk
+//   waves 2, 3  output: O^T = Ut^T + S^T Qt^T for tokens 32 (w-2) .. +31, Qt
+//           and Ut held in registers one chunk ahead; each stores its O
+//           rows itself, issuing the next chunk's loads first so that its
+//           load waits never include its stores
+//   waves 4, 5  loaders: [-W] and U; K'^T, gamma_C and the L2 touches
+// Every wave executes one barrier before the first chunk and two per
+// chunk (the state waves swap pseudo-value halves between them).
 constexpr int kF32UOff = 2 * 32768;            // slot offsets (bytes)
 constexpr int kF32GOff = kF32UOff + 4096;
 constexpr int kF32Buf = kF32GOff + 1024;       // 69 KiB
+constexpr int kF32Threads = 6 * kWave;
 
-__global__ __launch_bounds__(kCarryThreads) void carry_f32_kernel(
+__global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     const uint8_t* inter, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
     const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
@@ -1228,8 +1235,10 @@ __global__ __launch_bounds__(kCarryThreads) void carry_f32_kernel(
     WindowArgs win) {
   typedef float E;
   constexpr int kSBuf = 4 * kWave * 8;   // one published state (fp32 fragments)
+  constexpr int kXBuf = 2 * kWave * 4;   // one half of the pseudo-value (two tiles)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kF32Buf];
   __shared__ __attribute__((aligned(16))) float sS[2 * kSBuf];
+  __shared__ __attribute__((aligned(16))) float sX[2 * kXBuf];
   __shared__ __attribute__((aligned(16))) int32_t sTouch[kWave];
 
   const int id = blockIdx.x;
@@ -1251,7 +1260,10 @@ __global__ __launch_bounds__(kCarryThreads) void carry_f32_kernel(
   };
   auto slot = [&](int b) { return lds + ((b - b0) & 1) * kF32Buf; };
 
-  if (w == 0) {
+  // the halves are template constants so that every register array index
+  // stays static
+  auto state_role = [&](auto hsc) {
+    constexpr int hs = decltype(hsc)::value;
     const int j = 16 * jt + (lane & 15);
     floatx4 S[8];
     Frag<E> fs[4];
@@ -1261,59 +1273,89 @@ __global__ __launch_bounds__(kCarryThreads) void carry_f32_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         S[mt][e] = h0p ? h0p[(16 * mt + 4 * g + e) * kD + j] : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
+    // fragments kb = 2 hs, 2 hs + 1 hold this wave's state rows
     auto publish = [&](int b) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
       float* dst = sS + ((b - b0) & 1) * kSBuf;
+      if (b == b0) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) store8(dst + (kb * kWave + lane) * 8, fs[kb]);
+        for (int kb = 0; kb < 4; ++kb)
+          if (kb >> 1 == hs) store8(dst + (kb * kWave + lane) * 8, fs[kb]);
+        return;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int kb = 2 * hs + q;
+        Frag<E> f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f.set(e, S[4 * hs + 2 * q][e]);
+          f.set(4 + e, S[4 * hs + 2 * q + 1][e]);
+        }
+        fs[kb] = f;
+        store8(dst + (kb * kWave + lane) * 8, f);
+      }
     };
     publish(b0);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
+      if (b > b0) {
+        // the other half of the state, published in the previous step
+        const float* src = sS + ((b - b0) & 1) * kSBuf;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          if (kb >> 1 != hs) lds_frag(src + (kb * kWave + lane) * 8, fs[kb]);
+      }
       const uint8_t* sl = slot(b);
       const float* XW = reinterpret_cast<const float*>(sl);
       const float* KT = reinterpret_cast<const float*>(sl + 32768);
       const float* UA = reinterpret_cast<const float*>(sl + kF32UOff);
       const float* GC = reinterpret_cast<const float*>(sl + kF32GOff);
-      // the same products in the same order as the bf16 carry's carry_state
+      // pseudo-value rows of this half: the same products in the same order
+      // as the bf16 carry's carry_state
       floatx4 X[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) X[mt] = zero4();
+      for (int q = 0; q < 2; ++q) {
+        const int mt = 2 * hs + q;
+        X[mt] = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int kb = 0; kb < 4; ++kb) {
           Frag<E> a;
           lds_frag(XW + ((mt * 4 + kb) * kWave + lane) * 8, a);
           X[mt] = mma(X[mt], a, fs[kb]);
         }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int mt = 2; mt < 4; ++mt) {
-          Frag<E> a;
-          lds_frag(XW + ((mt * 4 + kb) * kWave + lane) * 8, a);
-          X[mt] = mma(X[mt], a, fs[kb]);
-        }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
         const Frag16<E> u = ld16(UA + (mt * kWave + lane) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) X[mt][e] += u.get(e);
+        st16(sX + hs * kXBuf + (q * kWave + lane) * 4, frag16<E>(X[mt]));
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      ring_barrier();
+      // the other half of the pseudo-value
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) S[mt] *= *reinterpret_cast<const floatx4*>(GC + 16 * mt + 4 * g);
+      for (int q = 0; q < 2; ++q) {
+        const Frag16<E> x = ld16(sX + (1 - hs) * kXBuf + (q * kWave + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[2 * (1 - hs) + q][e] = x.get(e);
+      }
+      // this half of the state: rows 64 hs .. 64 hs + 63
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int mt = 4 * hs + q;
+        S[mt] *= *reinterpret_cast<const floatx4*>(GC + 16 * mt + 4 * g);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         Frag<E> fv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) { fv.set(e, X[2 * kb][e]); fv.set(4 + e, X[2 * kb + 1][e]); }
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
+        for (int q = 0; q < 4; ++q) {
+          const int mt = 4 * hs + q;
           Frag<E> a;
           lds_frag(KT + ((mt * 2 + kb) * kWave + lane) * 8, a);
           S[mt] = mma(S[mt], a, fv);
@@ -1325,38 +1367,66 @@ __global__ __launch_bounds__(kCarryThreads) void carry_f32_kernel(
     }
     if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int q = 0; q < 4; ++q) {
+        const int mt = 4 * hs + q;
 #pragma unroll
         for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
+      }
     }
+  };
+  if (w == 0) {
+    state_role(std::integral_constant<int, 0>{});
   } else if (w == 1) {
-    // output wave
-    OutOps<E, 1> out;
-    if (b0 < b1) load_out_ops(out, reinterpret_cast<const E*>(block_of(b0)), jt, lane);
+    state_role(std::integral_constant<int, 1>{});
+  } else if (w < 4) {
+    // output wave for tokens 32 ho .. 32 ho + 31 (tiles nt = 2 ho, 2 ho + 1)
+    const int ho = w - 2;
+    Frag<E> fq[2][4];
+    Frag16<E> ut[2];
+    auto load_ops = [&](int b) {
+      const E* blk = reinterpret_cast<const E*>(block_of(b));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int nt = 2 * ho + q;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          load_frag(blk + Inter<E>::kXA + ((4 + nt) * 4 + kb) * kWave * 8, lane, fq[q][kb]);
+        ut[q] = ld16(blk + Inter<E>::kUC + ((jt * 8 + 4 + nt) * kWave + lane) * 4);
+      }
+    };
+    if (b0 < b1) load_ops(b0);
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
       Frag<E> fsb[4];
       const float* src = sS + ((b - b0) & 1) * kSBuf;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) lds_frag(src + (kb * kWave + lane) * 8, fsb[kb]);
-      floatx4 X[4];
+      floatx4 X[2];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) X[nt] = zero4();
+      for (int q = 0; q < 2; ++q) X[q] = zero4();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) X[nt] = mma(X[nt], fsb[kb], out.fq[nt][kb]);
-      Frag16<E> ob[4];
+        for (int q = 0; q < 2; ++q) X[q] = mma(X[q], fsb[kb], fq[q][kb]);
+      Frag16<E> ob[2];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int q = 0; q < 2; ++q) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[nt][e] += out.ut[0][nt].get(e);
-        ob[nt] = frag16<E>(X[nt]);
+        for (int e = 0; e < 4; ++e) X[q][e] += ut[q].get(e);
+        ob[q] = frag16<E>(X[q]);
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      ring_barrier();   // the state waves' pseudo-value swap
       // next chunk's operands first, then this chunk's stores
-      load_out_ops(out, reinterpret_cast<const E*>(block_of(min(b + 1, b1 - 1))), jt, lane);
+      load_ops(min(b + 1, b1 - 1));
       const int64_t tok0 = seq_start + (int64_t)(b - sb0) * kC;
-      store_out<E>(ob, o, tok0, (int)min((int64_t)kC, seq_end - tok0), H, h, lane, 16 * jt);
+      const int len = (int)min((int64_t)kC, seq_end - tok0);
+      E* const base = o + ((tok0 + (lane & 15)) * H + h) * kD + 16 * jt + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int nt = 2 * ho + q;
+        if (16 * nt + (lane & 15) < len) st16(base + (int64_t)16 * nt * H * kD, ob[q]);
+      }
       __builtin_amdgcn_s_waitcnt(0xC07F);
       ring_barrier();
     }
@@ -1370,7 +1440,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_f32_kernel(
       uint8_t* dst = slot(b);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)src, 0, (int)Inter<E>::kBytes, 0x00020000);
-      if (w == 2) {
+      if (w == 4) {
 #pragma unroll
         for (int i = 0; i < 32; ++i)   // [-W]: the first half of [-W ; Qt]
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1405,13 +1475,14 @@ __global__ __launch_bounds__(kCarryThreads) void carry_f32_kernel(
       }
     };
     if (b0 < b1) issue(b0);
-    if (w == 3 && b0 + 1 < b1) touch(b0 + 1);
+    if (w == 5 && b0 + 1 < b1) touch(b0 + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
       if (b + 1 < b1) issue(b + 1);
-      if (w == 3 && b + 2 < b1) touch(b + 2);
+      if (w == 5 && b + 2 < b1) touch(b + 2);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk b + 1 landed
+      ring_barrier();   // the state waves' pseudo-value swap
       ring_barrier();
     }
   }
@@ -1574,7 +1645,7 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
       carry_kernel<bf16, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
           inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single, win);
     else
-      carry_f32_kernel<<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+      carry_f32_kernel<<<(unsigned)nblocks, kF32Threads, 0, stream>>>(
           inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H, single, win);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
