@@ -725,7 +725,8 @@ struct WindowArgs {
 //   state wave    X = U + [-W] S            pseudo-value (rows = token)
 //                 S = Diag(gamma_C) S + K'^T X
 //   output wave   O^T = Ut^T + S^T Qt^T     (rows = value column)
-//   loader waves  stream the state wave's operands into an LDS ring
+//   loader waves  stream the state wave's operands into an LDS ring; one
+//                 of them also stores the output wave's O tiles
 // Wave 3 (a loader) also touches one word per 128-byte line of this
 // workgroup's share of the block six chunks ahead (an eighth, or a quarter
 // with two tiles; buffer->LDS loads into a scratch slot, no registers), so
@@ -852,8 +853,8 @@ __device__ __forceinline__ void load_out_ops(OutOps<E, kTiles>& p, const E* blk,
 
 // Output wave, one chunk and column tile t: O^T = Ut^T + S^T Qt^T; lane
 // (i = 16 nt + r, j = j0 + 4 g .. +3) holds four consecutive outputs of one
-// token. They go to LDS in the I/O type; the tile's state wave stores them
-// to global memory.
+// token. They go to LDS in the I/O type; a loader wave stores them to
+// global memory in the next chunk.
 template <class E, int kTiles>
 __device__ __forceinline__ void carry_out(const OutOps<E, kTiles>& p, int t,
                                           const Frag<E> (&fs)[4], E* sOb, int lane) {
