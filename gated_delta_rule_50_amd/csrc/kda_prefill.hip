@@ -1206,27 +1206,29 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
 // The carry for fp32 intermediates (fp32 I/O). A chunk's state operands
 // take 69 KiB in fp32, so the ring has two slots and the loaders stay one
 // chunk ahead. fp32 products run at a sixteenth of the bf16 rate (eight
-// 16x16x4 products per fragment), so the chain is bound by the state
-// products: 256 per chunk and column tile, about 8 k cycles on one SIMD.
-// Two state waves on two SIMDs share them, with the same products in the
-// same order as one wave would issue (so the results do not depend on the
-// split). One workgroup per (sequence, head, 16-column tile), six waves:
-//   waves 0, 1  state: wave s computes the pseudo-value rows 32 s .. 32 s + 31
-//           (over all 128 state rows) and, after the two halves are swapped
-//           through LDS, updates the state rows 64 s .. 64 s + 63; each
-//           publishes its half of the new state, and both read the full
-//           state back for the next chunk
-//   waves 2, 3  output: O^T = Ut^T + S^T Qt^T for tokens 32 (w-2) .. +31, Qt
-//           and Ut held in registers one chunk ahead; each stores its O
+// 16x16x4 products per fragment), so the chain is bound by the products:
+// 256 per chunk for the state and 128 for the output of one column tile,
+// about 12 k cycles on one SIMD. They are spread over four state and four
+// output waves, with the same products in the same order per tile as one
+// wave would issue (so the results do not depend on the split). One
+// workgroup per (sequence, head, 16-column tile), ten waves:
+//   waves 0 .. 3  state: wave s computes the pseudo-value rows 16 s .. +15
+//           (over all 128 state rows), the rows are swapped through LDS at a
+//           second barrier per chunk, and wave s updates the state rows
+//           32 s .. 32 s + 31 and publishes them; each reads the others'
+//           rows back for the next chunk
+//   waves 4 .. 7  output: O^T = Ut^T + S^T Qt^T for tokens 16 (w-4) .. +15,
+//           Qt and Ut held in registers one chunk ahead; each stores its O
 //           rows itself, issuing the next chunk's loads first so that its
 //           load waits never include its stores
-//   waves 4, 5  loaders: [-W] and U; K'^T, gamma_C and the L2 touches
+//   waves 8, 9  loaders: [-W] and U; K'^T, gamma_C and the L2 touches
 // Every wave executes one barrier before the first chunk and two per
-// chunk (the state waves swap pseudo-value halves between them).
+// chunk (the state waves swap pseudo-value rows between them).
 constexpr int kF32UOff = 2 * 32768;            // slot offsets (bytes)
 constexpr int kF32GOff = kF32UOff + 4096;
 constexpr int kF32Buf = kF32GOff + 1024;       // 69 KiB
-constexpr int kF32Threads = 6 * kWave;
+constexpr int kF32States = 4;                  // state waves (and output waves)
+constexpr int kF32Threads = (2 * kF32States + 2) * kWave;
 
 __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     const uint8_t* inter, const int32_t* __restrict__ cu,
@@ -1235,11 +1237,16 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     float* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, int32_t single,
     WindowArgs win) {
   typedef float E;
+  constexpr int kNS = kF32States;
+  constexpr int kXT = 4 / kNS;           // pseudo-value tiles per state wave
+  constexpr int kST = 8 / kNS;           // state row tiles per state wave
+  constexpr int kSF = 4 / kNS;           // state fragments per state wave
+  static_assert(kNS == 2 || kNS == 4, "two or four state waves");
   constexpr int kSBuf = 4 * kWave * 8;   // one published state (fp32 fragments)
-  constexpr int kXBuf = 2 * kWave * 4;   // one half of the pseudo-value (two tiles)
+  constexpr int kXBuf = kWave * 4;       // one pseudo-value tile
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kF32Buf];
   __shared__ __attribute__((aligned(16))) float sS[2 * kSBuf];
-  __shared__ __attribute__((aligned(16))) float sX[2 * kXBuf];
+  __shared__ __attribute__((aligned(16))) float sX[4 * kXBuf];
   __shared__ __attribute__((aligned(16))) int32_t sTouch[kWave];
 
   const int id = blockIdx.x;
@@ -1261,8 +1268,8 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
   };
   auto slot = [&](int b) { return lds + ((b - b0) & 1) * kF32Buf; };
 
-  // the halves are template constants so that every register array index
-  // stays static
+  // the state wave index is a template constant so that every register
+  // array index stays static
   auto state_role = [&](auto hsc) {
     constexpr int hs = decltype(hsc)::value;
     const int j = 16 * jt + (lane & 15);
@@ -1278,26 +1285,20 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
-    // fragments kb = 2 hs, 2 hs + 1 hold this wave's state rows
+    // fragments kb = kSF hs .. kSF hs + kSF - 1 hold this wave's state rows
     auto publish = [&](int b) {
       float* dst = sS + ((b - b0) & 1) * kSBuf;
-      if (b == b0) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          if (kb >> 1 == hs) store8(dst + (kb * kWave + lane) * 8, fs[kb]);
-        return;
-      }
+      for (int q = 0; q < kSF; ++q) {
+        const int kb = kSF * hs + q;
+        if (b > b0) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int kb = 2 * hs + q;
-        Frag<E> f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f.set(e, S[4 * hs + 2 * q][e]);
-          f.set(4 + e, S[4 * hs + 2 * q + 1][e]);
+          for (int e = 0; e < 4; ++e) {
+            fs[kb].set(e, S[2 * kb][e]);
+            fs[kb].set(4 + e, S[2 * kb + 1][e]);
+          }
         }
-        fs[kb] = f;
-        store8(dst + (kb * kWave + lane) * 8, f);
+        store8(dst + (kb * kWave + lane) * 8, fs[kb]);
       }
     };
     publish(b0);
@@ -1305,23 +1306,23 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
       if (b > b0) {
-        // the other half of the state, published in the previous step
+        // the other waves' state rows, published in the previous step
         const float* src = sS + ((b - b0) & 1) * kSBuf;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          if (kb >> 1 != hs) lds_frag(src + (kb * kWave + lane) * 8, fs[kb]);
+          if (kb / kSF != hs) lds_frag(src + (kb * kWave + lane) * 8, fs[kb]);
       }
       const uint8_t* sl = slot(b);
       const float* XW = reinterpret_cast<const float*>(sl);
       const float* KT = reinterpret_cast<const float*>(sl + 32768);
       const float* UA = reinterpret_cast<const float*>(sl + kF32UOff);
       const float* GC = reinterpret_cast<const float*>(sl + kF32GOff);
-      // pseudo-value rows of this half: the same products in the same order
+      // this wave's pseudo-value rows: the same products in the same order
       // as the bf16 carry's carry_state
       floatx4 X[4];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int mt = 2 * hs + q;
+      for (int q = 0; q < kXT; ++q) {
+        const int mt = kXT * hs + q;
         X[mt] = zero4();
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -1332,21 +1333,22 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
         const Frag16<E> u = ld16(UA + (mt * kWave + lane) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) X[mt][e] += u.get(e);
-        st16(sX + hs * kXBuf + (q * kWave + lane) * 4, frag16<E>(X[mt]));
+        st16(sX + (mt * kWave + lane) * 4, frag16<E>(X[mt]));
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);
       ring_barrier();
-      // the other half of the pseudo-value
+      // the other waves' pseudo-value rows
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const Frag16<E> x = ld16(sX + (1 - hs) * kXBuf + (q * kWave + lane) * 4);
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt / kXT == hs) continue;
+        const Frag16<E> x = ld16(sX + (mt * kWave + lane) * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[2 * (1 - hs) + q][e] = x.get(e);
+        for (int e = 0; e < 4; ++e) X[mt][e] = x.get(e);
       }
-      // this half of the state: rows 64 hs .. 64 hs + 63
+      // this wave's state rows
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int mt = 4 * hs + q;
+      for (int q = 0; q < kST; ++q) {
+        const int mt = kST * hs + q;
         S[mt] *= *reinterpret_cast<const floatx4*>(GC + 16 * mt + 4 * g);
       }
 #pragma unroll
@@ -1355,8 +1357,8 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) { fv.set(e, X[2 * kb][e]); fv.set(4 + e, X[2 * kb + 1][e]); }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int mt = 4 * hs + q;
+        for (int q = 0; q < kST; ++q) {
+          const int mt = kST * hs + q;
           Frag<E> a;
           lds_frag(KT + ((mt * 2 + kb) * kWave + lane) * 8, a);
           S[mt] = mma(S[mt], a, fv);
@@ -1368,27 +1370,22 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     }
     if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int mt = 4 * hs + q;
+      for (int q = 0; q < kST; ++q) {
+        const int mt = kST * hs + q;
 #pragma unroll
         for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
       }
     }
   };
-  if (w == 0) {
-    state_role(std::integral_constant<int, 0>{});
-  } else if (w == 1) {
-    state_role(std::integral_constant<int, 1>{});
-  } else if (w < 4) {
-    // output wave for tokens 32 ho .. 32 ho + 31 (tiles nt = 2 ho, 2 ho + 1)
-    const int ho = w - 2;
-    Frag<E> fq[2][4];
-    Frag16<E> ut[2];
+  // output wave ho: O tiles nt = kXT ho .. kXT ho + kXT - 1
+  auto output_role = [&](int ho) {
+    Frag<E> fq[kXT][4];
+    Frag16<E> ut[kXT];
     auto load_ops = [&](int b) {
       const E* blk = reinterpret_cast<const E*>(block_of(b));
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int nt = 2 * ho + q;
+      for (int q = 0; q < kXT; ++q) {
+        const int nt = kXT * ho + q;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
           load_frag(blk + Inter<E>::kXA + ((4 + nt) * 4 + kb) * kWave * 8, lane, fq[q][kb]);
@@ -1402,16 +1399,16 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
       const float* src = sS + ((b - b0) & 1) * kSBuf;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) lds_frag(src + (kb * kWave + lane) * 8, fsb[kb]);
-      floatx4 X[2];
+      floatx4 X[kXT];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) X[q] = zero4();
+      for (int q = 0; q < kXT; ++q) X[q] = zero4();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) X[q] = mma(X[q], fsb[kb], fq[q][kb]);
-      Frag16<E> ob[2];
+        for (int q = 0; q < kXT; ++q) X[q] = mma(X[q], fsb[kb], fq[q][kb]);
+      Frag16<E> ob[kXT];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kXT; ++q) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) X[q][e] += ut[q].get(e);
         ob[q] = frag16<E>(X[q]);
@@ -1424,13 +1421,24 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
       const int len = (int)min((int64_t)kC, seq_end - tok0);
       E* const base = o + ((tok0 + (lane & 15)) * H + h) * kD + 16 * jt + 4 * g;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int nt = 2 * ho + q;
+      for (int q = 0; q < kXT; ++q) {
+        const int nt = kXT * ho + q;
         if (16 * nt + (lane & 15) < len) st16(base + (int64_t)16 * nt * H * kD, ob[q]);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);
       ring_barrier();
     }
+  };
+  const int wl = w - 2 * kNS;   // loader index
+  if (w < kNS) {
+    switch (w) {
+      case 0: state_role(std::integral_constant<int, 0>{}); break;
+      case 1: state_role(std::integral_constant<int, 1>{}); break;
+      case 2: if constexpr (kNS > 2) state_role(std::integral_constant<int, 2 % kNS>{}); break;
+      default: if constexpr (kNS > 3) state_role(std::integral_constant<int, 3 % kNS>{}); break;
+    }
+  } else if (w < 2 * kNS) {
+    output_role(w - kNS);
   } else {
     // loaders: chunk b + 1 into the other slot while chunk b is computed
     constexpr int kLines = (int)((Inter<E>::kBytes + 127) / 128);
@@ -1441,7 +1449,7 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
       uint8_t* dst = slot(b);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)src, 0, (int)Inter<E>::kBytes, 0x00020000);
-      if (w == 4) {
+      if (wl == 0) {
 #pragma unroll
         for (int i = 0; i < 32; ++i)   // [-W]: the first half of [-W ; Qt]
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1476,12 +1484,12 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
       }
     };
     if (b0 < b1) issue(b0);
-    if (w == 5 && b0 + 1 < b1) touch(b0 + 1);
+    if (wl == 1 && b0 + 1 < b1) touch(b0 + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
       if (b + 1 < b1) issue(b + 1);
-      if (w == 5 && b + 2 < b1) touch(b + 2);
+      if (wl == 1 && b + 2 < b1) touch(b + 2);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk b + 1 landed
       ring_barrier();   // the state waves' pseudo-value swap
       ring_barrier();
