@@ -457,7 +457,7 @@ def extensions(torch, d, pre_args, steps, warmup, extra=None, us_8k=None):
             "tflops": tf, "roofline": roof}
         if L == 64:
             # the same batch through the chunked path (its short-sequence
-            # carry): from 48 tokens per sequence on the faster of the two
+            # carry): from 40 tokens per sequence on the faster of the two
             pre = Prefill(*ins, d(p.h0), d(p.cu_seqlens, torch.int32))
             us = _time_calls(torch, pre.run, steps, warmup)
             out["chunked_L64"] = {

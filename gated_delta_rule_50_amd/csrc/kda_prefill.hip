@@ -1498,34 +1498,48 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
 }
 
 // ------------------------------------------------- carry for short sequences
-// One wave per (sequence, head, 16-column tile) and no staging: for batches
-// of short sequences, where the pipelined carry above pays its fixed cost
-// (state load, ring fill and drain in a workgroup that fills a CU) for one
-// or two chunks. Here every wave loads its operands straight from the
-// intermediate block (the eight tile waves of a block share an XCD, so the
-// block comes from HBM once) and several waves share each SIMD, so the
-// latency of one wave's loads hides behind the others. Same arithmetic per
-// chunk as the pipelined carry (O = Ut + Qt S from the state at the chunk
-// start, then the state update), so the results are bit-identical to it.
+// One workgroup of eight waves per (sequence, head), for batches of short
+// sequences, where the pipelined carry pays its fixed cost (state load, ring
+// fill and drain in a workgroup that fills a CU) for one or two chunks. Per
+// chunk the eight waves stage the operands all column tiles share ([-W ; Qt]
+// and K'^T, 48 KiB, and gamma_C) in LDS with buffer->LDS transfers, a
+// seventh of them each; wave t loads column tile t's state and its U and
+// Ut^T rows itself and computes the tile with the same products in the same
+// order as the pipelined carry (O = Ut + Qt S from the state at the chunk
+// start, then the state update), reading each fragment from LDS just before
+// its product, so the results are bit-identical to it. Each block is read
+// from memory once per chunk (the one-wave-per-tile form read its shared
+// part eight times through the CUs' memory pipelines), and at most 128
+// registers and 50 KiB of LDS let two or three workgroups share a CU.
+constexpr int kShortThreads = 8 * kWave;
+constexpr int kShortShared = kStageW * 2 + kStageKT;   // [-W ; Qt] and K'^T bytes
+constexpr int kShortXfers = kShortShared / 1024 + 1;   // and gamma_C
+
 template <class E>
-__global__ __launch_bounds__(kWave) void carry_short_kernel(
+__global__ __launch_bounds__(kShortThreads, 2) void carry_short_kernel(
     const uint8_t* __restrict__ inter, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
     const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
     E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, WindowArgs win) {
-  // the eight tiles of a (sequence, head) get ids with the same id % 8 (one XCD)
-  const int id = blockIdx.x;
-  const int pair = (id & 7) + 8 * ((id >> 3) / 8);
-  const int jt = (id >> 3) % 8;
+  static_assert(sizeof(E) == 2, "bf16 intermediates");
+  static_assert(Inter<E>::kXA == 0 && Inter<E>::kKT * sizeof(E) == kStageW * 2,
+                "[-W ; Qt] and K'^T open the block, in this order");
+  __shared__ __attribute__((aligned(1024))) uint8_t sm[kShortShared + 1024];
+  const E* const sXA = reinterpret_cast<const E*>(sm);
+  const E* const sKT = reinterpret_cast<const E*>(sm + kStageW * 2);
+  const float* const sGC = reinterpret_cast<const float*>(sm + kShortShared);
+
+  const int pair = blockIdx.x;
   if (pair >= n_seqs * H || status[0] != 0) return;
   const int n = pair / H, h = pair % H;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int jt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // column tile
   const int g = lane >> 4;
   const int j = 16 * jt + (lane & 15);
   const int64_t seq_start = cu ? cu[n] : 0, seq_end = cu ? cu[n + 1] : T;
   const int sb0 = chunk_offset[n], sb1 = chunk_offset[n + 1];
   int b0, b1;
-  if (!win.part(sb0, sb1, b0, b1)) return;
+  if (!win.part(sb0, sb1, b0, b1)) return;   // whole workgroup: no barrier reached
 
   floatx4 S[8];
   Frag<E> fs[4];
@@ -1540,34 +1554,102 @@ __global__ __launch_bounds__(kWave) void carry_short_kernel(
     for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
 
   for (int b = b0; b < b1; ++b) {
-    const E* blk =
-        reinterpret_cast<const E*>(inter + ((int64_t)(b - win.W0) * H + h) * Inter<E>::kBytes);
-    // O^T = Ut^T + S^T Qt^T from the state at the chunk start
-    OutOps<E, 1> po;
-    load_out_ops<E, 1>(po, blk, jt, lane);
+    const uint8_t* blk8 = inter + ((int64_t)(b - win.W0) * H + h) * Inter<E>::kBytes;
+    const E* blk = reinterpret_cast<const E*>(blk8);
+    {
+      // transfers x = jt, jt + 8, ...: 1 KiB pieces of [-W ; Qt] and K'^T,
+      // then gamma_C (512 bytes; lanes >= 32 read past the block and get
+      // zeros)
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)blk8, 0, (int)Inter<E>::kBytes, 0x00020000);
+      for (int x = jt; x < kShortXfers; x += 8) {
+        const int so = x < kShortXfers - 1 ? x * 1024 : (int)Inter<E>::kGCByte;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(sm + x * 1024), 16, lane * 16, so, 0,
+            0);
+      }
+    }
+    // this tile's U and Ut^T rows
+    Frag16<E> u[4], ut[4];
+    const E* UA = blk + Inter<E>::kUC + jt * 8 * kWave * 4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      u[mt] = ld16(UA + (mt * kWave + lane) * 4);
+      ut[mt] = ld16(UA + ((4 + mt) * kWave + lane) * 4);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    // O^T = Ut^T + S^T Qt^T from the state at the chunk start (the
+    // pipelined carry's carry_out, with Qt from LDS)
     floatx4 X[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) X[nt] = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) X[nt] = mma(X[nt], fs[kb], po.fq[nt][kb]);
+      for (int nt = 0; nt < 4; ++nt) {
+        Frag<E> fq;
+        load_frag(sXA + ((4 + nt) * 4 + kb) * kWave * 8, lane, fq);
+        X[nt] = mma(X[nt], fs[kb], fq);
+      }
     Frag16<E> ob[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X[nt][e] += po.ut[0][nt].get(e);
+      for (int e = 0; e < 4; ++e) X[nt][e] += ut[nt].get(e);
       ob[nt] = frag16<E>(X[nt]);
     }
-    StateOps<E> ps;
-    load_state_ops(ps, blk + Inter<E>::kXA, blk + Inter<E>::kKT,
-                   blk + Inter<E>::kUC + jt * 8 * kWave * 4,
-                   reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(blk) +
-                                                  Inter<E>::kGCByte),
-                   lane);
-    carry_state<E>(S, fs, ps);
+    // S <- Diag(gamma) S + K'^T (U + [-W] S) (the pipelined carry's
+    // carry_state, with the fragments from LDS)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) X[mt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        Frag<E> fw;
+        load_frag(sXA + (mt * 4 + kb) * kWave * 8, lane, fw);
+        X[mt] = mma(X[mt], fw, fs[kb]);
+      }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int mt = 2; mt < 4; ++mt) {
+        Frag<E> fw;
+        load_frag(sXA + (mt * 4 + kb) * kWave * 8, lane, fw);
+        X[mt] = mma(X[mt], fw, fs[kb]);
+      }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[mt][e] += u[mt].get(e);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      S[mt] *= *reinterpret_cast<const floatx4*>(sGC + 16 * mt + 4 * g);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<E> fv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { fv.set(e, X[2 * kb][e]); fv.set(4 + e, X[2 * kb + 1][e]); }
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        Frag<E> fk;
+        load_frag(sKT + (mt * 2 + kb) * kWave * 8, lane, fk);
+        S[mt] = mma(S[mt], fk, fv);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { fs[kb].set(e, S[2 * kb][e]); fs[kb].set(4 + e, S[2 * kb + 1][e]); }
     const int64_t tok0 = seq_start + (int64_t)(b - sb0) * kC;
     store_out<E>(ob, o, tok0, (int)min((int64_t)kC, seq_end - tok0), H, h, lane, 16 * jt);
+    // every wave has read this chunk's operands before the next transfers
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
   if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
 #pragma unroll
@@ -1611,13 +1693,17 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
   // 1.28 us per chunk on the 8K workload).
   const bool two = bf16_io && pairs * 8 > kCarryRound;
   const int64_t nblocks = ((pairs + 7) / 8) * 8 * (two ? 4 : 8);   // column-tile groups
-  // batches of short sequences (mean length up to two chunks): one wave per
-  // tile, no pipeline (the single-sequence call always pipelines). Measured
-  // crossover: the short carry wins up to 128 tokens per sequence, ties at
-  // 256 and loses at 512.
-  constexpr int64_t kShortMeanTokens = 2 * kC;
+  // batches of short sequences: one workgroup per pair, no pipeline (the
+  // single-sequence call always pipelines). It runs a sequence's chunks one
+  // after another at about 3.5 us each where the pipelined carry takes about
+  // 1 us, but reads each block once and packs two workgroups per CU. Measured
+  // at 32 heads (whole call): 256 x 64 tokens 817 -> 706 us, 32 x 256
+  // 347 -> 278 us, 16 x 512 307 -> 261 us, 8 x 2048 589 -> 558 us; with few
+  // pairs or long sequences it loses (4 x 2048 277 -> 338 us, 2 x 4096
+  // 271 -> 463 us). The choice sees only the mean length: a batch that mixes
+  // one long sequence with many short ones runs the long one unpipelined.
   const bool short_seqs = bf16_io && !single && n_seqs > 0 &&
-                          T <= kShortMeanTokens * n_seqs;
+                          (T <= 2 * kC * n_seqs || (T <= 4 * kC * n_seqs && pairs >= kCarryRound));
   const int64_t n_windows = n_slots > 0 ? (n_slots + win_slots - 1) / win_slots : 1;
   const int64_t state_floats = (int64_t)H * kD * kD;
   for (int64_t w = 0; w < n_windows; ++w) {
@@ -1645,7 +1731,7 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
     win.resume = state_area + ((w + 1) & 1) * state_floats;
     win.suspend = state_area + (w & 1) * state_floats;
     if (short_seqs)
-      carry_short_kernel<bf16><<<(unsigned)(((pairs + 7) / 8) * 64), kWave, 0, stream>>>(
+      carry_short_kernel<bf16><<<(unsigned)pairs, kShortThreads, 0, stream>>>(
           inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, win);
     else if (two)
       carry_kernel<bf16, 2><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(

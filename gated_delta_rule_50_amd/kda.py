@@ -406,10 +406,13 @@ def check_inputs(q, k, v, log_alpha, beta, cu_seqlens=None, *, flags=None, strea
 
 
 # Longest sequence routed to the recurrent kernel. The pages' serving notes
-# switch at 64 new tokens; on MI355X the two paths cost the same at 48 (256
-# or 64 sequences x 32 heads, fp32 states) and the chunked one is 12-23 %
-# faster from 56 to 64, so the switch sits at the measured crossover.
-RECURRENT_MAX_LEN = 48
+# switch at 64 new tokens; on MI355X (32 heads, fp32 states, whole calls) the
+# chunked path with its short-sequence carry is faster from 40 tokens on for
+# 64 and 256 sequences (L = 40: 177 against 186 us and 671 against 706 us)
+# and from 32 on for 16 sequences, and the recurrent one up to 32 for 64 and
+# 256 sequences (154 against 170 us, 597 against 639 us), so the switch sits
+# at 32.
+RECURRENT_MAX_LEN = 32
 
 
 def forward(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, max_seqlen, n_seqs=None,
