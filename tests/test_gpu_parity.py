@@ -252,6 +252,42 @@ def test_short_sequence_carry_equals_pipelined_bitwise():
         assert np.array_equal(host(on), o[s:e]) and np.array_equal(host(hn)[0], hf[n]), n
 
 
+def _short_many_pairs_batch(seed):
+    """At least 256 (sequence, head) pairs with a mean length between two and
+    four chunks: the short-sequence carry's second case."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(100, 330, size=60)] + [0, 1, 64, 256]
+    p = workloads.make_prefill(lengths, H=4, seed=seed, io="bf16", h0_std=0.05)
+    assert 128 * p.N < p.T <= 256 * p.N and p.N * p.H >= 256
+    return p
+
+
+def test_short_carry_many_pairs_matches_oracle():
+    p = _short_many_pairs_batch(67)
+    o, hf = _run_prefill(p)
+    _check_prefill(p, o, hf)
+    rh = recurrent.forward(p.q, p.k, p.v, p.log_alpha, p.beta, p.h0, p.cu_seqlens)[1]
+    for n in range(p.N):
+        assert rel_fro_err(hf[n], rh[n]) <= TOL[p.io][1], n
+
+
+def test_short_carry_many_pairs_equals_pipelined_bitwise():
+    """Sequences of the many-pair batch run alone (pipelined carry) give the
+    same bits as inside the batch (short-sequence carry)."""
+    p = _short_many_pairs_batch(68)
+    o, hf = _run_prefill(p)
+    bf = torch.bfloat16
+    cu = p.cu_seqlens
+    for n in list(range(0, p.N, 7)) + [p.N - 3, p.N - 2, p.N - 1]:
+        s, e = int(cu[n]), int(cu[n + 1])
+        if e == s:
+            continue
+        on, hn = kda.chunk_fwd(dev(p.q[s:e], bf), dev(p.k[s:e], bf), dev(p.v[s:e], bf),
+                               dev(p.log_alpha[s:e]), dev(p.beta[s:e]), dev(p.h0[n:n + 1]))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(on), o[s:e]) and np.array_equal(host(hn)[0], hf[n]), n
+
+
 def test_two_tile_carry_matches_oracle():
     p = _many_pairs_batch(60)
     assert p.N * p.H * 8 > 256
