@@ -230,7 +230,7 @@ __device__ __forceinline__ void exact_diag_block(const E* __restrict__ k_row,
 }
 
 template <class E, bool kNorm>
-__global__ __launch_bounds__(kIntraThreads) void intra_kernel(
+__global__ __launch_bounds__(kIntraThreads, sizeof(E) == 4 ? 2 : 1) void intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int32_t* chunk_offset, int32_t* status, int32_t n_seqs,
@@ -244,17 +244,19 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   //                     channels) and beta V (8-15, value columns), each
   //                     replaced by W / U once solved
   //                sNL  -L_IJ (J < I) A-operand tiles [I][J]; sTI Ti_II^T tiles
-  //   sB           beta (both phases)
+  //                sB beta (read up to step 3, before the tiles phase
+  //                overwrites the region)
   constexpr int kTile = kWave * 4;                        // elements per tile
   constexpr int kRowsBytes = 4 * 4 * kWave * 8 * (int)sizeof(E) + (5 + 3) * 4 * kD * 4;
   constexpr int kTilesBytes = (4 * 16 + 12 + 4) * kTile * (int)sizeof(E);
   // exact diagonal path: per wave, 16 x 16 alpha (fp32) and k (E) values,
   // placed after the rows-phase data
   constexpr int kStageBytes = 16 * 16 * (4 + (int)sizeof(E));
-  static_assert(kRowsBytes + 4 * kStageBytes <= kTilesBytes, "staging fits the shared region");
+  static_assert(kRowsBytes + 4 * kStageBytes + kC * 4 <= kTilesBytes,
+                "staging and sB fit the shared region");
+  // (fp32 I/O: 80 KiB in all, so that two workgroups may share a CU)
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRowsBytes > kTilesBytes ? kRowsBytes : kTilesBytes];
-  __shared__ __attribute__((aligned(16))) float sB[kC];
-  __shared__ float sRk[kNorm ? kC : 1], sRq[kNorm ? kC : 1];   // L2Norm row scales
+  float* const sB = reinterpret_cast<float*>(smem + kRowsBytes + 4 * kStageBytes);
   E* const sKf = reinterpret_cast<E*>(smem);
   float* const sF = reinterpret_cast<float*>(smem + 4 * 4 * kWave * 8 * sizeof(E));
   float* const sTot = sF + 4 * 5 * kD;
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
   }
   // optional L2Norm of the q and k rows: the row's 128 channels sit in the
   // four lanes r + 16 g; the scales are applied where the rows are first
-  // used (in fp32), and kept in LDS for the exact diagonal path.
+  // used (in fp32); the exact diagonal path takes them from the lanes.
   float rk = 1.f, rq = 1.f;
   if constexpr (kNorm) {
     float kk = 0.f, qq = 0.f;
@@ -363,7 +365,6 @@ __global__ __launch_bounds__(kIntraThreads) void intra_kernel(
     // hardware reciprocal square root (about 1 ulp), as the recurrent kernel
     rk = __builtin_amdgcn_rsqf(kk + kL2NormEps);
     rq = __builtin_amdgcn_rsqf(qq + kL2NormEps);
-    if (g == 0) { sRk[i] = rk; sRq[i] = rq; }
   }
 
   // ---- 1. gate: l_i = sum of log alpha over rows 16 I .. i (a scan across
