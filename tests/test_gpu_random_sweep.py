@@ -6,9 +6,10 @@ one-token, chunk-boundary and ragged sequences, the single-sequence launch
 (no cu_seqlens), nonzero or absent initial states, mild, split and extreme
 decay recipes, in-kernel L2Norm on raw q/k, and workspaces that force the
 prefill into windows of a few chunk slots. Batches whose mean length is at
-most two chunks take the short-sequence carry, batches with more than 32
-(sequence, head) pairs the two-tile carry; batches of sequences no longer
-than 64 tokens also go through the recurrent path. Tolerances as in the
+most two chunks (or four, with at least 256 (sequence, head) pairs: a mode
+of its own) take the short-sequence carry, other batches with more than 32
+pairs the two-tile carry; batches of sequences no longer than 64 tokens
+also go through the recurrent path. Tolerances as in the
 other parity tests (max |o - o_ref| / max |o_ref|, relative Frobenius error
 of the final state)."""
 import numpy as np
@@ -22,7 +23,7 @@ from tests.kda_testutil import TOL, dev, host, io_dtype, rel_fro_err, rel_max_er
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+N_CASES = 128
 
 
 def _draw_case(i):
@@ -52,6 +53,13 @@ def _draw_case(i):
     window = None
     if rng.random() < 0.4:
         window = int(rng.integers(1, 6))
+    if rng.random() < 0.12:
+        # at least 256 (sequence, head) pairs with a mean of two to four
+        # chunks: the short-sequence carry's many-pair case
+        H = 16
+        N = int(rng.integers(16, 25))
+        lengths = [int(x) for x in rng.integers(100, 300, size=N)]
+        single = False
     return dict(lengths=lengths, H=H, seed=7100 + i, io=io, decay=decay,
                 h0_std=h0_std, qk="raw" if l2norm else "unit"), \
         dict(l2norm=l2norm, single=single, window=window)
