@@ -1,4 +1,5 @@
-"""A seeded sweep of prefill and recurrent calls against the fp64 oracle.
+"""Seeded sweeps against the fp64 oracle: prefill and recurrent calls, and
+decode steps.
 
 Each case draws its own combination of the features the fixed parity tests
 cover one at a time: I/O dtype, head count, packed batches with empty,
@@ -11,7 +12,9 @@ of its own) take the short-sequence carry, other batches with more than 32
 pairs the two-tile carry; batches of sequences no longer than 64 tokens
 also go through the recurrent path. Tolerances as in the
 other parity tests (max |o - o_ref| / max |o_ref|, relative Frobenius error
-of the final state)."""
+of the final state). The decode sweep draws sequence and head counts (so
+both decode slice widths run), I/O dtype, fp32 or bf16 states and in-kernel
+L2Norm, and runs one to three steps with the state carried on the device."""
 import numpy as np
 import pytest
 
@@ -108,3 +111,57 @@ def test_random_case_against_oracle(i):
                                    qk_l2norm=opt["l2norm"])
         torch.cuda.synchronize()
         _check(p, host(o2), host(h2), ro, rh, "recurrent_fwd")
+
+
+N_DECODE = 32
+
+
+def _draw_decode(i):
+    """Decode case i: (io, N, H, steps, bf16 state, L2Norm), from its own
+    seeded stream. Small pair counts take the 16-column decode slices, bf16
+    states the 64-column ones."""
+    rng = np.random.default_rng(8000 + i)
+    io = "bf16" if rng.random() < 0.6 else "f32"
+    N = int(rng.choice([1, 2, 3, 5, 8, 17, 40]))
+    H = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
+    steps = int(rng.integers(1, 4))
+    bf16_state = bool(rng.random() < 0.3)
+    l2norm = bool(rng.random() < 0.25)
+    return io, N, H, steps, bf16_state, l2norm
+
+
+@pytest.mark.parametrize("i", range(N_DECODE))
+def test_random_decode_against_oracle(i):
+    """A few decode steps per case, the state carried on the device and in
+    fp64 by the oracle; fp32 states through kda_decode_step (or, with
+    L2Norm, kda_recurrent_fwd on one token), bf16 states through
+    kda_recurrent_fwd (rounded after every step, state tolerance 1e-2)."""
+    io, N, H, steps, bf16_state, l2norm = _draw_decode(i)
+    print(f"decode case {i}: io {io} N {N} H {H} steps {steps} bf16 state {bf16_state} "
+          f"l2norm {l2norm}")
+    S0 = workloads.make_decode_state(N, H, 8100 + i)
+    if bf16_state:
+        S0 = workloads.round_bf16(S0)
+    S = dev(S0, torch.bfloat16 if bf16_state else torch.float32)
+    ref = S0.astype(np.float64)
+    dt = io_dtype(io)
+    tol_o, tol_s = TOL[io]
+    if bf16_state:   # the rounded state sets the error, whatever the I/O dtype
+        tol_o, tol_s = TOL["bf16"]
+    for step in range(steps):
+        d = workloads.make_decode_step(N, H, 8200 + i, step, io=io,
+                                       qk="raw" if l2norm else "unit")
+        args = (dev(d.q, dt), dev(d.k, dt), dev(d.v, dt), dev(d.log_alpha), dev(d.beta))
+        if bf16_state or l2norm:
+            o, _ = kda.recurrent_fwd(*args, S, n_seqs=N, qk_l2norm=l2norm,
+                                     state_dtype=S.dtype, h_final=S)
+        else:
+            o = kda.decode_step(*args, S)
+        torch.cuda.synchronize()
+        q, k = (recurrent.l2norm(d.q), recurrent.l2norm(d.k)) if l2norm else (d.q, d.k)
+        ro, ref = recurrent.decode_step(q, k, d.v, d.log_alpha, d.beta, ref)
+        eo = rel_max_err(host(o).reshape(ro.shape), ro)
+        es = rel_fro_err(S.float().cpu().numpy().astype(np.float64), ref)
+        print(f"  step {step}: o err {eo:.3e} (tol {tol_o}), state err {es:.3e} (tol {tol_s})")
+        assert np.isfinite(host(o)).all()
+        assert eo <= tol_o and es <= tol_s, (step, eo, es)
