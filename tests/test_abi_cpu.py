@@ -489,3 +489,15 @@ def test_workspace_below_minimum_and_phase_windows(lib):
     assert call_prefill(lib, dict(a, ws_bytes=mn - 1)) == WS
     for ph in (1, 2):
         assert call_prefill(lib, dict(a, ws_bytes=mn), phase=ph) == WS
+
+
+def test_mode_switch_thresholds():
+    """kda.forward's crossover: 32 tokens for bf16 I/O whatever the batch;
+    for fp32 I/O 32 below 256 (sequence, head) pairs, 64 from 256, 512 from
+    512 (the measurements are in kda.py)."""
+    import torch
+    from gated_delta_rule_50_amd import kda
+    for pairs in (1, 32, 255, 256, 511, 512, 8192):
+        assert kda.recurrent_max_len(torch.bfloat16, pairs) == 32
+    assert [kda.recurrent_max_len(torch.float32, p) for p in (1, 32, 255, 256, 511, 512, 8192)] \
+        == [32, 32, 32, 64, 64, 512, 512]

@@ -326,17 +326,25 @@ def test_degenerate_cases(path, case):
         assert rel_fro_err(hf, want) <= 1e-2
 
 
-@pytest.mark.parametrize("lens", [[32, 3, 20], [33, 2, 17], [48, 200, 1]])
-def test_mode_switch_forward(lens):
-    """kda.forward picks the recurrent path for max length <= 32 (the
-    measured crossover) and the chunked one otherwise; both match the
-    oracle."""
-    p = workloads.make_prefill(lens, H=2, seed=63, io="bf16", h0_std=0.05)
-    bf = torch.bfloat16
-    args = (dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta),
+@pytest.mark.parametrize("io,lens,H,path", [
+    ("bf16", [32, 3, 20], 2, "recurrent"), ("bf16", [33, 2, 17], 2, "chunk"),
+    ("bf16", [48, 200, 1], 2, "chunk"),
+    ("f32", [32, 3, 20], 2, "recurrent"), ("f32", [33, 2, 17], 2, "chunk"),
+    # fp32 I/O with many (sequence, head) pairs: recurrent up to 64 tokens
+    # from 256 pairs, up to 512 from 512 pairs
+    ("f32", [64] * 8, 32, "recurrent"), ("f32", [65] + [10] * 7, 32, "chunk"),
+    ("f32", [100, 7, 0, 64] * 4, 32, "recurrent"), ("f32", [513] + [3] * 15, 32, "chunk")])
+def test_mode_switch_forward(io, lens, H, path):
+    """kda.forward takes the recurrent path up to the measured crossover for
+    the batch's I/O dtype and (sequence, head) pair count, the chunked one
+    beyond it; both match the oracle."""
+    assert (max(lens) <= kda.recurrent_max_len(io_dtype(io), len(lens) * H)) == (path == "recurrent")
+    p = workloads.make_prefill(lens, H=H, seed=63, io=io, h0_std=0.05)
+    dt = io_dtype(io)
+    args = (dev(p.q, dt), dev(p.k, dt), dev(p.v, dt), dev(p.log_alpha), dev(p.beta),
             dev(p.h0), dev(p.cu_seqlens, torch.int32))
     o, hf = kda.forward(*args, max_seqlen=max(lens))
-    want = kda.recurrent_fwd if max(lens) <= kda.RECURRENT_MAX_LEN else kda.chunk_fwd
+    want = kda.recurrent_fwd if path == "recurrent" else kda.chunk_fwd
     o2, hf2 = want(*args)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(hf, hf2)   # the path the switch names
