@@ -411,8 +411,13 @@ def check_inputs(q, k, v, log_alpha, beta, cu_seqlens=None, *, flags=None, strea
 # 64 and 256 sequences (L = 40: 177 against 186 us and 671 against 706 us)
 # and from 32 on for 16 sequences, and the recurrent one up to 32 for 64 and
 # 256 sequences (154 against 170 us, 597 against 639 us), so the switch sits
-# at 32 for bf16 I/O.
+# at 32 for bf16 I/O. A single sequence (a single prompt) takes the chunked
+# path's one-sequence launch, which skips the chunk map: there the recurrent
+# kernel wins only up to about 20 tokens (32 heads: 16 tokens 17.2 against
+# 19.6 us, 24 tokens 23.0 against 19.8, 32 tokens 28.8 against 19.9; 16
+# heads alike), so one bf16 sequence switches at 16.
 RECURRENT_MAX_LEN = 32
+RECURRENT_MAX_LEN_ONE_SEQ = 16
 # fp32 I/O: the chunked path's fp32 products run at a sixteenth of the bf16
 # rate and it has no short-sequence carry, so with many (sequence, head)
 # pairs the recurrent kernel stays faster much longer. Measured (32 heads,
@@ -424,27 +429,29 @@ RECURRENT_MAX_LEN = 32
 RECURRENT_MAX_LEN_F32 = ((512, 512), (256, 64))   # (at least this many pairs, max length)
 
 
-def recurrent_max_len(io_dtype: torch.dtype, pairs: int) -> int:
+def recurrent_max_len(io_dtype: torch.dtype, n_seqs: int, heads: int) -> int:
     """Longest sequence that kda.forward sends to the recurrent kernel for a
-    batch of `pairs` (sequence, head) pairs in this I/O dtype."""
+    batch of n_seqs sequences of `heads` heads in this I/O dtype."""
     if io_dtype == torch.float32:
         for min_pairs, max_len in RECURRENT_MAX_LEN_F32:
-            if pairs >= min_pairs:
+            if n_seqs * heads >= min_pairs:
                 return max_len
-    return RECURRENT_MAX_LEN
+        return RECURRENT_MAX_LEN
+    return RECURRENT_MAX_LEN_ONE_SEQ if n_seqs == 1 else RECURRENT_MAX_LEN
 
 
 def forward(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, max_seqlen, n_seqs=None,
             qk_l2norm=False, o=None, h_final=None, stream=None):
     """Mode switch after the "L2 Deep Distill" page's serving notes: batches
     whose sequences have at most recurrent_max_len(...) new tokens (32 for
-    bf16 I/O; for fp32 I/O up to 512 with many (sequence, head) pairs) go
+    bf16 I/O, 16 for one bf16 sequence; for fp32 I/O up to 512 with many
+    (sequence, head) pairs) go
     through the fused recurrent kernel, longer ones through the chunked
     prefill. max_seqlen is the longest sequence in the batch (the caller
     knows it; cu_seqlens stays on the device). Same tensors as chunk_fwd
     (fp32 states). Returns (o, h_final)."""
     N = int(cu_seqlens.shape[0]) - 1 if cu_seqlens is not None else int(n_seqs or 1)
-    if max_seqlen <= recurrent_max_len(k.dtype, N * int(k.shape[1])):
+    if max_seqlen <= recurrent_max_len(k.dtype, N, int(k.shape[1])):
         return recurrent_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs=n_seqs,
                              qk_l2norm=qk_l2norm, o=o, h_final=h_final, stream=stream)
     if cu_seqlens is None and (n_seqs or 1) != 1:

@@ -492,12 +492,15 @@ def test_workspace_below_minimum_and_phase_windows(lib):
 
 
 def test_mode_switch_thresholds():
-    """kda.forward's crossover: 32 tokens for bf16 I/O whatever the batch;
-    for fp32 I/O 32 below 256 (sequence, head) pairs, 64 from 256, 512 from
-    512 (the measurements are in kda.py)."""
+    """kda.forward's crossover: for bf16 I/O 16 tokens for one sequence and
+    32 for more; for fp32 I/O 32 below 256 (sequence, head) pairs, 64 from
+    256, 512 from 512 (the measurements are in kda.py)."""
     import torch
     from gated_delta_rule_50_amd import kda
-    for pairs in (1, 32, 255, 256, 511, 512, 8192):
-        assert kda.recurrent_max_len(torch.bfloat16, pairs) == 32
-    assert [kda.recurrent_max_len(torch.float32, p) for p in (1, 32, 255, 256, 511, 512, 8192)] \
-        == [32, 32, 32, 64, 64, 512, 512]
+    assert kda.recurrent_max_len(torch.bfloat16, 1, 32) == 16
+    assert kda.recurrent_max_len(torch.bfloat16, 1, 1) == 16
+    for n, h in ((2, 1), (2, 32), (16, 32), (256, 32)):
+        assert kda.recurrent_max_len(torch.bfloat16, n, h) == 32
+    assert [kda.recurrent_max_len(torch.float32, n, 32) for n in (1, 7, 8, 15, 16, 256)] \
+        == [32, 32, 64, 64, 512, 512]
+    assert kda.recurrent_max_len(torch.float32, 1, 16) == 32

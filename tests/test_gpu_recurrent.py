@@ -329,6 +329,8 @@ def test_degenerate_cases(path, case):
 @pytest.mark.parametrize("io,lens,H,path", [
     ("bf16", [32, 3, 20], 2, "recurrent"), ("bf16", [33, 2, 17], 2, "chunk"),
     ("bf16", [48, 200, 1], 2, "chunk"),
+    # one bf16 sequence: recurrent up to 16 tokens
+    ("bf16", [16], 32, "recurrent"), ("bf16", [17], 32, "chunk"), ("bf16", [32], 4, "chunk"),
     ("f32", [32, 3, 20], 2, "recurrent"), ("f32", [33, 2, 17], 2, "chunk"),
     # fp32 I/O with many (sequence, head) pairs: recurrent up to 64 tokens
     # from 256 pairs, up to 512 from 512 pairs
@@ -338,7 +340,7 @@ def test_mode_switch_forward(io, lens, H, path):
     """kda.forward takes the recurrent path up to the measured crossover for
     the batch's I/O dtype and (sequence, head) pair count, the chunked one
     beyond it; both match the oracle."""
-    assert (max(lens) <= kda.recurrent_max_len(io_dtype(io), len(lens) * H)) == (path == "recurrent")
+    assert (max(lens) <= kda.recurrent_max_len(io_dtype(io), len(lens), H)) == (path == "recurrent")
     p = workloads.make_prefill(lens, H=H, seed=63, io=io, h0_std=0.05)
     dt = io_dtype(io)
     args = (dev(p.q, dt), dev(p.k, dt), dev(p.v, dt), dev(p.log_alpha), dev(p.beta),
