@@ -729,8 +729,9 @@ struct WindowArgs {
 //   loader waves  stream the state wave's operands into an LDS ring; one
 //                 of them also stores the output wave's O tiles
 // Wave 3 (a loader) also touches one word per 128-byte line of this
-// workgroup's share of the block six chunks ahead (an eighth, or a quarter
-// with two tiles; buffer->LDS loads into a scratch slot, no registers), so
+// workgroup's share of the block kTouchAhead chunks ahead (an eighth six
+// chunks ahead, or a quarter four ahead with two tiles; buffer->LDS loads
+// into a scratch slot, no registers), so
 // the loaders and the output wave find the blocks in L2 rather than waiting
 // on HBM.
 // The state never leaves the state wave's registers; its accumulator tiles
@@ -750,7 +751,13 @@ struct WindowArgs {
 constexpr int kRing = 3;
 constexpr int kCarryThreads = 256;
 constexpr int64_t kCarryRound = 256;   // carry workgroups resident at once (one per CU)
-constexpr int kTouchAhead = 6;   // chunks between the L2 touch and the use of a block
+// Chunks between the L2 touch of a block and its use: six for one tile per
+// workgroup, four for two (the two-tile form runs on batches with many
+// pairs; measured on the 16-sequence packed batch, 3,967-3,988 us against
+// 4,059-4,101 with six; the 8K workload's one-tile carry loses with four,
+// 310-323 against 296-318 us).
+template <int kTiles>
+constexpr int kTouchAhead = kTiles == 1 ? 6 : 4;
 
 // Workgroup barrier without a memory fence: no wave waits on another's
 // global memory traffic, and LDS hand-offs are fenced by lgkmcnt where
@@ -1153,7 +1160,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     for (int b = b0; b < b0 + 3 && b < b1; ++b) issue(b);
     loader_wait(b0 + 2 < b1, false, false);   // chunks b0, b0 + 1 landed
     if (w == 3)
-      for (int b = b0 + 3; b < b0 + kTouchAhead && b < b1; ++b) touch(b);
+      for (int b = b0 + 3; b < b0 + kTouchAhead<kTiles> && b < b1; ++b) touch(b);
     ring_barrier();
     ring_barrier();
     // Wave 2 issues chunk b-1's O stores after its wait, so at its next wait
@@ -1163,10 +1170,10 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     // and the allowance leaves no room for a store.
     for (int b = b0; b < b1; ++b) {
       const bool dma = b + 3 < b1;
-      const bool tch = w == 3 && b + kTouchAhead < b1;
-      const bool prev = w == 3 && b + kTouchAhead - 1 < b1;
+      const bool tch = w == 3 && b + kTouchAhead<kTiles> < b1;
+      const bool prev = w == 3 && b + kTouchAhead<kTiles> - 1 < b1;
       if (dma) issue(b + 3);
-      if (tch) touch(b + kTouchAhead);
+      if (tch) touch(b + kTouchAhead<kTiles>);
       loader_wait(dma, tch, prev);
       if (w == 2 && b > b0) store_o(b - 1);
       ring_barrier();
@@ -1183,17 +1190,17 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       if (b0 + 1 < b1) issue(b0 + 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunks b0, b0 + 1 landed
       if (b0 + 2 < b1) issue(b0 + 2);
-      for (int b = b0 + 3; b < b0 + kTouchAhead && b < b1; ++b) touch(b);
+      for (int b = b0 + 3; b < b0 + kTouchAhead<kTiles> && b < b1; ++b) touch(b);
     }
     ring_barrier();
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
-      if (b > b0 && b + kTouchAhead - 1 < b1)
+      if (b > b0 && b + kTouchAhead<kTiles> - 1 < b1)
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTouchOps) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (b + 3 < b1) issue(b + 3);
-      if (b + kTouchAhead < b1) touch(b + kTouchAhead);
+      if (b + kTouchAhead<kTiles> < b1) touch(b + kTouchAhead<kTiles>);
       // after the issues: the next wait allows only the touch, so these
       // stores never let a DMA transfer count as landed
       if (b > b0) store_o(b - 1);
