@@ -1497,8 +1497,16 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     ring_barrier();
     for (int b = b0; b < b1; ++b) {
       if (b + 1 < b1) issue(b + 1);
-      if (wl == 1 && b + 2 < b1) touch(b + 2);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk b + 1 landed
+      const bool tch = wl == 1 && b + 2 < b1;
+      if (tch) touch(b + 2);
+      // chunk b + 1 landed; this iteration's touch may stay in flight (the
+      // counter retires in order and the touch was issued last): waiting
+      // for it too held the loader for its HBM round trip every chunk
+      // (fp32 8K call 643 -> 606 us)
+      if (tch)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTouchOps) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       ring_barrier();   // the state waves' pseudo-value swap
       ring_barrier();
     }
