@@ -98,7 +98,11 @@ int64_t block_bytes(int io) { return (int64_t)kda::inter_block_bytes(io == KDA_I
 // other over the chunk slots in sequence order, which costs one sequence
 // nothing but serialises the sequences of a packed batch (a window of 512
 // MiB holds one or two of the 16-sequence batch's): packed batches get a
-// larger window, so such batches stay one window.
+// larger window, so such batches stay one window. fp32 blocks take twice
+// the bytes of bf16 ones, so their cap is doubled to hold as many chunk
+// slots (the fp32 8K x 32-head call as one window: 638-684 against
+// 659-686 us in two; 65,536 tokens in windows of 198 slots 4.80 ms against
+// 4.97-5.00 in windows of 99).
 constexpr int64_t kWindowBytes = (int64_t)512 << 20;
 constexpr int64_t kPackedWindowBytes = (int64_t)8 << 30;
 
@@ -112,7 +116,8 @@ size_t workspace_bytes(int64_t n_seqs, int64_t T, int64_t heads, int io) {
   if (!valid_sizes(n_seqs, T, heads, io)) return 0;
   const int64_t slots = chunk_slots(n_seqs, T);
   const int64_t per_slot = heads * block_bytes(io);
-  const int64_t cap = n_seqs > 1 ? kPackedWindowBytes : kWindowBytes;
+  const int64_t cap =
+      n_seqs > 1 ? kPackedWindowBytes : (io == KDA_IO_F32 ? 2 : 1) * kWindowBytes;
   const int64_t win = std::min(slots, std::max<int64_t>(1, cap / per_slot));
   return (size_t)(inter_offset(n_seqs, heads) + win * per_slot);
 }

@@ -100,8 +100,9 @@ typedef enum {
  *   as the given workspace holds (below), so any size from the smallest up
  *   works and the results do not depend on it. For one sequence the
  *   recommended size holds every chunk of calls up to about 512 MiB of
- *   intermediates (8192 tokens x 32 heads in bf16 is one window) and that
- *   much otherwise: it does not grow with T beyond that. Windows follow the
+ *   intermediates in bf16, 1 GiB in float32 (8192 tokens x 32 heads is one
+ *   window either way) and that much otherwise: it does not grow with T
+ *   beyond that. Windows follow the
  *   chunk slots in sequence order, so a window holds few sequences of a
  *   packed batch and windows run one after the other: for N > 1 the
  *   recommended size holds up to 8 GiB of intermediates. The smallest size

@@ -93,13 +93,14 @@ def _block_bytes(io):
                                    (3, 64, 2), (300, 100000, 4), (1, 1 << 20, 32),
                                    (1, 1 << 24, 64), (16, 1 << 22, 32)])
 def test_workspace_formula(lib, io, N, T, H):
-    """Recommended size: the whole call's blocks up to 512 MiB of them (8 GiB
-    for a packed batch), else that much (it stops growing with T); smallest:
-    one chunk slot."""
+    """Recommended size: the whole call's blocks up to 512 MiB of them for one
+    bf16 sequence (1 GiB in fp32: as many chunk slots; 8 GiB for a packed
+    batch), else that much (it stops growing with T); smallest: one chunk
+    slot."""
     slots = (T + 63) // 64 + N - 1
     inter = 256 + (4 * (N + 1) + 255) // 256 * 256 + 2 * H * 128 * 128 * 4
     per_slot = H * _block_bytes(io)
-    cap = (512 << 20) if N == 1 else (8 << 30)
+    cap = ((1024 << 20) if io == F32 else (512 << 20)) if N == 1 else (8 << 30)
     win = min(slots, max(1, cap // per_slot))
     assert lib.kda_chunk_fwd_workspace_bytes(N, T, H, 128, 128, io) == inter + win * per_slot
     assert lib.kda_chunk_fwd_workspace_min_bytes(N, T, H, 128, 128, io) == \
