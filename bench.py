@@ -435,7 +435,8 @@ def prefill_alg_bytes(T, H, N, io_bytes=2, h0=False):
 def extensions(torch, d, pre_args, steps, warmup, extra=None, us_8k=None):
     """Timings of the optional paths (module docstring), inputs resident.
     extra: device inputs of the fp32 and exact-diagonal 8K prefills."""
-    from gated_delta_rule_50_amd import Prefill, Recurrent, decode_step, rmsnorm_gate, workloads
+    from gated_delta_rule_50_amd import (Decode, Prefill, Recurrent, decode_step, rmsnorm_gate,
+                                         workloads)
     bf = torch.bfloat16
     out = {}
     N, H = 256, 32
@@ -492,6 +493,13 @@ def extensions(torch, d, pre_args, steps, warmup, extra=None, us_8k=None):
         for t in toks:
             decode_step(*t, S1, o=o1)
     us_eager = _time_calls(torch, loop, steps, warmup) / steps1
+    # the same steps bound once (Decode): one library call per token
+    bound = [Decode(*t, S1, o=o1) for t in toks]
+
+    def loop_bound():
+        for b in bound:
+            b.run()
+    us_bound = _time_calls(torch, loop_bound, steps, warmup) / steps1
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -506,9 +514,10 @@ def extensions(torch, d, pre_args, steps, warmup, extra=None, us_8k=None):
     out["decode_batch1"] = {
         "workload": f"decode, 1 sequence x {cfg4.H} heads, fp32 state, {steps1} steps per "
                     "launch sequence", "us_per_token_eager": us_eager,
+        "us_per_token_bound": us_bound,
         "us_per_token_graph": us_graph, "tokens_per_s_graph": 1.0 / (us_graph * 1e-6),
         "alg_bytes": alg, "roofline": _hbm(alg, us_graph)}
-    del S1, toks, graph
+    del S1, toks, graph, bound
     pre_n = Prefill(*pre_args, qk_l2norm=True)
     us = _time_calls(torch, pre_n.run, steps, warmup)
     out["prefill_qk_l2norm"] = {

@@ -5,5 +5,5 @@
 """
 from .kda import (KDAError, Prefill, Recurrent, alloc_workspace, check_inputs,  # noqa: F401
                   chunk_fwd, chunk_fwd_noalloc, chunk_fwd_workspace_bytes,
-                  chunk_fwd_workspace_min_bytes, decode_step,
+                  chunk_fwd_workspace_min_bytes, Decode, decode_step,
                   forward, lib, recurrent_fwd, rmsnorm_gate)

@@ -252,33 +252,53 @@ def chunk_fwd_noalloc(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=N
                    want_final=want_final, qk_l2norm=qk_l2norm, noalloc=True).run(stream)
 
 
+class Decode:
+    """Device buffers of one decode step (kda_decode_step), marshalled once.
+
+    q, k, v [N, H, 128] (bf16 or fp32, one dtype); log_alpha [N, H, 128]
+    fp32; beta [N, H] fp32; S [N, H, 128, 128] fp32, updated in place by
+    every run. A serving loop that writes each new token into the same
+    q/k/v/log_alpha/beta buffers binds them once and pays one library call
+    per token in run(); the shape, dtype and device checks happen here.
+    """
+
+    def __init__(self, q, k, v, log_alpha, beta, S, *, o=None):
+        dev = k.device
+        N, H = _head_rows(k)
+        for t, n in ((q, "q"), (v, "v"), (log_alpha, "log_alpha"), (o, "o")):
+            _shape(t, n, (N, H, HEAD_DIM))
+        _shape(beta, "beta", (N, H))
+        _shape(S, "S", (N, H, HEAD_DIM, HEAD_DIM))
+        io = _io(k.dtype)
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _check(t, n, k.dtype, dev)
+        _check(log_alpha, "log_alpha", torch.float32, dev)
+        _check(beta, "beta", torch.float32, dev)
+        _check(S, "S", torch.float32, dev)
+        if o is None:
+            o = torch.empty((N, H, v.shape[2]), dtype=k.dtype, device=dev)
+        _check(o, "o", k.dtype, dev)
+        self.device, self.o, self.S = dev, o, S
+        self._keep = (q, k, v, log_alpha, beta)
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), N, H,
+                      int(k.shape[2]), int(v.shape[2]), io, _ptr(o))
+        self._fn = lib().kda_decode_step
+
+    def run(self, stream=None):
+        st = self._fn(*self._args, _stream(stream, self.device))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_decode_step")
+        return self.o
+
+
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     """One recurrent step; S [N, H, 128, 128] fp32 is updated in place.
 
     q, k, v [N, H, 128] (bf16 or fp32); log_alpha [N, H, 128] fp32;
-    beta [N, H] fp32. Returns o [N, H, 128].
+    beta [N, H] fp32. Returns o [N, H, 128]. (Decode binds the buffers once
+    for repeated steps.)
     """
-    dev = k.device
-    N, H = _head_rows(k)
-    for t, n in ((q, "q"), (v, "v"), (log_alpha, "log_alpha"), (o, "o")):
-        _shape(t, n, (N, H, HEAD_DIM))
-    _shape(beta, "beta", (N, H))
-    _shape(S, "S", (N, H, HEAD_DIM, HEAD_DIM))
-    io = _io(k.dtype)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, k.dtype, dev)
-    _check(log_alpha, "log_alpha", torch.float32, dev)
-    _check(beta, "beta", torch.float32, dev)
-    _check(S, "S", torch.float32, dev)
-    if o is None:
-        o = torch.empty((N, H, v.shape[2]), dtype=k.dtype, device=dev)
-    _check(o, "o", k.dtype, dev)
-    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                               _ptr(S), N, H, int(k.shape[2]), int(v.shape[2]), io,
-                               _ptr(o), _stream(stream, dev))
-    if st != KDA_OK:
-        raise KDAError(st, "kda_decode_step")
-    return o
+    return Decode(q, k, v, log_alpha, beta, S, o=o).run(stream)
 
 
 class Recurrent:
