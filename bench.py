@@ -22,7 +22,7 @@ entry point) to measure each kernel's own duration (``kernels``).
 decay, nonzero h0) and on the 16-sequence packed batch, each with its own
 roofline and traffic. ``sweep_h16``: one sequence of 16 heads at T = 2K ..
 64K, the shape of the pages' kernel-speed figure (their times are quoted as
-context; the pages do not name the hardware).
+context; the pages do not name the hardware), and at 2^20 tokens.
 
 ``extensions`` times the operator's optional paths, each on its own
 workload with its own roofline: the fused multi-token recurrent call
@@ -605,7 +605,9 @@ def long_config(torch, x, name, steps, warmup):
 
 def sweep_h16(torch, x, steps, warmup):
     """One sequence of 16 heads at T = 2K .. 64K (prefixes of one seeded
-    64K-token batch): the operator shape of the pages' kernel-speed figure."""
+    64K-token batch): the operator shape of the pages' kernel-speed figure;
+    and at 2^20 tokens, the longest context at which the pages report the
+    whole model's prefill and decode times."""
     from gated_delta_rule_50_amd import Prefill
     rows = []
     for T in SWEEP_T:
@@ -616,6 +618,19 @@ def sweep_h16(torch, x, steps, warmup):
                      "frac_hbm": alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                      "chunks": (T + C - 1) // C})
         del pre
+    # the pages' million-token context: the 64K draw repeated 16 times (the
+    # timing does not depend on the values; the workspace stays at its cap)
+    reps = (1 << 20) // SWEEP_T[-1]
+    big = {n: x[n].repeat(reps, *([1] * (x[n].dim() - 1))) for n in ("q", "k", "v", "la", "beta")}
+    T = int(big["k"].shape[0])
+    pre = Prefill(big["q"], big["k"], big["v"], big["la"], big["beta"])
+    us = _time_calls(torch, pre.run, max(3, steps // 4), max(1, warmup // 2))
+    alg = prefill_alg_bytes(T, SWEEP_H, 1)
+    rows.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6),
+                 "frac_hbm": alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                 "chunks": (T + C - 1) // C, "workspace_bytes": int(pre.workspace.numel()),
+                 "inputs": f"the {SWEEP_T[-1]}-token draw repeated {reps} times"})
+    del pre, big
     torch.cuda.empty_cache()
     return {"workload": f"1 sequence, H={SWEEP_H}, d=128, bf16 q/k/v, h0=0",
             "rows": rows,
