@@ -3,6 +3,12 @@
 Argument marshalling only: torch tensors supply device memory and the
 current HIP stream; every step of the operator runs in the HIP kernels. If
 the library is not built the calls raise instead of falling back to anything.
+
+Streams: the functions that take stream= allocate what they allocate (o,
+h_final, the workspace) with that stream current, so torch's caching
+allocator hands the memory on only in that stream's order. The classes
+allocate on the stream current at construction; a caller that runs them on
+another stream keeps the object alive until that stream's work is done.
 """
 from __future__ import annotations
 
@@ -237,9 +243,10 @@ class Prefill:
 def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
               h_final=None, want_final=True, workspace=None, qk_l2norm=False, stream=None):
     """Chunked prefill (see Prefill for shapes). Returns (o, h_final or None)."""
-    return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
-                   want_final=want_final, workspace=workspace,
-                   qk_l2norm=qk_l2norm).run(stream)
+    with torch.cuda.stream(stream):
+        return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
+                       want_final=want_final, workspace=workspace,
+                       qk_l2norm=qk_l2norm).run(stream)
 
 
 def chunk_fwd_noalloc(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
@@ -248,8 +255,9 @@ def chunk_fwd_noalloc(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=N
     library's fixed per-GPU array, so the call itself allocates nothing
     (pass o, and h_final or want_final=False, to allocate nothing here
     either). Calls overlapping on one GPU race on that array."""
-    return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
-                   want_final=want_final, qk_l2norm=qk_l2norm, noalloc=True).run(stream)
+    with torch.cuda.stream(stream):
+        return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
+                       want_final=want_final, qk_l2norm=qk_l2norm, noalloc=True).run(stream)
 
 
 class Decode:
@@ -298,7 +306,8 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     beta [N, H] fp32. Returns o [N, H, 128]. (Decode binds the buffers once
     for repeated steps.)
     """
-    return Decode(q, k, v, log_alpha, beta, S, o=o).run(stream)
+    with torch.cuda.stream(stream):
+        return Decode(q, k, v, log_alpha, beta, S, o=o).run(stream)
 
 
 class Recurrent:
@@ -362,9 +371,10 @@ def recurrent_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, n_seqs=
                   state_dtype=torch.float32, qk_l2norm=False, o=None, h_final=None,
                   want_final=True, stream=None):
     """Fused token-by-token forward (see Recurrent). Returns (o, h_final or None)."""
-    return Recurrent(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs=n_seqs,
-                     state_dtype=state_dtype, qk_l2norm=qk_l2norm, o=o, h_final=h_final,
-                     want_final=want_final).run(stream)
+    with torch.cuda.stream(stream):
+        return Recurrent(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs=n_seqs,
+                         state_dtype=state_dtype, qk_l2norm=qk_l2norm, o=o, h_final=h_final,
+                         want_final=want_final).run(stream)
 
 
 def rmsnorm_gate(o, gate, weight=None, eps=1e-6, *, y=None, stream=None):
@@ -382,7 +392,8 @@ def rmsnorm_gate(o, gate, weight=None, eps=1e-6, *, y=None, stream=None):
     _check(gate, "gate", o.dtype, dev)
     _check(weight, "weight", torch.float32, dev)
     if y is None:
-        y = torch.empty_like(o)
+        with torch.cuda.stream(stream):
+            y = torch.empty_like(o)
     _check(y, "y", o.dtype, dev)
     dv = int(o.shape[-1])
     rows = o.numel() // max(dv, 1)
@@ -414,15 +425,17 @@ def check_inputs(q, k, v, log_alpha, beta, cu_seqlens=None, *, flags=None, strea
     _check(log_alpha, "log_alpha", torch.float32, dev)
     _check(beta, "beta", torch.float32, dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    out = torch.empty(1, dtype=torch.int32, device=dev) if flags is None else flags
-    _check(out, "flags", torch.int32, dev)
-    n = 0 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
-    st = lib().kda_check_inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                _ptr(cu_seqlens), n, T, H, int(k.shape[2]), int(v.shape[2]),
-                                _io(k.dtype), _ptr(out), _stream(stream, dev))
-    if st != KDA_OK:
-        raise KDAError(st, "kda_check_inputs")
-    return out if flags is not None else int(out.item())
+    with torch.cuda.stream(stream):   # out and its read-back on the check's stream
+        out = torch.empty(1, dtype=torch.int32, device=dev) if flags is None else flags
+        _check(out, "flags", torch.int32, dev)
+        n = 0 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+        st = lib().kda_check_inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                    _ptr(cu_seqlens), n, T, H, int(k.shape[2]),
+                                    int(v.shape[2]), _io(k.dtype), _ptr(out),
+                                    _stream(stream, dev))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_check_inputs")
+        return out if flags is not None else int(out.item())
 
 
 # Longest sequence routed to the recurrent kernel. The pages' serving notes
@@ -469,12 +482,18 @@ def forward(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, max_seqlen, n
     through the fused recurrent kernel, longer ones through the chunked
     prefill. max_seqlen is the longest sequence in the batch (the caller
     knows it; cu_seqlens stays on the device). Same tensors as chunk_fwd
-    (fp32 states). Returns (o, h_final)."""
+    (fp32 states); with cu_seqlens None, n_seqs sequences of T / n_seqs
+    tokens each. Returns (o, h_final)."""
     N = int(cu_seqlens.shape[0]) - 1 if cu_seqlens is not None else int(n_seqs or 1)
     if max_seqlen <= recurrent_max_len(k.dtype, N, int(k.shape[1])):
         return recurrent_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs=n_seqs,
                              qk_l2norm=qk_l2norm, o=o, h_final=h_final, stream=stream)
-    if cu_seqlens is None and (n_seqs or 1) != 1:
-        raise ValueError("the chunked path needs cu_seqlens for more than one sequence")
+    if cu_seqlens is None and N != 1:
+        # fixed-length batch: the chunked path takes its sequence offsets
+        T = int(k.shape[0])
+        if N < 1 or T % N != 0:
+            raise ValueError(f"{T} tokens do not split into {N} sequences of equal length")
+        with torch.cuda.stream(stream):
+            cu_seqlens = torch.arange(N + 1, dtype=torch.int32, device=k.device) * (T // N)
     return chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
                      qk_l2norm=qk_l2norm, stream=stream)

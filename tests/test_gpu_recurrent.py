@@ -351,3 +351,75 @@ def test_mode_switch_forward(io, lens, H, path):
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(hf, hf2)   # the path the switch names
     _check(p, host(o), host(hf))
+
+
+
+@pytest.mark.parametrize("L,path", [(20, "recurrent"), (100, "chunk"), (0, "recurrent")])
+def test_mode_switch_fixed_length_batch(L, path):
+    """A fixed-length batch (no cu_seqlens, n_seqs sequences of L tokens):
+    kda.forward takes either path; past the crossover the chunked path gets
+    evenly spaced sequence offsets and matches chunk_fwd given them
+    explicitly, and the oracle."""
+    N, H = 3, 2
+    p = workloads.make_prefill([L] * N, H=H, seed=64, io="bf16", h0_std=0.05)
+    bf = torch.bfloat16
+    args = (dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta),
+            dev(p.h0))
+    o, hf = kda.forward(*args, max_seqlen=L, n_seqs=N)
+    if path == "chunk":
+        o2, hf2 = kda.chunk_fwd(*args, dev(p.cu_seqlens, torch.int32))
+    else:
+        o2, hf2 = kda.recurrent_fwd(*args, n_seqs=N)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(hf, hf2)
+    if L:
+        _check(p, host(o), host(hf))
+    else:                            # no tokens: the states pass through
+        np.testing.assert_array_equal(host(hf), p.h0)
+
+
+def test_mode_switch_fixed_length_needs_equal_lengths():
+    p = workloads.make_prefill([100] * 3, H=2, seed=64, io="bf16")
+    bf = torch.bfloat16
+    args = (dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta))
+    with pytest.raises(ValueError, match="equal length"):
+        kda.forward(*args, max_seqlen=100, n_seqs=7)
+
+
+def test_functional_calls_on_a_side_stream():
+    """Every functional entry point given stream= runs its kernels and its
+    allocations on that stream: results equal the same calls on the default
+    stream, with default-stream work queued beside them."""
+    p = workloads.make_prefill([130, 7, 64], H=2, seed=65, io="bf16", h0_std=0.05)
+    bf = torch.bfloat16
+    args = (dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta),
+            dev(p.h0), dev(p.cu_seqlens, torch.int32))
+    d = workloads.make_decode_step(3, 2, seed=65, step=0, io="bf16")
+    toks = (dev(d.q, bf), dev(d.k, bf), dev(d.v, bf), dev(d.log_alpha), dev(d.beta))
+    S0 = dev(workloads.make_decode_state(3, 2, seed=65, std=0.05))
+    gate = dev(workloads.make_epilogue(p.q.shape[0] * 2, seed=65).gate, bf).view(p.q.shape)
+
+    def calls(stream):
+        with torch.cuda.stream(stream):
+            S = S0.clone()
+        o, hf = kda.chunk_fwd(*args, stream=stream)
+        o_r, hf_r = kda.recurrent_fwd(*args, stream=stream)
+        o_d = kda.decode_step(*toks, S, stream=stream)
+        y = kda.rmsnorm_gate(o, gate, stream=stream)
+        bad = kda.check_inputs(*args[:5], args[6], stream=stream)
+        o_f, hf_f = kda.forward(*args, max_seqlen=130, stream=stream)
+        return [o, hf, o_r, hf_r, o_d, S, y, o_f, hf_f], bad
+
+    ref, bad_ref = calls(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    busy = torch.zeros(1 << 26, device="cuda")
+    for _ in range(4):
+        busy.add_(1.0)               # default-stream work queued beside the calls
+    got, bad = calls(side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert bad == bad_ref == 0
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert torch.equal(a, b), i
