@@ -10,12 +10,13 @@
 #include "kda.h"
 
 namespace kda {
-hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q, const void* k,
-                            const void* v, const float* log_alpha, const float* beta,
-                            const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
-                            int32_t H, int64_t n_slots, int64_t win_slots, void* o,
-                            float* h_final, int32_t* status, int32_t* chunk_offset,
-                            float* state_area, uint8_t* inter, hipStream_t stream);
+hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, bool bf16_state,
+                            const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* beta, const void* h0,
+                            const int32_t* cu, int32_t n_seqs, int64_t T, int32_t H,
+                            int64_t n_slots, int64_t win_slots, void* o, void* h_final,
+                            int32_t* status, int32_t* chunk_offset, float* state_area,
+                            uint8_t* inter, hipStream_t stream);
 size_t inter_block_bytes(bool bf16_io);
 hipError_t launch_recurrent_fwd(bool bf16_io, bool bf16_state, bool l2norm, const void* q,
                                 const void* k, const void* v, const float* log_alpha,
@@ -154,15 +155,15 @@ namespace {
 // Validates the prefill arguments and launches the phases selected by the
 // bit mask `phases` (bit 0: chunk map, bit 1: intra-chunk, bit 2: carry).
 kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* v,
-                          const float* log_alpha, const float* beta, const float* h0,
+                          const float* log_alpha, const float* beta, const void* h0,
                           const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
                           int32_t heads, int32_t dk, int32_t dv, int io,
-                          uint32_t flags, void* o, float* h_final, void* workspace,
+                          uint32_t flags, void* o, void* h_final, void* workspace,
                           size_t workspace_bytes_given, void* stream) {
   const int64_t T = total_tokens;
   if (T < 0 || n_seqs < 1 || heads < 1) return KDA_ERR_SHAPE;
   if (dk != kDim || dv != kDim || !valid_io(io) || heads > 65535) return KDA_ERR_UNSUPPORTED;
-  if (flags & ~(uint32_t)KDA_FLAG_QK_L2NORM) return KDA_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)(KDA_FLAG_QK_L2NORM | KDA_FLAG_STATE_BF16)) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens == nullptr && n_seqs != 1) return KDA_ERR_NULL;
   if (cu_seqlens != nullptr && T > INT32_MAX) return KDA_ERR_SHAPE;
   // the carry grid has up to eight workgroups per (sequence, head) pair
@@ -189,7 +190,8 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
   const Range rq(q, th * kDim * eb), rk(k, th * kDim * eb), rv(v, th * kDim * eb);
   const Range rla(log_alpha, th * kDim * 4), rb(beta, th * 4);
   const Range ro(o, th * kDim * eb);
-  const int64_t state_bytes = (int64_t)n_seqs * heads * kDim * kDim * 4;
+  const int64_t state_bytes =
+      (int64_t)n_seqs * heads * kDim * kDim * ((flags & KDA_FLAG_STATE_BF16) ? 2 : 4);
   const Range rh0(h0, state_bytes), rhf(h_final, state_bytes);
   const Range rcu(cu_seqlens, 4 * ((int64_t)n_seqs + 1));
   const Range rws(workspace, used);
@@ -207,9 +209,10 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
   float* state_area = reinterpret_cast<float*>(ws + state_offset(n_seqs));
   uint8_t* inter = ws + inter_offset(n_seqs, heads);
   const hipError_t err = kda::launch_chunk_fwd(
-      phases, io == KDA_IO_BF16, (flags & KDA_FLAG_QK_L2NORM) != 0, q, k, v, log_alpha, beta,
-      h0, cu_seqlens, n_seqs, T, heads, slots, std::max<int64_t>(win, 1), o, h_final, status,
-      chunk_offset, state_area, inter, static_cast<hipStream_t>(stream));
+      phases, io == KDA_IO_BF16, (flags & KDA_FLAG_QK_L2NORM) != 0,
+      (flags & KDA_FLAG_STATE_BF16) != 0, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs,
+      T, heads, slots, std::max<int64_t>(win, 1), o, h_final, status, chunk_offset,
+      state_area, inter, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -218,10 +221,10 @@ kda_status chunk_fwd_impl(int phases, const void* q, const void* k, const void* 
 extern "C" {
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
-                         const float* log_alpha, const float* beta, const float* h0,
+                         const float* log_alpha, const float* beta, const void* h0,
                          const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
                          int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io,
-                         uint32_t flags, void* o, float* h_final, void* workspace,
+                         uint32_t flags, void* o, void* h_final, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl(7, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens,
                         heads, dk, dv, raw(io), flags, o, h_final, workspace, workspace_bytes,
@@ -229,10 +232,10 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
 }
 
 kda_status kda_chunk_fwd_phase(int32_t phase, const void* q, const void* k, const void* v,
-                               const float* log_alpha, const float* beta, const float* h0,
+                               const float* log_alpha, const float* beta, const void* h0,
                                const int32_t* cu_seqlens, int32_t n_seqs,
                                int64_t total_tokens, int32_t heads, int32_t dk, int32_t dv,
-                               kda_io_dtype io, uint32_t flags, void* o, float* h_final,
+                               kda_io_dtype io, uint32_t flags, void* o, void* h_final,
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (phase < 0 || phase > 2) return KDA_ERR_SHAPE;
   return chunk_fwd_impl(1 << phase, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs,

@@ -39,9 +39,9 @@ void* scratch_ptr() {
 
 extern "C" kda_status kda_chunk_fwd_noalloc(
     const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
-    const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+    const void* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
     int32_t heads, int32_t dk, int32_t dv, kda_io_dtype io, uint32_t flags, void* o,
-    float* h_final, void* stream) {
+    void* h_final, void* stream) {
   // the size check is host arithmetic only: a call beyond the array is
   // refused before any HIP call. The prefill runs over windows of chunk
   // slots sized to the workspace, so the array only has to hold one slot.

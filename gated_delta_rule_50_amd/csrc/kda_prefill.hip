@@ -685,6 +685,55 @@ __global__ __launch_bounds__(kIntraThreads, sizeof(E) == 4 ? 2 : 1) void intra_k
 // the area holds one state per head, in two slots that alternate between
 // windows (a window reads the slot the previous one wrote and writes the
 // other).
+// A sequence-head's state where a carry workgroup starts: the fp32 state
+// the previous window left in the workspace, or the caller's h0 in the state
+// type SE (float or bf16), or zeros.
+template <class SE>
+struct StateIn {
+  const float* f;
+  const SE* s;
+  // S[mt][e] = state[16 mt + 4 g + e][j], the accumulator layout of a
+  // 128 x 16 column tile (zeros when there is no state)
+  __device__ void load(floatx4 (&S)[8], int g, int j) const {
+    if (f) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[mt][e] = f[(16 * mt + 4 * g + e) * kD + j];
+    } else if (s) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[mt][e] = to_f(s[(16 * mt + 4 * g + e) * kD + j]);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) S[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+};
+// Where it leaves the state: the next window's fp32 slot, or the caller's
+// h_final in SE (rounded to nearest even for bf16), or nowhere.
+template <class SE>
+struct StateOut {
+  float* f;
+  SE* s;
+  // row tiles [mt0, mt1) of the accumulator layout above
+  template <int kMt0 = 0, int kMt1 = 8>
+  __device__ void store(const floatx4 (&S)[8], int g, int j) const {
+    if (f) {
+#pragma unroll
+      for (int mt = kMt0; mt < kMt1; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
+    } else if (s) {
+#pragma unroll
+      for (int mt = kMt0; mt < kMt1; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[(16 * mt + 4 * g + e) * kD + j] = from_f<SE>(S[mt][e]);
+    }
+  }
+};
+
 struct WindowArgs {
   int32_t W0, W1;          // this window's chunk slots
   int32_t last;            // 1 for the last window of the call
@@ -707,15 +756,17 @@ struct WindowArgs {
   }
   // State at chunk b0: h0 (or NULL for zeros) at the sequence's first
   // chunk, else the state the previous window left.
-  __device__ const float* state_in(int sb0, int b0, const float* h0, int pair, int h) const {
-    if (b0 > sb0) return resume + (int64_t)h * kD * kD;
-    return h0 ? h0 + (int64_t)pair * kD * kD : nullptr;
+  template <class SE>
+  __device__ StateIn<SE> state_in(int sb0, int b0, const SE* h0, int pair, int h) const {
+    if (b0 > sb0) return {resume + (int64_t)h * kD * kD, nullptr};
+    return {nullptr, h0 ? h0 + (int64_t)pair * kD * kD : nullptr};
   }
   // Where the state after chunk b1 - 1 goes: h_final (or nowhere) after the
   // sequence's last chunk, else the next window's state slot.
-  __device__ float* state_out(int sb1, int b1, float* h_final, int pair, int h) const {
-    if (b1 < sb1) return suspend + (int64_t)h * kD * kD;
-    return h_final ? h_final + (int64_t)pair * kD * kD : nullptr;
+  template <class SE>
+  __device__ StateOut<SE> state_out(int sb1, int b1, SE* h_final, int pair, int h) const {
+    if (b1 < sb1) return {suspend + (int64_t)h * kD * kD, nullptr};
+    return {nullptr, h_final ? h_final + (int64_t)pair * kD * kD : nullptr};
   }
 };
 
@@ -909,12 +960,12 @@ __device__ __forceinline__ void store_out(const Frag16<E> (&x)[4], E* __restrict
 // Two tiles per workgroup halve the L2 traffic per column tile at the cost
 // of a longer chain per chunk; they pay when there are more (sequence,
 // head) pairs than one round of one-tile workgroups fills.
-template <class E, int kTiles>
+template <class E, int kTiles, class SE>
 __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     const uint8_t* inter,   // not restrict: prefetch loads stay ahead of the barriers
     const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
-    const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
+    const SE* h0, SE* h_final,   // not restrict: h_final may be h0 (in place)
     E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, int32_t single,
     WindowArgs win) {
   static_assert(kTiles == 1 || kTiles == 2, "one or two column tiles per workgroup");
@@ -1069,12 +1120,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     auto gc_src = [&](int b) { return reinterpret_cast<const float*>(slot(b) + kGOff); };
     floatx4 S[8];
     Frag<E> fs[4];
-    const float* h0p = win.state_in(sb0, b0, h0, pair, h);
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        S[mt][e] = h0p ? h0p[(16 * mt + 4 * g + e) * kD + j] : 0.f;
+    win.state_in(sb0, b0, h0, pair, h).load(S, g, j);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -1112,12 +1158,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       step(b + 1, sb, sa);
     }
     if (b < b1) step(b, sa, sb);
-    if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
-    }
+    win.state_out(sb1, b1, h_final, pair, h).store(S, g, j);
   } else if (w == kTiles) {
     // output wave of the group's tiles
     auto step = [&](int b, OutOps<E, kTiles>& out) {
@@ -1238,10 +1279,11 @@ constexpr int kF32Buf = kF32GOff + 1024;       // 69 KiB
 constexpr int kF32States = 4;                  // state waves (and output waves)
 constexpr int kF32Threads = (2 * kF32States + 2) * kWave;
 
+template <class SE>
 __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     const uint8_t* inter, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
-    const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
+    const SE* h0, SE* h_final,   // not restrict: h_final may be h0 (in place)
     float* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, int32_t single,
     WindowArgs win) {
   typedef float E;
@@ -1283,12 +1325,7 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
     const int j = 16 * jt + (lane & 15);
     floatx4 S[8];
     Frag<E> fs[4];
-    const float* h0p = win.state_in(sb0, b0, h0, pair, h);
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        S[mt][e] = h0p ? h0p[(16 * mt + 4 * g + e) * kD + j] : 0.f;
+    win.state_in(sb0, b0, h0, pair, h).load(S, g, j);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -1376,14 +1413,8 @@ __global__ __launch_bounds__(kF32Threads) void carry_f32_kernel(
       __builtin_amdgcn_s_waitcnt(0xC07F);
       ring_barrier();
     }
-    if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
-#pragma unroll
-      for (int q = 0; q < kST; ++q) {
-        const int mt = kST * hs + q;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
-      }
-    }
+    // this wave's state rows: tiles kST hs .. kST hs + kST - 1
+    win.state_out(sb1, b1, h_final, pair, h).template store<kST * hs, kST * hs + kST>(S, g, j);
   };
   // output wave ho: O tiles nt = kXT ho .. kXT ho + kXT - 1
   auto output_role = [&](int ho) {
@@ -1531,11 +1562,11 @@ constexpr int kShortThreads = 8 * kWave;
 constexpr int kShortShared = kStageW * 2 + kStageKT;   // [-W ; Qt] and K'^T bytes
 constexpr int kShortXfers = kShortShared / 1024 + 1;   // and gamma_C
 
-template <class E>
+template <class E, class SE>
 __global__ __launch_bounds__(kShortThreads, 2) void carry_short_kernel(
     const uint8_t* __restrict__ inter, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_offset, const int32_t* __restrict__ status,
-    const float* h0, float* h_final,   // not restrict: h_final may be h0 (in place)
+    const SE* h0, SE* h_final,   // not restrict: h_final may be h0 (in place)
     E* __restrict__ o, int32_t n_seqs, int64_t T, int32_t H, WindowArgs win) {
   static_assert(sizeof(E) == 2, "bf16 intermediates");
   static_assert(Inter<E>::kXA == 0 && Inter<E>::kKT * sizeof(E) == kStageW * 2,
@@ -1559,11 +1590,7 @@ __global__ __launch_bounds__(kShortThreads, 2) void carry_short_kernel(
 
   floatx4 S[8];
   Frag<E> fs[4];
-  const float* h0p = win.state_in(sb0, b0, h0, pair, h);
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) S[mt][e] = h0p ? h0p[(16 * mt + 4 * g + e) * kD + j] : 0.f;
+  win.state_in(sb0, b0, h0, pair, h).load(S, g, j);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -1667,12 +1694,7 @@ __global__ __launch_bounds__(kShortThreads, 2) void carry_short_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
-  if (float* hf = win.state_out(sb1, b1, h_final, pair, h)) {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hf[(16 * mt + 4 * g + e) * kD + j] = S[mt][e];
-  }
+  win.state_out(sb1, b1, h_final, pair, h).store(S, g, j);
 }
 
 // ------------------------------------------------------------- launchers
@@ -1686,12 +1708,13 @@ size_t inter_block_bytes(bool bf16_io) {
 // run in windows of win_slots: per window the intra-chunk kernel, then the
 // carry. state_area holds two [H, 128, 128] float32 states for sequences
 // crossing a window boundary.
-hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q, const void* k,
-                            const void* v, const float* log_alpha, const float* beta,
-                            const float* h0, const int32_t* cu, int32_t n_seqs, int64_t T,
-                            int32_t H, int64_t n_slots, int64_t win_slots, void* o,
-                            float* h_final, int32_t* status, int32_t* chunk_offset,
-                            float* state_area, uint8_t* inter, hipStream_t stream) {
+hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, bool bf16_state,
+                            const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* beta, const void* h0,
+                            const int32_t* cu, int32_t n_seqs, int64_t T, int32_t H,
+                            int64_t n_slots, int64_t win_slots, void* o, void* h_final,
+                            int32_t* status, int32_t* chunk_offset, float* state_area,
+                            uint8_t* inter, hipStream_t stream) {
   hipError_t err = hipSuccess;
   // A full call on one sequence needs no chunk map: the two kernels derive
   // the chunk range from T and check cu_seqlens themselves.
@@ -1746,18 +1769,25 @@ hipError_t launch_chunk_fwd(int phases, bool bf16_io, bool l2norm, const void* q
     win.last = w == n_windows - 1;
     win.resume = state_area + ((w + 1) & 1) * state_floats;
     win.suspend = state_area + (w & 1) * state_floats;
-    if (short_seqs)
-      carry_short_kernel<bf16><<<(unsigned)pairs, kShortThreads, 0, stream>>>(
-          inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, win);
-    else if (two)
-      carry_kernel<bf16, 2><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
-          inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single, win);
-    else if (bf16_io)
-      carry_kernel<bf16, 1><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
-          inter, cu, chunk_offset, status, h0, h_final, (bf16*)o, n_seqs, T, H, single, win);
-    else
-      carry_f32_kernel<<<(unsigned)nblocks, kF32Threads, 0, stream>>>(
-          inter, cu, chunk_offset, status, h0, h_final, (float*)o, n_seqs, T, H, single, win);
+    // h0 and h_final in the state type SE (the carry keeps fp32 inside)
+    auto carry = [&](auto se) {
+      typedef decltype(se) SE;
+      const SE* h0s = static_cast<const SE*>(h0);
+      SE* hfs = static_cast<SE*>(h_final);
+      if (short_seqs)
+        carry_short_kernel<bf16, SE><<<(unsigned)pairs, kShortThreads, 0, stream>>>(
+            inter, cu, chunk_offset, status, h0s, hfs, (bf16*)o, n_seqs, T, H, win);
+      else if (two)
+        carry_kernel<bf16, 2, SE><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+            inter, cu, chunk_offset, status, h0s, hfs, (bf16*)o, n_seqs, T, H, single, win);
+      else if (bf16_io)
+        carry_kernel<bf16, 1, SE><<<(unsigned)nblocks, kCarryThreads, 0, stream>>>(
+            inter, cu, chunk_offset, status, h0s, hfs, (bf16*)o, n_seqs, T, H, single, win);
+      else
+        carry_f32_kernel<SE><<<(unsigned)nblocks, kF32Threads, 0, stream>>>(
+            inter, cu, chunk_offset, status, h0s, hfs, (float*)o, n_seqs, T, H, single, win);
+    };
+    if (bf16_state) carry(bf16{}); else carry(0.f);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -24,6 +24,7 @@ KDA_ERR_WORKSPACE, KDA_ERR_ALIAS, KDA_ERR_HIP, KDA_ERR_ALIGN, KDA_ERR_SCRATCH = 
 KDA_IO_F32, KDA_IO_BF16 = 0, 1
 KDA_STATE_F32, KDA_STATE_BF16 = 0, 1
 KDA_FLAG_QK_L2NORM = 1
+KDA_FLAG_STATE_BF16 = 2
 KDA_BAD_QKV, KDA_BAD_GATE, KDA_BAD_BETA, KDA_BAD_CU = 1, 2, 4, 8
 CHUNK = 64
 HEAD_DIM = 128
@@ -171,15 +172,16 @@ class Prefill:
     """Device buffers of one prefill call, marshalled once for repeated use.
 
     q, k [T, H, 128], v [T, H, 128] (bf16 or fp32, one dtype); log_alpha
-    [T, H, 128] fp32; beta [T, H] fp32; h0 [N, H, 128, 128] fp32 or None;
-    cu_seqlens int32 [N + 1] on the device or None (one sequence). h_final
-    may be passed as h0 to continue in place. qk_l2norm normalises q and k
-    inside the kernel.
+    [T, H, 128] fp32; beta [T, H] fp32; h0 [N, H, 128, 128] in state_dtype
+    (float32, or bfloat16: the serving format; the state is carried in fp32
+    inside the call and rounded once into h_final) or None; cu_seqlens int32
+    [N + 1] on the device or None (one sequence). h_final may be passed as h0
+    to continue in place. qk_l2norm normalises q and k inside the kernel.
     """
 
     def __init__(self, q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
                  h_final=None, want_final=True, workspace=None, qk_l2norm=False,
-                 noalloc=False):
+                 noalloc=False, state_dtype=torch.float32):
         dev = k.device
         self.T, self.H = _head_rows(k)
         if cu_seqlens is not None and cu_seqlens.dim() != 1:
@@ -196,15 +198,17 @@ class Prefill:
             _check(t, n, k.dtype, dev)
         _check(log_alpha, "log_alpha", torch.float32, dev)
         _check(beta, "beta", torch.float32, dev)
-        _check(h0, "h0", torch.float32, dev)
+        flags = (KDA_FLAG_QK_L2NORM if qk_l2norm else 0) | (
+            KDA_FLAG_STATE_BF16 if _state(state_dtype) == KDA_STATE_BF16 else 0)
+        _check(h0, "h0", state_dtype, dev)
         _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
         if o is None:
             o = torch.empty((self.T, self.H, v.shape[2]), dtype=k.dtype, device=dev)
         _check(o, "o", k.dtype, dev)
         if h_final is None and want_final:
             h_final = torch.empty((self.N, self.H, k.shape[2], v.shape[2]),
-                                  dtype=torch.float32, device=dev)
-        _check(h_final, "h_final", torch.float32, dev)
+                                  dtype=state_dtype, device=dev)
+        _check(h_final, "h_final", state_dtype, dev)
         if noalloc and workspace is not None:
             raise ValueError("noalloc calls take no workspace")
         if workspace is None and not noalloc:
@@ -216,8 +220,7 @@ class Prefill:
         self._keep = (q, k, v, log_alpha, beta, h0, cu_seqlens)
         self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
                       _ptr(cu_seqlens), self.N, self.T, self.H, int(k.shape[2]),
-                      int(v.shape[2]), self.io, KDA_FLAG_QK_L2NORM if qk_l2norm else 0,
-                      _ptr(o), _ptr(h_final))
+                      int(v.shape[2]), self.io, flags, _ptr(o), _ptr(h_final))
         if not noalloc:
             self._args += (_ptr(workspace), workspace.numel())
 
@@ -241,23 +244,26 @@ class Prefill:
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
-              h_final=None, want_final=True, workspace=None, qk_l2norm=False, stream=None):
+              h_final=None, want_final=True, workspace=None, qk_l2norm=False,
+              state_dtype=torch.float32, stream=None):
     """Chunked prefill (see Prefill for shapes). Returns (o, h_final or None)."""
     with torch.cuda.stream(stream):
         return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
-                       want_final=want_final, workspace=workspace,
-                       qk_l2norm=qk_l2norm).run(stream)
+                       want_final=want_final, workspace=workspace, qk_l2norm=qk_l2norm,
+                       state_dtype=state_dtype).run(stream)
 
 
 def chunk_fwd_noalloc(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
-                      h_final=None, want_final=True, qk_l2norm=False, stream=None):
+                      h_final=None, want_final=True, qk_l2norm=False,
+                      state_dtype=torch.float32, stream=None):
     """chunk_fwd through kda_chunk_fwd_noalloc: the workspace is the
     library's fixed per-GPU array, so the call itself allocates nothing
     (pass o, and h_final or want_final=False, to allocate nothing here
     either). Calls overlapping on one GPU race on that array."""
     with torch.cuda.stream(stream):
         return Prefill(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
-                       want_final=want_final, qk_l2norm=qk_l2norm, noalloc=True).run(stream)
+                       want_final=want_final, qk_l2norm=qk_l2norm, noalloc=True,
+                       state_dtype=state_dtype).run(stream)
 
 
 class Decode:
@@ -474,20 +480,22 @@ def recurrent_max_len(io_dtype: torch.dtype, n_seqs: int, heads: int) -> int:
 
 
 def forward(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, max_seqlen, n_seqs=None,
-            qk_l2norm=False, o=None, h_final=None, stream=None):
+            qk_l2norm=False, o=None, h_final=None, state_dtype=torch.float32, stream=None):
     """Mode switch after the "L2 Deep Distill" page's serving notes: batches
     whose sequences have at most recurrent_max_len(...) new tokens (32 for
     bf16 I/O, 16 for one bf16 sequence; for fp32 I/O up to 512 with many
     (sequence, head) pairs) go
     through the fused recurrent kernel, longer ones through the chunked
     prefill. max_seqlen is the longest sequence in the batch (the caller
-    knows it; cu_seqlens stays on the device). Same tensors as chunk_fwd
-    (fp32 states); with cu_seqlens None, n_seqs sequences of T / n_seqs
-    tokens each. Returns (o, h_final)."""
+    knows it; cu_seqlens stays on the device). Same tensors as chunk_fwd,
+    states in state_dtype (float32 or bfloat16) on both paths; with
+    cu_seqlens None, n_seqs sequences of T / n_seqs tokens each. Returns
+    (o, h_final)."""
     N = int(cu_seqlens.shape[0]) - 1 if cu_seqlens is not None else int(n_seqs or 1)
     if max_seqlen <= recurrent_max_len(k.dtype, N, int(k.shape[1])):
         return recurrent_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs=n_seqs,
-                             qk_l2norm=qk_l2norm, o=o, h_final=h_final, stream=stream)
+                             state_dtype=state_dtype, qk_l2norm=qk_l2norm, o=o,
+                             h_final=h_final, stream=stream)
     if cu_seqlens is None and N != 1:
         # fixed-length batch: the chunked path takes its sequence offsets
         T = int(k.shape[0])
@@ -496,4 +504,4 @@ def forward(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, max_seqlen, n
         with torch.cuda.stream(stream):
             cu_seqlens = torch.arange(N + 1, dtype=torch.int32, device=k.device) * (T // N)
     return chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o=o, h_final=h_final,
-                     qk_l2norm=qk_l2norm, stream=stream)
+                     qk_l2norm=qk_l2norm, state_dtype=state_dtype, stream=stream)

@@ -88,6 +88,14 @@ typedef enum {
  * page's serving note does. The pages give no epsilon; 1e-6 keeps zero
  * vectors at zero. Unknown bits are rejected with KDA_ERR_UNSUPPORTED. */
 #define KDA_FLAG_QK_L2NORM 1u
+/* Flag bit of kda_chunk_fwd (and its _phase and _noalloc forms):
+ * KDA_FLAG_STATE_BF16 makes h0 and h_final bfloat16 [N, H, 128, 128], the
+ * state format of the "L2 Deep Distill" page's serving notes (32 x 128 x
+ * 128 bf16, 1 MB per layer), which kda_recurrent_fwd also takes
+ * (KDA_STATE_BF16). The call widens h0 to float32, carries the state in
+ * float32 across all of a sequence's chunks (and windows) and rounds it to
+ * bf16 (nearest even) once, into h_final. */
+#define KDA_FLAG_STATE_BF16 2u
 
 /*
  * kda_chunk_fwd_workspace_bytes, kda_chunk_fwd_workspace_min_bytes
@@ -128,10 +136,12 @@ size_t kda_chunk_fwd_workspace_min_bytes(int32_t n_seqs, int64_t total_tokens,
  *
  *   q, k, v, o      see layouts above; io selects float32 or bfloat16
  *   log_alpha, beta float32
- *   flags           0 or KDA_FLAG_QK_L2NORM (q, k normalised in the kernel)
- *   h0              [N, H, 128, 128] float32, or NULL for zero states
+ *   flags           KDA_FLAG_QK_L2NORM (q, k normalised in the kernel) and
+ *                   KDA_FLAG_STATE_BF16 (h0, h_final in bfloat16), or 0
+ *   h0              [N, H, 128, 128] float32 (bfloat16 with
+ *                   KDA_FLAG_STATE_BF16), or NULL for zero states
  *   cu_seqlens      device int32 [N + 1], or NULL for one sequence (N = 1)
- *   h_final         [N, H, 128, 128] float32, or NULL to skip; it may be the
+ *   h_final         [N, H, 128, 128] in h0's type, or NULL to skip; it may be the
  *                   same pointer as h0 (in-place continuation) but must not
  *                   partially overlap it
  *   workspace       device scratch of at least
@@ -197,10 +207,10 @@ size_t kda_chunk_fwd_workspace_min_bytes(int32_t n_seqs, int64_t total_tokens,
  */
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          const float *log_alpha, const float *beta,
-                         const float *h0, const int32_t *cu_seqlens,
+                         const void *h0, const int32_t *cu_seqlens,
                          int32_t n_seqs, int64_t total_tokens, int32_t heads,
                          int32_t dk, int32_t dv, kda_io_dtype io,
-                         uint32_t flags, void *o, float *h_final,
+                         uint32_t flags, void *o, void *h_final,
                          void *workspace, size_t workspace_bytes,
                          void *stream);
 
@@ -220,11 +230,11 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
  */
 kda_status kda_chunk_fwd_phase(int32_t phase, const void *q, const void *k,
                                const void *v, const float *log_alpha,
-                               const float *beta, const float *h0,
+                               const float *beta, const void *h0,
                                const int32_t *cu_seqlens, int32_t n_seqs,
                                int64_t total_tokens, int32_t heads, int32_t dk,
                                int32_t dv, kda_io_dtype io, uint32_t flags,
-                               void *o, float *h_final, void *workspace,
+                               void *o, void *h_final, void *workspace,
                                size_t workspace_bytes, void *stream);
 
 /*
@@ -251,11 +261,11 @@ kda_status kda_chunk_fwd_phase(int32_t phase, const void *q, const void *k,
 #define KDA_NOALLOC_SCRATCH_BYTES (128u << 20) /* 128 MiB per GPU */
 kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
                                  const float *log_alpha, const float *beta,
-                                 const float *h0, const int32_t *cu_seqlens,
+                                 const void *h0, const int32_t *cu_seqlens,
                                  int32_t n_seqs, int64_t total_tokens,
                                  int32_t heads, int32_t dk, int32_t dv,
                                  kda_io_dtype io, uint32_t flags, void *o,
-                                 float *h_final, void *stream);
+                                 void *h_final, void *stream);
 
 /*
  * kda_decode_step - one recurrent step for a batch of sequences.

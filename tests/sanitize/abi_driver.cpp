@@ -13,10 +13,10 @@
 namespace kda {
 int g_chunk = 0, g_rec = 0, g_epi = 0, g_chk = 0;
 int64_t g_win = -1;   // window size of the last chunk launch
-hipError_t launch_chunk_fwd(int, bool, bool, const void*, const void*, const void*, const float*,
-                            const float*, const float*, const int32_t*, int32_t, int64_t, int32_t,
-                            int64_t, int64_t win_slots, void*, float*, int32_t*, int32_t*, float*,
-                            uint8_t*, hipStream_t) {
+hipError_t launch_chunk_fwd(int, bool, bool, bool, const void*, const void*, const void*,
+                            const float*, const float*, const void*, const int32_t*, int32_t,
+                            int64_t, int32_t, int64_t, int64_t win_slots, void*, void*, int32_t*,
+                            int32_t*, float*, uint8_t*, hipStream_t) {
   ++g_chunk;
   g_win = win_slots;
   return hipSuccess;
@@ -83,7 +83,8 @@ int main() {
                                   const_cast<void*>(o), hf, const_cast<void*>(w), ws_min, nullptr),
          KDA_ERR_WORKSPACE, "phase with a partial window");
   expect(prefill(at(0), at(4096), h0, hf, w, ws, 1, nullptr, T, 0), KDA_ERR_ALIAS, "o over q");
-  expect(prefill(at(0), o, h0, hf, w, ws, 1, nullptr, T, 2), KDA_ERR_UNSUPPORTED, "flag");
+  expect(prefill(at(0), o, h0, hf, w, ws, 1, nullptr, T, 4), KDA_ERR_UNSUPPORTED, "flag");
+  expect(prefill(at(0), o, h0, hf, w, ws, 1, nullptr, T, 2), KDA_OK, "bf16 state flag");
   expect(prefill(at(0), o, h0, hf, w, ws, 1, nullptr, -1, 0), KDA_ERR_SHAPE, "T < 0");
   expect(prefill(at(0), o, h0, hf, w, ws, 1 << 27, (const int32_t*)at(6 * 64 * MB), T, 0),
          KDA_ERR_SHAPE, "pairs");   // 2^27 sequences x 2 heads
@@ -149,7 +150,7 @@ int main() {
                                fl, nullptr), KDA_ERR_UNSUPPORTED, "check io 4");
   for (int st = -1; st < 9; ++st)
     if (kda_status_string((kda_status)st) == nullptr) ++fails;
-  if (kda::g_chunk != 7 || kda::g_rec != 2 || kda::g_epi != 1 || kda::g_chk != 2) {
+  if (kda::g_chunk != 8 || kda::g_rec != 2 || kda::g_epi != 1 || kda::g_chk != 2) {
     fprintf(stderr, "launch counts %d %d %d %d\n", kda::g_chunk, kda::g_rec, kda::g_epi,
             kda::g_chk);
     ++fails;

@@ -167,7 +167,7 @@ def call_prefill(lib, a, phase=None):
     (dict(dv=256), UNSUP),
     (dict(io=5), UNSUP),
     (dict(H=70000), UNSUP),
-    (dict(flags=2), UNSUP),
+    (dict(flags=4), UNSUP),
     (dict(flags=0x80000000), UNSUP),
     (dict(q=None), NULL),
     (dict(beta=None), NULL),
@@ -211,6 +211,16 @@ def test_prefill_alias_errors(lib):
     assert call_prefill(lib, dict(a, h_final=a["h0"] + 1024)) == ALIAS    # partial overlap
     assert call_prefill(lib, dict(a, ws=a["k"])) == ALIAS                 # workspace over k
     assert call_prefill(lib, dict(a, o=a["ws"] + 256)) == ALIAS           # o inside workspace
+
+
+def test_prefill_state_size_follows_state_flag(lib):
+    # 1 x 2 states are 128 KiB in fp32 and 64 KiB with KDA_FLAG_STATE_BF16;
+    # o starting just before either end overlaps h0 (calls that pass every
+    # check would launch, so only rejected calls appear here)
+    a = prefill_args(lib)
+    assert call_prefill(lib, dict(a, o=a["h0"] + 128 * 1024 - 256)) == ALIAS
+    assert call_prefill(lib, dict(a, flags=2, o=a["h0"] + 64 * 1024 - 256)) == ALIAS
+    assert call_prefill(lib, dict(a, flags=3, h_final=a["h0"] + 32 * 1024)) == ALIAS
 
 
 def test_prefill_invalid_phase(lib):
