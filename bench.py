@@ -30,7 +30,7 @@ workload with its own roofline: the fused multi-token recurrent call
 through the chunked path, which is the faster one there), the decode step with a
 bf16 state, batch-1 decode (one sequence x 32 heads) launched step by step
 and replayed from a HIP graph, the prefill with in-kernel q/k L2Norm, the 8K
-prefill with fp32 I/O, the 8K prefill with decays strong enough that every
+prefill continuing a bf16 state in place, the 8K prefill with fp32 I/O, the 8K prefill with decays strong enough that every
 chunk takes the exact per-element diagonal blocks, and the RMSNorm x
 sigmoid-gate epilogue over the prefill's 8192 x 32 output rows.
 
@@ -524,6 +524,18 @@ def extensions(torch, d, pre_args, steps, warmup, extra=None, us_8k=None):
         "workload": "the 8K prefill with KDA_FLAG_QK_L2NORM", "us": us,
         "tokens_per_s": pre_args[0].shape[0] / (us * 1e-6)}
     o = pre_n.o
+    # the serving state format: the 8K prefill continuing a bf16 state in
+    # place (h0 = h_final, KDA_FLAG_STATE_BF16)
+    T8, H8 = pre_args[0].shape[0], pre_args[0].shape[1]
+    Sb8 = d(workloads.make_decode_state(1, H8, seed=2100), bf)
+    pre_b = Prefill(*pre_args[:5], Sb8, pre_args[6], h_final=Sb8, state_dtype=bf)
+    us = _time_calls(torch, pre_b.run, steps, warmup)
+    alg = prefill_alg_bytes(T8, H8, 1, 2) - H8 * STATE_BYTES + 2 * H8 * STATE_BYTES // 2
+    out["prefill_bf16_state"] = {
+        "workload": "the 8K prefill continuing a bf16 state ~N(0,0.02) in place "
+                    "(KDA_FLAG_STATE_BF16)", "us": us,
+        "tokens_per_s": T8 / (us * 1e-6), "alg_bytes": alg, "roofline": _hbm(alg, us)}
+    del pre_b, Sb8
     for name, what in (("fp32_8k", "the 8K x 32-head prefill with fp32 q/k/v/o (fp32 "
                                     "intermediates)"),
                        ("exact_diag_8k", "the 8K x 32-head prefill, bf16, with half the "
