@@ -158,3 +158,18 @@ def test_bf16_state_dtype_checked_by_the_binding():
         kda.chunk_fwd(q, k, v, la, b, dev(p.h0), state_dtype=bf)   # fp32 h0 for a bf16 state
     with pytest.raises(TypeError):
         kda.chunk_fwd(q, k, v, la, b, dev(p.h0).to(bf))            # bf16 h0 for an fp32 state
+
+
+@pytest.mark.parametrize("T,H,N", [(8192, 32, 1), (8192, 32, 4)])
+def test_bf16_state_full_size_equals_rounded_fp32_state_call(T, H, N):
+    """At the 8K x 32-head size (every carry workgroup of the one-tile and,
+    with four sequences, the two-tile form), the bf16-state call is the
+    fp32-state call with its final state rounded."""
+    p = workloads.make_prefill([T // N] * N, H=H, seed=82 + N, io="bf16", h0_std=0.02)
+    (q, k, v, la, b), cu = _args(p)
+    h0b, _ = _bf16_h0(p)
+    o32, h32 = kda.chunk_fwd(q, k, v, la, b, h0b.float(), cu)
+    o16, h16 = kda.chunk_fwd(q, k, v, la, b, h0b, cu, state_dtype=bf)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32)
+    assert torch.equal(h16, h32.to(bf))
