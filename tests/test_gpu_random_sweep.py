@@ -4,8 +4,9 @@ decode steps.
 Each case draws its own combination of the features the fixed parity tests
 cover one at a time: I/O dtype, head count, packed batches with empty,
 one-token, chunk-boundary and ragged sequences, the single-sequence launch
-(no cu_seqlens), nonzero or absent initial states, mild, split and extreme
-decay recipes, in-kernel L2Norm on raw q/k, and workspaces that force the
+(no cu_seqlens), nonzero or absent initial states in fp32 or bf16, mild,
+split and extreme decay recipes, in-kernel L2Norm on raw q/k, and workspaces
+that force the
 prefill into windows of a few chunk slots. Batches whose mean length is at
 most two chunks (or four, with at least 256 (sequence, head) pairs: a mode
 of its own) take the short-sequence carry, other batches with more than 32
@@ -63,9 +64,11 @@ def _draw_case(i):
         N = int(rng.integers(16, 25))
         lengths = [int(x) for x in rng.integers(100, 300, size=N)]
         single = False
+    # drawn last, so the other draws of every case stay as they were
+    bf16_state = bool(rng.random() < 0.25)
     return dict(lengths=lengths, H=H, seed=7100 + i, io=io, decay=decay,
                 h0_std=h0_std, qk="raw" if l2norm else "unit"), \
-        dict(l2norm=l2norm, single=single, window=window)
+        dict(l2norm=l2norm, single=single, window=window, bf16_state=bf16_state)
 
 
 def _slot_bytes(H, io):
@@ -77,8 +80,9 @@ def _oracle(p, l2norm):
     return recurrent.forward(q, k, p.v, p.log_alpha, p.beta, p.h0, p.cu_seqlens)
 
 
-def _check(p, o, hf, ro, rh, what):
-    tol_o, tol_s = TOL[p.io]
+def _check(p, o, hf, ro, rh, what, bf16_state=False):
+    # a bf16 state sets the error, whatever the I/O dtype
+    tol_o, tol_s = TOL["bf16" if bf16_state else p.io]
     assert np.isfinite(o).all() and np.isfinite(hf).all(), what
     if p.T == 0:
         return
@@ -94,23 +98,27 @@ def test_random_case_against_oracle(i):
     print(f"case {i}: lengths {wargs['lengths']} H {p.H} io {p.io} decay {wargs['decay']} "
           f"h0 {p.h0 is not None} {opt}")
     dt = io_dtype(p.io)
+    sdt = torch.bfloat16 if opt["bf16_state"] else torch.float32
+    if opt["bf16_state"] and p.h0 is not None:
+        p.h0 = workloads.round_bf16(p.h0)   # the oracle starts from the bf16 state
     args = (dev(p.q, dt), dev(p.k, dt), dev(p.v, dt), dev(p.log_alpha), dev(p.beta),
-            None if p.h0 is None else dev(p.h0),
+            None if p.h0 is None else dev(p.h0, sdt),
             None if opt["single"] else dev(p.cu_seqlens, torch.int32))
     ws = None
     if opt["window"] is not None:
         nbytes = (kda.chunk_fwd_workspace_min_bytes(p.N, p.T, p.H, dt) +
                   (opt["window"] - 1) * _slot_bytes(p.H, p.io))
         ws = kda.alloc_workspace(p.N, p.T, p.H, dt, "cuda", nbytes=nbytes)
-    o, hf = kda.chunk_fwd(*args, workspace=ws, qk_l2norm=opt["l2norm"])
+    o, hf = kda.chunk_fwd(*args, workspace=ws, qk_l2norm=opt["l2norm"], state_dtype=sdt)
     torch.cuda.synchronize()
+    assert hf.dtype == sdt
     ro, rh = _oracle(p, opt["l2norm"])
-    _check(p, host(o), host(hf), ro, rh, "chunk_fwd")
+    _check(p, host(o), host(hf), ro, rh, "chunk_fwd", opt["bf16_state"])
     if max(wargs["lengths"]) <= 64:
         o2, h2 = kda.recurrent_fwd(*args[:6], dev(p.cu_seqlens, torch.int32), n_seqs=p.N,
-                                   qk_l2norm=opt["l2norm"])
+                                   qk_l2norm=opt["l2norm"], state_dtype=sdt)
         torch.cuda.synchronize()
-        _check(p, host(o2), host(h2), ro, rh, "recurrent_fwd")
+        _check(p, host(o2), host(h2), ro, rh, "recurrent_fwd", opt["bf16_state"])
 
 
 N_DECODE = 32
