@@ -6,8 +6,7 @@ cover one at a time: I/O dtype, head count, packed batches with empty,
 one-token, chunk-boundary and ragged sequences, the single-sequence launch
 (no cu_seqlens), nonzero or absent initial states in fp32 or bf16, mild,
 split and extreme decay recipes, in-kernel L2Norm on raw q/k, and workspaces
-that force the
-prefill into windows of a few chunk slots. Batches whose mean length is at
+that force the prefill into windows of a few chunk slots. Batches whose mean length is at
 most two chunks (or four, with at least 256 (sequence, head) pairs: a mode
 of its own) take the short-sequence carry, other batches with more than 32
 pairs the two-tile carry; batches of sequences no longer than 64 tokens
