@@ -105,6 +105,48 @@ def test_prefill_then_decode_graph():
     assert np.isfinite(pre.o.float().cpu().numpy()).all()
 
 
+def test_bf16_state_prefill_then_decode_in_a_graph():
+    """The serving flow with bf16 states captured in one graph: a prefill
+    writing its final states in bf16 (KDA_FLAG_STATE_BF16), then single-token
+    recurrent steps updating them in place; replayed twice, bitwise equal to
+    the eager run."""
+    p = workloads.make_prefill([100, 37], H=2, seed=83, io="bf16", h0_std=0.05)
+    bf = torch.bfloat16
+    pre = kda.Prefill(dev(p.q, bf), dev(p.k, bf), dev(p.v, bf), dev(p.log_alpha), dev(p.beta),
+                      dev(p.h0).to(bf), dev(p.cu_seqlens, torch.int32), state_dtype=bf)
+    toks = _decode_inputs(2, 2, 4, seed=83)
+    recs = [kda.Recurrent(*t, pre.h_final, None, n_seqs=2, state_dtype=bf, h_final=pre.h_final)
+            for t in toks]
+
+    def run():
+        pre.run()
+        for r in recs:
+            r.run()
+
+    run()
+    torch.cuda.synchronize()
+    assert pre.h_final.dtype == bf
+    ref = [pre.o.clone(), pre.h_final.clone()] + [r.o.clone() for r in recs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(2):
+        pre.o.fill_(0.0)
+        pre.h_final.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [pre.o, pre.h_final] + [r.o for r in recs]
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep
+
+
 def test_input_check_in_a_graph():
     """kda_check_inputs clears its flag word with a kernel, so a captured
     check reports each replay's inputs: clean, then with a planted positive
